@@ -1,0 +1,334 @@
+"""CPU oracle for the fused GEMM + tile-reduce path.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import or run anything in this package.  The product path
+(gemm_tile_granular_amd) never imports it, and it imports nothing from there.
+It shares no code with the HIP path; the only common module is `workloads`,
+which draws the seeded inputs and does none of the method's arithmetic.
+
+What it computes, and from which passage:
+
+* `gemm_reduce` -- the result of GEMM+AllReduce for one rank's output:
+  C = A.B (this rank's partial) plus the sum of the other ranks' partial
+  outputs.  The method computes C = A @ B and reduces the partial outputs
+  across ranks (abstract of "mKernel: Fast Multi-GPU, Multi-Node Fused
+  Kernels"; GEMM + AllReduce row of the five-kernel table on the MarkTechPost
+  and chathome pages).  Fusion only reorders and overlaps this sum, so the
+  oracle is the definition itself, in float64, on the exact bfloat16 input
+  values.  The reduction operator is addition (partial sums of a row-parallel
+  product).
+* `controller_update` / `controller_target` -- the adaptive partition rule of
+  "【学习】mKernel 分析" section 2.4: the target number of communication
+  (here: reduce) workgroups n_s* = B (R_s C_s) / (R_p C_p + R_s C_s), the value
+  that makes both roles' predicted finish times equal.  The page leaves the
+  symbols, rounding and clamping open; the readings used are written next to
+  each line below.
+* `expected_state` / `check_state` / `deterministic_owners` -- the integer
+  protocol: per-tile readiness flags (section 2.2, Figure 2), per-chunk
+  counters where the last tile of a 4-tile chunk releases it (section 2.3),
+  roles chosen by workgroup index and re-checked at task boundaries
+  (sections 2.4 and 4.1).
+
+Parity pins (tests/test_oracle.py) tie each function to something other than
+itself: hand-worked fixtures, closed forms (A = 0, no peers, B = I, all-ones,
+rank-1), an independent C brute force on tiny shapes, the controller's
+defining equal-finish-time condition, and mutation checks that a planted
+mistake in the oracle fails a pin.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from fractions import Fraction
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+# ---------------------------------------------------------------------------
+# Inputs: bfloat16 bit patterns -> exact values
+# ---------------------------------------------------------------------------
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of each bfloat16 bit pattern, as float64.
+
+    A bfloat16 pattern is the upper half of an IEEE binary32 pattern, so the
+    value is the binary32 number whose low 16 bits are zero.
+    """
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Result definition
+# ---------------------------------------------------------------------------
+
+
+def gemm_part(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """This rank's partial product A.B in float64 (A [M,K], B [K,N])."""
+    return bf16_bits_to_f64(a_bits) @ bf16_bits_to_f64(b_bits)
+
+
+def peer_sum(peers: np.ndarray, row_block: int = 1024) -> np.ndarray:
+    """Sum over the P peer partials (float32 [P,M,N]) in float64."""
+    P, M, N = peers.shape
+    out = np.zeros((M, N), dtype=np.float64)
+    for r0 in range(0, M, row_block):
+        r1 = min(M, r0 + row_block)
+        for p in range(P):
+            out[r0:r1] += peers[p, r0:r1].astype(np.float64)
+    return out
+
+
+def gemm_reduce(a_bits: np.ndarray, b_bits: np.ndarray, peers: np.ndarray) -> np.ndarray:
+    """C_ref = A.B + sum_p peers[p], float64, exact bfloat16 operands."""
+    a = np.asarray(a_bits)
+    b = np.asarray(b_bits)
+    if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError("A must be [M,K] and B must be [K,N]")
+    out = gemm_part(a, b)
+    if peers is not None and peers.shape[0]:
+        if peers.shape[1:] != out.shape:
+            raise ValueError("peers must be [P,M,N]")
+        out += peer_sum(peers)
+    return out
+
+
+def gemm_reduce_at(a_bits: np.ndarray, b_bits: np.ndarray, peers: np.ndarray,
+                   rows: Sequence[int], cols: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+    """C_ref at the listed (row, col) positions, one element at a time.
+
+    Returns (full value, GEMM part) in float64.  Used where the whole product
+    is too large for the CPU in a test's time budget.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    a_rows = bf16_bits_to_f64(a_bits[rows, :])            # [S, K]
+    b_cols = bf16_bits_to_f64(b_bits[:, cols]).T          # [S, K]
+    gemm = np.einsum("sk,sk->s", a_rows, b_cols)
+    full = gemm.copy()
+    if peers is not None and peers.shape[0]:
+        full += peers[:, rows, cols].astype(np.float64).sum(axis=0)
+    return full, gemm
+
+
+# ---------------------------------------------------------------------------
+# Independent brute force (C, single thread) for tiny shapes
+# ---------------------------------------------------------------------------
+
+_brute_lib = None
+
+
+def brute_library_path() -> str:
+    return os.path.join(_HERE, "libmkbrute.so")
+
+
+def build_brute(force: bool = False) -> str:
+    """Compile oracle/brute.c with the host C compiler."""
+    out = brute_library_path()
+    src = os.path.join(_HERE, "brute.c")
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
+        tmp = out + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-shared", "-fPIC", "-o", tmp, src])
+        os.replace(tmp, out)
+    return out
+
+
+def _brute():
+    global _brute_lib
+    if _brute_lib is None:
+        lib = ctypes.CDLL(build_brute())
+        lib.mk_brute_gemm_reduce.restype = None
+        lib.mk_brute_gemm_reduce.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+        _brute_lib = lib
+    return _brute_lib
+
+
+def gemm_reduce_brute(a_bits: np.ndarray, b_bits: np.ndarray, peers: np.ndarray) -> np.ndarray:
+    """Triple-loop float64 brute force in C (tiny shapes only)."""
+    a = np.ascontiguousarray(a_bits, dtype=np.uint16)
+    b = np.ascontiguousarray(b_bits, dtype=np.uint16)
+    M, K = a.shape
+    K2, N = b.shape
+    assert K == K2
+    P = 0 if peers is None else peers.shape[0]
+    pe = np.ascontiguousarray(peers if P else np.zeros((1, 1, 1), np.float32), dtype=np.float32)
+    out = np.empty((M, N), dtype=np.float64)
+    _brute().mk_brute_gemm_reduce(a.ctypes.data, b.ctypes.data, pe.ctypes.data, P,
+                                  M, N, K, out.ctypes.data)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Adaptive partition controller (section 2.4 of the analysis page)
+# ---------------------------------------------------------------------------
+
+U64 = (1 << 64) - 1
+COST_CAP = (1 << 26) - 1     # per-task cycle means saturate here (keeps the u64 math exact)
+
+
+def controller_target(B: int, R_s: int, C_s: int, R_p: int, C_p: int,
+                      current: int, floor: int = 2) -> int:
+    """Target reduce-workgroup count n_s*.
+
+    Readings of the page's undefined symbols (applied here and on the GPU):
+      B   -- persistent workgroups sharing the two roles;
+      s   -- the communication role (here: tile-reduce); p -- compute;
+      R_x -- tasks of role x not yet finished; C_x -- mean cycles per task.
+    n_s* = B R_s C_s / (R_p C_p + R_s C_s) is the n at which the two roles'
+    predicted finish times R_s C_s / n and R_p C_p / (B - n) are equal.
+    Rounding: nearest, ties up, in unsigned 64-bit integers.
+    Clamp: while compute remains (R_p > 0) keep at least one compute
+    workgroup (n <= B-1) and at least `floor` reducers (2, the low end of the
+    page's static sweep); with no compute left the formula itself gives B.
+    A zero denominator carries no information: the current target stays.
+    """
+    if B < 2:
+        raise ValueError("need at least two workgroups")
+    if R_p == 0:
+        return B
+    hi = B - 1
+    lo = min(floor, hi)
+    num = B * R_s * C_s
+    den = R_p * C_p + R_s * C_s
+    if den == 0:
+        n = current
+    else:
+        if 2 * num + den > U64:
+            raise OverflowError("controller operands exceed the unsigned 64-bit range")
+        n = (2 * num + den) // (2 * den)
+    return min(max(n, lo), hi)
+
+
+def cycle_mean(total_cycles: int, tasks: int) -> int:
+    """Cumulative mean cost per task since launch (integer, saturating)."""
+    return min(total_cycles // tasks, COST_CAP)
+
+
+def controller_update(B: int, T: int, compute_done: int, reduce_done: int,
+                      sum_cycles_compute: int, sum_cycles_reduce: int,
+                      current: int, floor: int = 2) -> int:
+    """One controller step from the progress counters.
+
+    R_p counts compute tasks not yet finished (claimed-but-running tasks count
+    as remaining); R_s counts tiles not yet reduced, ready or not.  Until both
+    roles have finished a task there is no cost estimate and the current
+    target stays (clamped).
+    """
+    R_p = T - compute_done
+    R_s = T - reduce_done
+    if R_p == 0:
+        return B
+    if compute_done == 0 or reduce_done == 0:
+        hi = B - 1
+        return min(max(current, min(floor, hi)), hi)
+    C_p = cycle_mean(sum_cycles_compute, compute_done)
+    C_s = cycle_mean(sum_cycles_reduce, reduce_done)
+    return controller_target(B, R_s, C_s, R_p, C_p, current, floor)
+
+
+def controller_exact(B: int, R_s: int, C_s: int, R_p: int, C_p: int) -> Fraction:
+    """Unrounded, unclamped n_s* as an exact rational."""
+    return Fraction(B * R_s * C_s, R_p * C_p + R_s * C_s)
+
+
+# ---------------------------------------------------------------------------
+# Tiles, chunks and the integer protocol
+# ---------------------------------------------------------------------------
+
+
+def tile_grid(M: int, N: int, tile_m: int, tile_n: int) -> Tuple[int, int]:
+    """Tile rows and tile columns; ragged edges make a partial last tile."""
+    return -(-M // tile_m), -(-N // tile_n)
+
+
+def chunk_sizes(T: int, tiles_per_chunk: int) -> np.ndarray:
+    """Tiles in each chunk.  Chunk c holds tiles [c*tpc, (c+1)*tpc) in row-major
+    tile order; only the last chunk may be short."""
+    Ch = -(-T // tiles_per_chunk)
+    sizes = np.full(Ch, tiles_per_chunk, dtype=np.int64)
+    if Ch and T % tiles_per_chunk:
+        sizes[-1] = T % tiles_per_chunk
+    return sizes
+
+
+def deterministic_owners(T: int, B: int, n_reduce: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Owner maps of the deterministic static schedule.
+
+    Workgroups [0, n_reduce) reduce and the rest compute (roles by workgroup
+    index); each takes its tiles round-robin in increasing tile order.
+    """
+    t = np.arange(T, dtype=np.int64)
+    return n_reduce + t % (B - n_reduce), t % n_reduce
+
+
+OWNER_WG_MASK = 0xFFFF
+
+
+def expected_state(T: int, tiles_per_chunk: int, epoch: int, calls: int) -> Dict[str, np.ndarray]:
+    """Integer state after `calls` complete launches of one shape since the
+    counters were last cleared; `epoch` is the last launch's epoch."""
+    sizes = chunk_sizes(T, tiles_per_chunk)
+    return {
+        "tile_flag": np.full(T, epoch, dtype=np.int64),
+        "tile_reduce_cnt": np.full(T, calls, dtype=np.int64),
+        "chunk_cnt": sizes * calls,
+        "chunk_flag": np.full(sizes.shape[0], epoch, dtype=np.int64),
+    }
+
+
+def check_state(maps: Dict[str, np.ndarray], T: int, tiles_per_chunk: int, epoch: int,
+                calls: int, B: int, mode: str, n_reduce: int) -> List[str]:
+    """Compare the protocol state against its closed form.
+
+    Returns a list of human-readable violations (empty when all holds).
+    `mode` is "deterministic", "static" or "adaptive".
+    """
+    bad: List[str] = []
+    exp = expected_state(T, tiles_per_chunk, epoch, calls)
+    for key, want in exp.items():
+        got = np.asarray(maps[key], dtype=np.int64)
+        if got.shape != want.shape:
+            bad.append(f"{key}: shape {got.shape} != {want.shape}")
+            continue
+        idx = np.nonzero(got != want)[0]
+        if idx.size:
+            i = int(idx[0])
+            bad.append(f"{key}[{i}] = {int(got[i])}, expected {int(want[i])} "
+                       f"({idx.size} mismatches)")
+    co = np.asarray(maps["compute_owner"], dtype=np.int64)
+    ro = np.asarray(maps["reduce_owner"], dtype=np.int64)
+    co_wg, co_ns = co & OWNER_WG_MASK, co >> 16
+    ro_wg, ro_ns = ro & OWNER_WG_MASK, ro >> 16
+    if mode == "deterministic":
+        dc, dr = deterministic_owners(T, B, n_reduce)
+        if not np.array_equal(co_wg, dc):
+            i = int(np.nonzero(co_wg != dc)[0][0])
+            bad.append(f"compute_owner[{i}] = {int(co_wg[i])}, expected {int(dc[i])}")
+        if not np.array_equal(ro_wg, dr):
+            i = int(np.nonzero(ro_wg != dr)[0][0])
+            bad.append(f"reduce_owner[{i}] = {int(ro_wg[i])}, expected {int(dr[i])}")
+    if np.any(co_wg >= B):
+        bad.append("compute owner outside [0, B)")
+    if np.any(ro_wg >= B):
+        bad.append("reduce owner outside [0, B)")
+    # role at the time of the task: compute iff index >= target, reduce iff index < target
+    if np.any(co_wg < co_ns):
+        i = int(np.nonzero(co_wg < co_ns)[0][0])
+        bad.append(f"tile {i} computed by workgroup {int(co_wg[i])} while the reduce "
+                   f"target was {int(co_ns[i])}")
+    if np.any(ro_wg >= ro_ns):
+        i = int(np.nonzero(ro_wg >= ro_ns)[0][0])
+        bad.append(f"tile {i} reduced by workgroup {int(ro_wg[i])} while the reduce "
+                   f"target was {int(ro_ns[i])}")
+    if mode in ("static", "deterministic"):
+        if np.any(co_ns != n_reduce):
+            bad.append("static partition changed during the launch (compute side)")
+        if np.any(ro_ns != n_reduce):
+            bad.append("static partition changed during the launch (reduce side)")
+    return bad

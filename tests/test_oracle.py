@@ -1,0 +1,323 @@
+"""Pins for the CPU oracle: each function is tied to something other than itself.
+
+* result definition: a hand-worked fixture, closed forms (no peers, A = 0,
+  B = I, all-ones, rank-1, integer operands against exact integer arithmetic)
+  and an independent C brute force;
+* controller: a hand-worked table and the defining equal-finish-time
+  condition of the adaptive partition rule;
+* protocol checker: the closed-form state is accepted, every kind of
+  corruption is rejected;
+* mutation checks: a planted mistake in the oracle (dropped term, wrong sign,
+  transposed operand, wrong index, wrong rounding, missing clamp) fails at
+  least one pin.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle
+import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _bits_of(values):
+    return wl.round_to_bf16_bits(np.asarray(values, dtype=np.float32))
+
+
+# ---------------------------------------------------------------------------
+# result pins, written so that any implementation can be checked
+# ---------------------------------------------------------------------------
+
+def pin_golden(fn):
+    g = _load("tiny_gemm_reduce.json")
+    a = np.array(g["A_bits"], dtype=np.uint16)
+    b = np.array(g["B_bits"], dtype=np.uint16)
+    peers = np.array(g["peers"], dtype=np.float32)
+    np.testing.assert_array_equal(_bits_of(g["A_values"]), a)
+    np.testing.assert_array_equal(_bits_of(g["B_values"]), b)
+    got = fn(a, b, peers)
+    return np.array_equal(got, np.array(g["C"]))
+
+
+def pin_no_peers_is_integer_matmul(fn):
+    # integer-valued bf16 operands: the product is exact in float64 and equals
+    # exact integer arithmetic
+    rng = np.random.default_rng(3)
+    ai = rng.integers(-8, 9, size=(5, 7))
+    bi = rng.integers(-8, 9, size=(7, 6))
+    got = fn(_bits_of(ai), _bits_of(bi), np.zeros((0, 5, 6), np.float32))
+    want = np.array([[sum(int(ai[i, k]) * int(bi[k, j]) for k in range(7)) for j in range(6)]
+                     for i in range(5)])
+    return got.shape == want.shape and np.array_equal(got, want)
+
+
+def pin_zero_a_is_peer_sum(fn):
+    peers = np.array([[[1.5, -2.0, 0.25]], [[4.0, 0.5, -0.75]], [[-1.0, 1.0, 2.0]]],
+                     dtype=np.float32)               # [3, 1, 3]
+    a = np.zeros((1, 4), np.uint16)
+    b = _bits_of(np.arange(12, dtype=np.float32).reshape(4, 3))
+    got = fn(a, b, peers)
+    return np.array_equal(got, np.array([[4.5, -0.5, 1.5]]))
+
+
+def pin_identity_b(fn):
+    rng = np.random.default_rng(4)
+    a = _bits_of(rng.uniform(-3, 3, size=(4, 6)).astype(np.float32))
+    b = _bits_of(np.eye(6, dtype=np.float32))
+    peers = rng.standard_normal((2, 4, 6)).astype(np.float32)
+    got = fn(a, b, peers)
+    av = (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    want = av + peers[0].astype(np.float64) + peers[1].astype(np.float64)
+    return np.allclose(got, want, rtol=0, atol=1e-12)
+
+
+def pin_all_ones(fn):
+    K = 37
+    a = _bits_of(np.ones((3, K), np.float32))
+    b = _bits_of(np.ones((K, 2), np.float32))
+    peers = np.full((4, 3, 2), 0.5, np.float32)
+    got = fn(a, b, peers)
+    return np.array_equal(got, np.full((3, 2), K + 2.0))
+
+
+def pin_rank_one(fn):
+    u = np.array([[1.0], [-2.0], [0.5]], np.float32)      # [3,1]
+    v = np.array([[3.0, -1.0, 0.25, 8.0]], np.float32)     # [1,4]
+    got = fn(_bits_of(u), _bits_of(v), np.zeros((0, 3, 4), np.float32))
+    return np.array_equal(got, (u.astype(np.float64) @ v.astype(np.float64)))
+
+
+def pin_brute_force(fn):
+    for seed, (M, N, K, P) in enumerate([(3, 5, 7, 2), (8, 4, 16, 1), (2, 9, 3, 0), (6, 6, 6, 3)]):
+        w = wl.custom(M, N, K, P, wid=200 + seed)
+        a, b, p = wl.make_inputs(w, seed=seed)
+        got = fn(a, b, p)
+        want = oracle.gemm_reduce_brute(a, b, p)
+        if got.shape != want.shape or not np.allclose(got, want, rtol=1e-12, atol=1e-12):
+            return False
+    return True
+
+
+RESULT_PINS = [pin_golden, pin_no_peers_is_integer_matmul, pin_zero_a_is_peer_sum,
+               pin_identity_b, pin_all_ones, pin_rank_one, pin_brute_force]
+
+
+@pytest.mark.parametrize("pin", RESULT_PINS, ids=lambda p: p.__name__)
+def test_oracle_meets_pin(pin):
+    assert pin(oracle.gemm_reduce)
+
+
+def test_brute_force_meets_closed_form_pins():
+    # the C brute force is itself held to the hand-worked and closed-form pins
+    for pin in RESULT_PINS[:-1]:
+        assert pin(oracle.gemm_reduce_brute), pin.__name__
+
+
+def test_elementwise_oracle_agrees_with_full_oracle():
+    w = wl.custom(50, 70, 90, 3, wid=300)
+    a, b, p = wl.make_inputs(w)
+    full = oracle.gemm_reduce(a, b, p)
+    gemm = oracle.gemm_part(a, b)
+    rng = np.random.default_rng(0)
+    rows = rng.integers(0, 50, 200)
+    cols = rng.integers(0, 70, 200)
+    v, g = oracle.gemm_reduce_at(a, b, p, rows, cols)
+    np.testing.assert_allclose(v, full[rows, cols], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(g, gemm[rows, cols], rtol=1e-13, atol=1e-13)
+
+
+def test_oracle_rejects_bad_shapes():
+    with pytest.raises(ValueError):
+        oracle.gemm_reduce(np.zeros((2, 3), np.uint16), np.zeros((4, 2), np.uint16), None)
+
+
+# ---------------------------------------------------------------------------
+# mutation checks: plausible mistakes must fail a pin
+# ---------------------------------------------------------------------------
+
+def _dec(bits):
+    return oracle.bf16_bits_to_f64(bits)
+
+
+MUTANTS = {
+    "dropped_peer_sum": lambda a, b, p: _dec(a) @ _dec(b),
+    "peers_subtracted": lambda a, b, p: _dec(a) @ _dec(b) - p.astype(np.float64).sum(0),
+    "only_first_peer": lambda a, b, p: _dec(a) @ _dec(b) + (p[0].astype(np.float64) if p.shape[0] else 0),
+    # row-major [K,N] buffer read as if it were [N,K] column-major
+    "b_layout_transposed": lambda a, b, p: (_dec(a) @ _dec(b).reshape(b.shape[1], b.shape[0]).T
+                                            + p.astype(np.float64).sum(0)),
+    "last_k_dropped": lambda a, b, p: _dec(a)[:, :-1] @ _dec(b)[:-1] + p.astype(np.float64).sum(0),
+    "bf16_low_half": lambda a, b, p: ((a.astype(np.uint32)).view(np.float32).astype(np.float64)
+                                      @ (b.astype(np.uint32)).view(np.float32).astype(np.float64)
+                                      + p.astype(np.float64).sum(0)),
+    "peers_counted_twice": lambda a, b, p: _dec(a) @ _dec(b) + 2 * p.astype(np.float64).sum(0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_result_mistake_fails_a_pin(name):
+    fn = MUTANTS[name]
+    failed = []
+    for pin in RESULT_PINS[:-1]:
+        try:
+            ok = pin(fn)
+        except Exception:
+            ok = False
+        if not ok:
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
+
+
+# ---------------------------------------------------------------------------
+# controller
+# ---------------------------------------------------------------------------
+
+def test_controller_hand_table():
+    g = _load("controller_table.json")
+    for B, R_s, C_s, R_p, C_p, exact, n in g["rows"]:
+        if R_p:
+            assert oracle.controller_exact(B, R_s, C_s, R_p, C_p) == Fraction(exact)
+        assert oracle.controller_target(B, R_s, C_s, R_p, C_p, current=7) == n, (B, R_s, C_s, R_p, C_p)
+
+
+@settings(max_examples=300, deadline=None)
+@given(B=st.integers(4, 1024), R_s=st.integers(1, 1 << 20), C_s=st.integers(1, (1 << 26) - 1),
+       R_p=st.integers(1, 1 << 20), C_p=st.integers(1, (1 << 26) - 1))
+def test_controller_equalises_predicted_finish_times(B, R_s, C_s, R_p, C_p):
+    x = oracle.controller_exact(B, R_s, C_s, R_p, C_p)
+    # defining condition: R_s C_s / n == R_p C_p / (B - n) at the exact n
+    assert 0 < x < B
+    assert Fraction(R_s * C_s) / x == Fraction(R_p * C_p) / (B - x)
+    n = oracle.controller_target(B, R_s, C_s, R_p, C_p, current=2)
+    lo, hi = min(2, B - 1), B - 1
+    if lo <= x <= hi:
+        assert abs(Fraction(n) - x) <= Fraction(1, 2)
+        if abs(Fraction(n) - x) == Fraction(1, 2):
+            assert n > x          # ties round up
+    assert lo <= n <= hi
+
+
+@settings(max_examples=200, deadline=None)
+@given(B=st.integers(4, 512), R_s=st.integers(1, 5000), C_s=st.integers(1, 100000),
+       R_p=st.integers(1, 5000), C_p=st.integers(1, 100000))
+def test_controller_monotone_in_reduce_cost(B, R_s, C_s, R_p, C_p):
+    n1 = oracle.controller_target(B, R_s, C_s, R_p, C_p, 2)
+    n2 = oracle.controller_target(B, R_s, C_s + 1000, R_p, C_p, 2)
+    n3 = oracle.controller_target(B, R_s, C_s, R_p, C_p + 1000, 2)
+    assert n2 >= n1 >= n3
+
+
+def test_controller_update_keeps_target_without_samples():
+    assert oracle.controller_update(256, 100, 0, 0, 0, 0, current=9) == 9
+    assert oracle.controller_update(256, 100, 5, 0, 500, 0, current=9) == 9
+    assert oracle.controller_update(256, 100, 0, 0, 0, 0, current=1) == 2      # clamped
+    assert oracle.controller_update(256, 100, 0, 0, 0, 0, current=300) == 255  # clamped
+    assert oracle.controller_update(256, 100, 100, 3, 10, 10, current=9) == 256  # drain
+    # with samples: cumulative means, then the closed form
+    got = oracle.controller_update(256, 1024, 24, 8, 24 * 1000, 8 * 3000, current=2)
+    assert got == oracle.controller_target(256, 1016, 3000, 1000, 1000, 2)
+
+
+def test_cycle_mean_saturates():
+    assert oracle.cycle_mean(10, 3) == 3
+    assert oracle.cycle_mean(1 << 40, 1) == oracle.COST_CAP
+
+
+CONTROLLER_MUTANTS = {
+    "roles_swapped": lambda B, R_s, C_s, R_p, C_p, cur: (
+        B if R_p == 0 else min(max((2 * B * R_p * C_p + R_p * C_p + R_s * C_s)
+                                   // (2 * (R_p * C_p + R_s * C_s)), 2), B - 1)),
+    "floor_rounding": lambda B, R_s, C_s, R_p, C_p, cur: (
+        B if R_p == 0 else min(max(B * R_s * C_s // (R_p * C_p + R_s * C_s), 2), B - 1)),
+    "no_upper_clamp": lambda B, R_s, C_s, R_p, C_p, cur: (
+        B if R_p == 0 else max((2 * B * R_s * C_s + R_p * C_p + R_s * C_s)
+                               // (2 * (R_p * C_p + R_s * C_s)), 2)),
+    "no_drain": lambda B, R_s, C_s, R_p, C_p, cur: (
+        min(max((2 * B * R_s * C_s + R_p * C_p + R_s * C_s)
+                // (2 * (R_p * C_p + R_s * C_s)), 2), B - 1)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CONTROLLER_MUTANTS))
+def test_planted_controller_mistake_fails_the_table(name):
+    fn = CONTROLLER_MUTANTS[name]
+    g = _load("controller_table.json")
+    mismatches = [r for r in g["rows"] if fn(*r[:5], 7) != r[6]]
+    assert mismatches, f"controller mutant {name} matched the whole table"
+
+
+# ---------------------------------------------------------------------------
+# tiles, chunks and the protocol checker
+# ---------------------------------------------------------------------------
+
+def test_chunk_sizes_and_grid():
+    assert oracle.tile_grid(256, 256, 64, 64) == (4, 4)
+    assert oracle.tile_grid(300, 130, 128, 128) == (3, 2)
+    np.testing.assert_array_equal(oracle.chunk_sizes(16, 4), [4, 4, 4, 4])
+    np.testing.assert_array_equal(oracle.chunk_sizes(10, 4), [4, 4, 2])
+    assert oracle.chunk_sizes(0, 4).shape == (0,)
+
+
+def test_deterministic_owners_partition_tiles():
+    T, B, ns = 1000, 256, 6
+    co, ro = oracle.deterministic_owners(T, B, ns)
+    assert np.all((co >= ns) & (co < B)) and np.all((ro >= 0) & (ro < ns))
+    # each workgroup's tiles, taken in increasing order, are round-robin
+    for w in range(ns, B):
+        ts = np.nonzero(co == w)[0]
+        np.testing.assert_array_equal(ts, np.arange(w - ns, T, B - ns))
+    for w in range(ns):
+        np.testing.assert_array_equal(np.nonzero(ro == w)[0], np.arange(w, T, ns))
+
+
+def _good_maps(T, tpc, epoch, calls, B, ns):
+    exp = oracle.expected_state(T, tpc, epoch, calls)
+    co, ro = oracle.deterministic_owners(T, B, ns)
+    maps = {k: v.copy() for k, v in exp.items()}
+    maps["compute_owner"] = co | (ns << 16)
+    maps["reduce_owner"] = ro | (ns << 16)
+    return maps
+
+
+def test_check_state_accepts_the_closed_form():
+    maps = _good_maps(18, 4, 5, 3, 16, 3)
+    assert oracle.check_state(maps, 18, 4, 5, 3, 16, "deterministic", 3) == []
+    assert oracle.check_state(maps, 18, 4, 5, 3, 16, "static", 3) == []
+
+
+@pytest.mark.parametrize("corrupt", [
+    ("tile_flag", 3, 4), ("tile_reduce_cnt", 0, 4), ("tile_reduce_cnt", 7, 2),
+    ("chunk_cnt", 1, 11), ("chunk_cnt", 4, 7), ("chunk_flag", 2, 0),
+    ("compute_owner", 5, 1 | (3 << 16)), ("reduce_owner", 6, 2 | (3 << 16)),
+    ("compute_owner", 0, 20 | (3 << 16)), ("reduce_owner", 1, 1 | (4 << 16)),
+])
+def test_check_state_rejects_corruption(corrupt):
+    key, i, v = corrupt
+    maps = _good_maps(18, 4, 5, 3, 16, 3)
+    maps[key][i] = v
+    assert oracle.check_state(maps, 18, 4, 5, 3, 16, "deterministic", 3)
+
+
+def test_check_state_role_log_in_adaptive_mode():
+    T, B = 8, 8
+    maps = _good_maps(T, 4, 1, 1, B, 2)
+    maps["compute_owner"][:] = 5 | (3 << 16)      # index 5 >= target 3: compute ok
+    maps["reduce_owner"][:] = 1 | (3 << 16)       # index 1 < target 3: reduce ok
+    assert oracle.check_state(maps, T, 4, 1, 1, B, "adaptive", 2) == []
+    maps["reduce_owner"][4] = 6 | (3 << 16)       # reduced while in the compute role
+    assert oracle.check_state(maps, T, 4, 1, 1, B, "adaptive", 2)
+
+
+def test_brute_library_builds():
+    path = oracle.build_brute()
+    assert os.path.exists(path)
