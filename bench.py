@@ -1,0 +1,258 @@
+"""Benchmark of the fused GEMM + tile-reduce path on one MI355X.
+
+One step = one mk_gemm_reduce_local launch over the whole workload: the
+local partial C_r = A.B on MFMA plus the tile-granular reduction of every
+output tile with the R-1 peer partials, inputs resident in HBM.  Prints one
+JSON line.
+
+Legs (all on the same seeded inputs, same stream):
+  fused (adaptive partition)  -> value, roofline
+  unfused: GEMM kernel then reduce kernel -> fused_vs_unfused
+  static partitions 2..64 reduce workgroups -> adaptive_vs_best_static
+  CPU oracle on a bounded sample of the same workload -> cpu_baseline
+Before each timed launch a 512 MiB scratch buffer is rewritten (outside the
+timed events) so the 256 MB Infinity Cache and the L2s start cold.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+STATIC_SWEEP = (2, 4, 8, 16, 32, 64)          # the pages' sweep range
+STATIC_SWEEP_EXT = (96, 128, 160, 192, 224)   # beyond it, for MI355X's reduce role
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="tp_share")
+    ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the static partition sweep")
+    ap.add_argument("--fused-only", action="store_true",
+                    help="only the fused leg (for profiler runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def time_leg(fn, steps, warmup, flush, stream, torch):
+    """Per-launch durations (ms) from HIP events on the launch stream."""
+    for _ in range(warmup):
+        if flush is not None:
+            flush()
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s, e in evs:
+        if flush is not None:
+            flush()
+        s.record(stream)
+        fn()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [s.elapsed_time(e) for s, e in evs]
+    return ms, wall
+
+
+def summary(ms):
+    return {"mean": statistics.fmean(ms), "median": statistics.median(ms), "min": min(ms),
+            "max": max(ms)}
+
+
+def cpu_baseline(w, a, b, p, seconds):
+    """The oracle, as it stands, on row blocks of the workload until `seconds`
+    of CPU time have been spent (at least one block)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    rb = max(1, min(w.M, 512))
+    rows_done = 0
+    t_total = 0.0
+    r0 = 0
+    while r0 < w.M and (t_total < seconds or rows_done == 0):
+        r1 = min(w.M, r0 + rb)
+        sub_p = p[:, r0:r1, :]
+        t = time.perf_counter()
+        oracle.gemm_reduce(a[r0:r1], b, sub_p)
+        t_total += time.perf_counter() - t
+        rows_done += r1 - r0
+        r0 = r1
+    flops = 2.0 * rows_done * w.N * w.K
+    return {
+        "value": flops / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"float64 oracle (numpy/OpenBLAS) on rows [0, {rows_done}) of {w.M} "
+                  f"({w.name}: {rows_done}x{w.N}x{w.K} GEMM + {w.peers}-peer sum), "
+                  f"{t_total:.2f} s",
+        "seconds": t_total,
+        "host_cpus": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
+              "multi-GPU GEMM+AllReduce is not part of it.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gemm_tile_granular_amd as mk
+    import workloads as wl
+    from gemm_tile_granular_amd.tensors import upload
+
+    w = wl.workload(args.workload)
+    t_gen = time.perf_counter()
+    a, b, p = wl.make_inputs(w)
+    A, B, P, C = upload(a, b, p, "cuda:0")
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    print(f"[bench] {w.name}: {w.M}x{w.N}x{w.K}, {w.peers} peers, tile {w.tile_m}x{w.tile_n}; "
+          f"inputs ready in {t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    scratch = None
+    flush = None
+    if not args.no_flush:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+        counter = [0]
+
+        def flush():
+            counter[0] = (counter[0] + 1) & 0xFF
+            scratch.fill_(counter[0])
+
+    def fused():
+        mk.gemm_reduce_local(A, B, P, C, w.tile_m, w.tile_n, w.tiles_per_chunk)
+
+    def unfused():
+        mk.gemm_reduce_unfused(A, B, P, C, w.tile_m, w.tile_n, w.tiles_per_chunk)
+
+    mk.set_partition("adaptive", 0)
+    ms_fused, wall_fused = time_leg(fused, args.steps, args.warmup, flush, stream, torch)
+    st = mk.get_stats()
+    print(f"[bench] fused adaptive: {summary(ms_fused)} (n_reduce final {st['n_reduce_final']}, "
+          f"range {st['n_reduce_min_seen']}-{st['n_reduce_max_seen']})", file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: {args.copy_calibration} MiB x3", file=sys.stderr, flush=True)
+
+    out_extra = {}
+    if not args.fused_only:
+        # consistency of the timed fused result with the two-kernel path, at
+        # sampled positions (the oracle comparison lives in the test suite)
+        C_fused = C.clone()
+        unfused()
+        torch.cuda.synchronize()
+        g = torch.Generator(device="cpu").manual_seed(0)
+        idx = torch.randint(0, w.M * w.N, (1 << 16,), generator=g).to(C.device)
+        fv, uv = C_fused.view(-1)[idx].double(), C.view(-1)[idx].double()
+        diff = float((fv - uv).abs().max())
+        scale = float(uv.abs().max())
+        out_extra["fused_matches_unfused"] = {"max_abs_diff": diff, "scale": scale,
+                                              "ok": diff <= 2e-3 * scale}
+        del C_fused
+        ms_unf, _ = time_leg(unfused, args.steps, args.warmup, flush, stream, torch)
+        print(f"[bench] unfused: {summary(ms_unf)}", file=sys.stderr, flush=True)
+        out_extra["unfused_ms"] = summary(ms_unf)
+        out_extra["fused_vs_unfused"] = statistics.fmean(ms_unf) / statistics.fmean(ms_fused)
+        if not args.no_sweep:
+            sweep = {}
+            for n in STATIC_SWEEP:
+                mk.set_partition("static", n)
+                ms_n, _ = time_leg(fused, max(3, args.steps // 2), 1, flush, stream, torch)
+                sweep[n] = statistics.fmean(ms_n)
+                print(f"[bench] static {n}: {sweep[n]:.4f} ms", file=sys.stderr, flush=True)
+            best_n = min(sweep, key=sweep.get)
+            ext = {}
+            for n in STATIC_SWEEP_EXT:
+                mk.set_partition("static", n)
+                ms_n, _ = time_leg(fused, max(3, args.steps // 2), 1, flush, stream, torch)
+                ext[n] = statistics.fmean(ms_n)
+                print(f"[bench] static {n}: {ext[n]:.4f} ms", file=sys.stderr, flush=True)
+            mk.set_partition("adaptive", 0)
+            best_all = min({**sweep, **ext}.items(), key=lambda kv: kv[1])
+            out_extra["static_sweep_ms"] = {str(k): v for k, v in sweep.items()}
+            out_extra["static_sweep_ext_ms"] = {str(k): v for k, v in ext.items()}
+            out_extra["best_static"] = {"n_reduce": best_n, "ms": sweep[best_n]}
+            out_extra["adaptive_vs_best_static"] = sweep[best_n] / statistics.fmean(ms_fused)
+            out_extra["best_static_any"] = {"n_reduce": best_all[0], "ms": best_all[1]}
+            out_extra["adaptive_vs_best_static_any"] = best_all[1] / statistics.fmean(ms_fused)
+
+    ms = statistics.fmean(ms_fused)
+    sec = ms / 1e3
+    tflops = w.flops / sec / 1e12
+    gbps = w.algorithmic_bytes / sec / 1e9
+    t_mfma = w.flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    t_hbm = w.algorithmic_bytes / (HBM_PEAK_GBPS * 1e9)
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": gbps / HBM_PEAK_GBPS}
+    else:
+        roof = {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS}
+    roof["traffic"] = None
+    roof["kernel"] = f"mk::fused_gemm_reduce_kernel<{w.tile_m}, {w.tile_n}>"
+    roof["max_roofline_frac"] = max(t_mfma, t_hbm) / sec
+
+    result = {
+        "metric": "fused GEMM+tile-reduce TFLOP/s & % roofline on 1 MI355X; speedup vs unfused",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded, resident in HBM)",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K_local": w.K, "peers": w.peers,
+                   "tile": [w.tile_m, w.tile_n], "tiles_per_chunk": w.tiles_per_chunk,
+                   "partition": "adaptive", "cache_flush_between_steps": not args.no_flush},
+        "roofline": roof,
+        "fused_ms": summary(ms_fused),
+        "hbm_GBps_algorithmic": gbps,
+        "wall_s_fused_leg": wall_fused,
+        "n_reduce_final": st["n_reduce_final"],
+        **out_extra,
+    }
+    if not args.no_cpu and not args.fused_only:
+        result["cpu_baseline"] = cpu_baseline(w, a, b, p, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

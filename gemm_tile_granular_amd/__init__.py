@@ -1,0 +1,249 @@
+"""Python binding of libmk.so, the fused GEMM + tile-reduce library for MI355X.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libmk.so (C ABI in include/mk.h).  PyTorch supplies device memory and the
+current stream; nothing here computes.  If the library is not built, import
+fails loudly -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmk.so")
+
+MK_OK = 0
+MK_ERR_INVALID_ARG = -1
+MK_ERR_SHAPE = -2
+MK_ERR_HIP = -3
+MK_ERR_TIMEOUT = -4
+MK_ERR_NO_DEVICE = -5
+MK_ERR_PROTOCOL = -6
+STATUS_NAMES = {0: "MK_OK", -1: "MK_ERR_INVALID_ARG", -2: "MK_ERR_SHAPE", -3: "MK_ERR_HIP",
+                -4: "MK_ERR_TIMEOUT", -5: "MK_ERR_NO_DEVICE", -6: "MK_ERR_PROTOCOL"}
+
+PART_ADAPTIVE = 0
+PART_STATIC = 1
+PART_STATIC_DETERMINISTIC = 2
+MODES = {"adaptive": PART_ADAPTIVE, "static": PART_STATIC,
+         "deterministic": PART_STATIC_DETERMINISTIC}
+TRACE_CAP = 1024
+SUPPORTED_TILES = ((64, 64), (128, 128), (256, 128))
+
+
+class MkError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(code, code)}: {message}")
+        self.code = code
+
+
+class Stats(ctypes.Structure):
+    """Mirror of struct mk_stats in include/mk.h (same order and types)."""
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("status", ctypes.c_int32),
+        ("epoch", ctypes.c_uint32),
+        ("calls_since_reset", ctypes.c_uint32),
+        ("num_wg", ctypes.c_uint32),
+        ("num_tiles", ctypes.c_uint32),
+        ("num_chunks", ctypes.c_uint32),
+        ("tiles_per_chunk", ctypes.c_uint32),
+        ("tile_m", ctypes.c_uint32),
+        ("tile_n", ctypes.c_uint32),
+        ("mode", ctypes.c_uint32),
+        ("n_reduce_initial", ctypes.c_uint32),
+        ("n_reduce_final", ctypes.c_uint32),
+        ("n_reduce_min_seen", ctypes.c_uint32),
+        ("n_reduce_max_seen", ctypes.c_uint32),
+        ("role_switches", ctypes.c_uint32),
+        ("compute_tasks", ctypes.c_uint32),
+        ("reduce_tasks", ctypes.c_uint32),
+        ("chunks_released", ctypes.c_uint32),
+        ("invariant_violations", ctypes.c_uint32),
+        ("ns_trace_len", ctypes.c_uint32),
+        ("reserved0", ctypes.c_uint32),
+        ("sum_cycles_compute", ctypes.c_uint64),
+        ("sum_cycles_reduce", ctypes.c_uint64),
+        ("kernel_ticks_start", ctypes.c_uint64),
+        ("kernel_ticks_end", ctypes.c_uint64),
+        ("reduce_ticks_start", ctypes.c_uint64),
+        ("reduce_ticks_end", ctypes.c_uint64),
+        ("timer_hz", ctypes.c_uint64),
+    ]
+
+
+_vp, _i32, _i64, _u32p = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.POINTER(ctypes.c_uint32)
+
+SIGNATURES = {
+    "mk_gemm_reduce_local": (_i32, [_vp, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp]),
+    "mk_gemm_reduce_unfused": (_i32, [_vp, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp]),
+    "mk_set_partition": (_i32, [_i32, _i32]),
+    "mk_set_controller_floor": (_i32, [_i32]),
+    "mk_set_num_workgroups": (_i32, [_i32]),
+    "mk_set_timeout_us": (_i32, [ctypes.c_uint64]),
+    "mk_set_fault_skip_publish": (_i32, [_i64]),
+    "mk_get_stats": (_i32, [ctypes.POINTER(Stats), _u32p, ctypes.c_size_t]),
+    "mk_controller_eval": (_i32, [_vp, _vp, _i32, _vp]),
+    "mk_device_cu_count": (_i32, []),
+    "mk_release_workspace": (_i32, []),
+    "mk_last_error": (ctypes.c_char_p, []),
+    "mk_abi_version": (_i32, []),
+}
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m gemm_tile_granular_amd.build` "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def _check(rc: int) -> None:
+    if rc != MK_OK:
+        raise MkError(rc, lib.mk_last_error().decode(errors="replace"))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check_tensors(A, B, peers, C):
+    torch = _torch()
+    for name, t, dt in (("A", A, torch.bfloat16), ("B", B, torch.bfloat16), ("C", C, torch.float32)):
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous() or t.dim() != 2:
+            raise ValueError(f"{name} must be a contiguous 2-D {dt} CUDA tensor")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
+    P = 0
+    if peers is not None:
+        if (peers.dtype != torch.float32 or not peers.is_cuda or not peers.is_contiguous()
+                or peers.dim() != 3 or tuple(peers.shape[1:]) != (M, N)):
+            raise ValueError("peers must be a contiguous [P, M, N] float32 CUDA tensor")
+        P = peers.shape[0]
+    return M, N, K, P
+
+
+def _call(fn, A, B, peers, C, tile_m, tile_n, tiles_per_chunk, stream):
+    M, N, K, P = _check_tensors(A, B, peers, C)
+    pp = peers.data_ptr() if (peers is not None and P > 0) else None
+    _check(fn(A.data_ptr(), B.data_ptr(), pp, P, C.data_ptr(), M, N, K,
+              tile_m, tile_n, tiles_per_chunk, _stream_handle(stream)))
+
+
+def gemm_reduce_local(A, B, peers, C, tile_m: int, tile_n: int, tiles_per_chunk: int = 4,
+                      stream=None) -> None:
+    """C = A.B + sum_p peers[p] in one persistent launch (mk_gemm_reduce_local)."""
+    _call(lib.mk_gemm_reduce_local, A, B, peers, C, tile_m, tile_n, tiles_per_chunk, stream)
+
+
+def gemm_reduce_unfused(A, B, peers, C, tile_m: int, tile_n: int, tiles_per_chunk: int = 4,
+                        stream=None) -> None:
+    """Same result from two launches: GEMM, then reduce (mk_gemm_reduce_unfused)."""
+    _call(lib.mk_gemm_reduce_unfused, A, B, peers, C, tile_m, tile_n, tiles_per_chunk, stream)
+
+
+def set_partition(mode, n_reduce: int = 0) -> None:
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    _check(lib.mk_set_partition(m, int(n_reduce)))
+
+
+def set_controller_floor(floor: int) -> None:
+    _check(lib.mk_set_controller_floor(int(floor)))
+
+
+def set_num_workgroups(num_wg: int) -> None:
+    _check(lib.mk_set_num_workgroups(int(num_wg)))
+
+
+def set_timeout_us(us: int) -> None:
+    _check(lib.mk_set_timeout_us(int(us)))
+
+
+def set_fault_skip_publish(tile: int) -> None:
+    _check(lib.mk_set_fault_skip_publish(int(tile)))
+
+
+def device_cu_count() -> int:
+    rc = lib.mk_device_cu_count()
+    if rc < 0:
+        _check(rc)
+    return rc
+
+
+def release_workspace() -> None:
+    _check(lib.mk_release_workspace())
+
+
+def abi_version() -> int:
+    return lib.mk_abi_version()
+
+
+def get_stats(maps: bool = False, raise_on_error: bool = True) -> Dict:
+    """Stats of the last fused launch (synchronizes).  With maps=True also the
+    tile/chunk maps and the controller trace as numpy arrays."""
+    st = Stats()
+    st.struct_size = ctypes.sizeof(Stats)
+    buf = None
+    n = 0
+    if maps:
+        # sized from a first call without maps
+        rc0 = lib.mk_get_stats(ctypes.byref(st), None, 0)
+        if rc0 not in (MK_OK, MK_ERR_TIMEOUT, MK_ERR_PROTOCOL):
+            _check(rc0)
+        T, Ch = st.num_tiles, st.num_chunks
+        n = 4 * T + 2 * Ch + 2 * TRACE_CAP
+        buf = np.zeros(n, dtype=np.uint32)
+        st = Stats()
+        st.struct_size = ctypes.sizeof(Stats)
+    rc = lib.mk_get_stats(ctypes.byref(st), buf.ctypes.data_as(_u32p) if buf is not None else None, n)
+    out = {name: getattr(st, name) for name, _ in Stats._fields_}
+    out["status_name"] = STATUS_NAMES.get(st.status, str(st.status))
+    if maps:
+        T, Ch = st.num_tiles, st.num_chunks
+        o = 0
+        for key, cnt in (("tile_flag", T), ("tile_reduce_cnt", T), ("chunk_cnt", Ch),
+                         ("chunk_flag", Ch), ("compute_owner", T), ("reduce_owner", T),
+                         ("ns_trace", 2 * TRACE_CAP)):
+            out[key] = buf[o:o + cnt].copy()
+            o += cnt
+        out["ns_trace"] = out["ns_trace"].reshape(TRACE_CAP, 2)[: st.ns_trace_len]
+    if raise_on_error and rc not in (MK_OK,):
+        _check(rc)
+    out["rc"] = rc
+    return out
+
+
+def controller_eval(rows: np.ndarray) -> np.ndarray:
+    """Runs the device controller step on each row (B, T, compute_done,
+    reduce_done, sum_cycles_compute, sum_cycles_reduce, current, floor)."""
+    torch = _torch()
+    rows = np.ascontiguousarray(rows, dtype=np.uint64)
+    assert rows.ndim == 2 and rows.shape[1] == 8
+    n = rows.shape[0]
+    dev_in = torch.from_numpy(rows.view(np.int64)).cuda()
+    dev_out = torch.zeros(n, dtype=torch.int32, device=dev_in.device)
+    _check(lib.mk_controller_eval(dev_in.data_ptr(), dev_out.data_ptr(), n, _stream_handle(None)))
+    torch.cuda.synchronize()
+    return dev_out.cpu().numpy().view(np.uint32)

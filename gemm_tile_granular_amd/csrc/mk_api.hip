@@ -1,0 +1,524 @@
+// C ABI of the fused GEMM + tile-reduce library (declarations and contracts
+// in include/mk.h).  Host side only: argument checks, the per-device
+// workspace (flags, counters, owner maps, control block), epochs, launches
+// and statistics.  Every check that can fail on the caller's arguments runs
+// before the first HIP call.
+#include <cstdarg>
+#include <mutex>
+#include <string>
+#include <cstring>
+#include <cstdio>
+
+#include "mk.h"
+#include "mk_internal.hpp"
+
+namespace {
+
+using namespace mk;
+
+thread_local std::string g_last_error;
+std::mutex g_mu;
+
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(MK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+struct Settings {
+    int mode = MK_PART_ADAPTIVE;
+    int n_reduce = 0;
+    int floor = 2;
+    int num_wg = 0;
+    uint64_t timeout_us = 2000000;
+    int64_t skip_publish = -1;
+    int group_m = 8;
+};
+Settings g_set;
+
+constexpr int kMaxDevices = 64;
+
+struct Launch {
+    bool valid = false;
+    uint32_t epoch = 0, calls = 0, nwg = 0, T = 0, Ch = 0, tpc = 0, tm = 0, tn = 0;
+    uint32_t mode = 0, ns_init = 0;
+};
+
+struct DevState {
+    bool init = false;
+    int num_cu = 0;
+    uint64_t timer_hz = 100000000ull;
+    char *ws = nullptr;
+    size_t ws_bytes = 0;
+    uint32_t Tcap = 0, Chcap = 0;
+    uint32_t epoch = 0;
+    uint32_t calls = 0;
+    uint32_t shape_T = 0, shape_tpc = 0;
+    bool dirty = false;
+    Launch last;
+};
+DevState g_dev[kMaxDevices];
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Layout {
+    size_t live, snap, trace, tile_flag, tile_cnt, chunk_cnt, chunk_flag, cowner, rowner, total;
+};
+
+Layout layout_for(uint32_t Tcap, uint32_t Chcap) {
+    Layout L;
+    size_t o = 0;
+    L.live = o; o += sizeof(Live);
+    L.snap = o; o += sizeof(Live);
+    L.trace = o; o = align_up(o + 2 * sizeof(uint32_t) * kTraceCap, 256);
+    L.tile_flag = o; o = align_up(o + 4ull * Tcap, 256);
+    L.tile_cnt = o; o = align_up(o + 4ull * Tcap, 256);
+    L.chunk_cnt = o; o = align_up(o + 4ull * Chcap, 256);
+    L.chunk_flag = o; o = align_up(o + 4ull * Chcap, 256);
+    L.cowner = o; o = align_up(o + 4ull * Tcap, 256);
+    L.rowner = o; o = align_up(o + 4ull * Tcap, 256);
+    L.total = o;
+    return L;
+}
+
+WsView view_of(const DevState &d) {
+    const Layout L = layout_for(d.Tcap, d.Chcap);
+    WsView v;
+    v.live = (Live *)(d.ws + L.live);
+    v.snap = (Live *)(d.ws + L.snap);
+    v.trace = (uint32_t *)(d.ws + L.trace);
+    v.tile_flag = (uint32_t *)(d.ws + L.tile_flag);
+    v.tile_cnt = (uint32_t *)(d.ws + L.tile_cnt);
+    v.chunk_cnt = (uint32_t *)(d.ws + L.chunk_cnt);
+    v.chunk_flag = (uint32_t *)(d.ws + L.chunk_flag);
+    v.cowner = (uint32_t *)(d.ws + L.cowner);
+    v.rowner = (uint32_t *)(d.ws + L.rowner);
+    return v;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// All argument checks that do not need the GPU.
+int check_args(const void *A, const void *B, const float *peers, int num_peers, const float *C,
+               int64_t M, int64_t N, int64_t K, int tile_m, int tile_n, int tpc) {
+    if (M < 0 || N < 0 || K < 0) return fail(MK_ERR_INVALID_ARG, "negative dimension");
+    if (num_peers < 0) return fail(MK_ERR_INVALID_ARG, "num_peers < 0");
+    if (!tile_supported(tile_m, tile_n))
+        return fail(MK_ERR_INVALID_ARG, "tile %dx%d not supported (64x64, 128x128, 256x128)",
+                    tile_m, tile_n);
+    if (tpc < 1 || tpc > 64) return fail(MK_ERR_INVALID_ARG, "tiles_per_chunk must be in [1, 64]");
+    if (N % 8 != 0 || K % 8 != 0)
+        return fail(MK_ERR_SHAPE, "N (%lld) and K (%lld) must be multiples of 8", (long long)N,
+                    (long long)K);
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+        return fail(MK_ERR_SHAPE, "dimension exceeds 2^31-1");
+    if (M == 0 || N == 0) return MK_OK;
+    // byte offsets inside one tile row band stay below 2^31 (32-bit buffer offsets)
+    if ((int64_t)tile_m * N * 4 >= (int64_t)INT32_MAX)
+        return fail(MK_ERR_SHAPE, "N (%lld) too large for tile_m %d", (long long)N, tile_m);
+    const int64_t T = ((M + tile_m - 1) / tile_m) * ((N + tile_n - 1) / tile_n);
+    if (T >= (int64_t)kMaxTiles) return fail(MK_ERR_SHAPE, "too many tiles (%lld)", (long long)T);
+    if (!C) return fail(MK_ERR_INVALID_ARG, "C is NULL");
+    if (K > 0 && (!A || !B)) return fail(MK_ERR_INVALID_ARG, "A or B is NULL");
+    if (num_peers > 0 && !peers) return fail(MK_ERR_INVALID_ARG, "peers is NULL with num_peers > 0");
+    if (num_peers == 0 && peers) return fail(MK_ERR_INVALID_ARG, "peers must be NULL when num_peers == 0");
+    if (!aligned16(C) || (A && !aligned16(A)) || (B && !aligned16(B)) || (peers && !aligned16(peers)))
+        return fail(MK_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+    return MK_OK;
+}
+
+int current_device(int *dev) {
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess || count == 0) {
+        (void)hipGetLastError();
+        return fail(MK_ERR_NO_DEVICE, "no HIP device visible");
+    }
+    e = hipGetDevice(dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (*dev < 0 || *dev >= kMaxDevices) return fail(MK_ERR_NO_DEVICE, "device index out of range");
+    return MK_OK;
+}
+
+int device_state(DevState **out) {
+    int dev = 0;
+    int rc = current_device(&dev);
+    if (rc) return rc;
+    DevState &d = g_dev[dev];
+    if (!d.init) {
+        hipDeviceProp_t prop;
+        hipError_t e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+        d.num_cu = prop.multiProcessorCount;
+        int khz = 0;
+        if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0)
+            d.timer_hz = (uint64_t)khz * 1000ull;
+        d.init = true;
+    }
+    *out = &d;
+    return MK_OK;
+}
+
+// Make room for T tiles and Ch chunks.  A new workspace is zeroed (flags at
+// 0 never equal an epoch, which starts at 1) and its control blocks set.
+int ensure_workspace(DevState &d, uint32_t T, uint32_t Ch, hipStream_t s) {
+    if (d.ws && T <= d.Tcap && Ch <= d.Chcap) return MK_OK;
+    uint32_t Tcap = d.Tcap, Chcap = d.Chcap;
+    while (Tcap < T) Tcap = Tcap ? 2 * Tcap : 4096;
+    while (Chcap < Ch) Chcap = Chcap ? 2 * Chcap : 1024;
+    if (d.ws) {
+        hipError_t e = hipDeviceSynchronize();
+        if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+        e = hipFree(d.ws);
+        d.ws = nullptr;
+        if (e != hipSuccess) return hip_fail(e, "hipFree");
+    }
+    const Layout L = layout_for(Tcap, Chcap);
+    hipError_t e = hipMalloc((void **)&d.ws, L.total);
+    if (e != hipSuccess) {
+        d.ws = nullptr;
+        return hip_fail(e, "hipMalloc(workspace)");
+    }
+    d.ws_bytes = L.total;
+    d.Tcap = Tcap;
+    d.Chcap = Chcap;
+    // a fill kernel rather than hipMemsetAsync, so the sequence stays valid
+    // inside a captured graph
+    e = launch_fill_u32((uint32_t *)d.ws, 0u, (int64_t)(L.total / 4), s);
+    if (e != hipSuccess) return hip_fail(e, "workspace clear launch");
+    WsView v = view_of(d);
+    e = launch_ws_init(v.live, v.snap, s);
+    if (e != hipSuccess) return hip_fail(e, "workspace init launch");
+    d.epoch = 0;
+    d.calls = 0;
+    d.shape_T = 0;
+    d.shape_tpc = 0;
+    d.dirty = false;
+    d.last.valid = false;
+    return MK_OK;
+}
+
+int run(bool fused, const void *A, const void *B, const float *peers, int num_peers, float *C,
+        int64_t M, int64_t N, int64_t K, int tile_m, int tile_n, int tpc, void *stream) {
+    int rc = check_args(A, B, peers, num_peers, C, M, N, K, tile_m, tile_n, tpc);
+    if (rc) return rc;
+    if (M == 0 || N == 0) return MK_OK;
+    const Settings set = g_set;
+    DevState *dp = nullptr;
+    rc = device_state(&dp);
+    if (rc) return rc;
+    DevState &d = *dp;
+    hipStream_t s = (hipStream_t)stream;
+
+    const int tiles_m = (int)((M + tile_m - 1) / tile_m);
+    const int tiles_n = (int)((N + tile_n - 1) / tile_n);
+    const uint32_t T = (uint32_t)tiles_m * (uint32_t)tiles_n;
+    const uint32_t Ch = (T + tpc - 1) / tpc;
+
+    if (!fused) {
+        GemmArgs g;
+        g.A = (const uint16_t *)A;
+        g.B = (const uint16_t *)B;
+        g.C = C;
+        g.M = M;
+        g.N = N;
+        g.K = K;
+        g.tiles_m = tiles_m;
+        g.tiles_n = tiles_n;
+        g.tpc = tpc;
+        g.group_m = set.group_m;
+        hipError_t e = launch_gemm(tile_m, tile_n, g, s);
+        if (e != hipSuccess) return hip_fail(e, "GEMM launch");
+        if (num_peers > 0) {
+            ReduceArgs r;
+            r.peers = peers;
+            r.C = C;
+            r.MN = M * N;
+            r.count4 = M * N / 4;
+            r.P = num_peers;
+            e = launch_reduce(r, d.num_cu, s);
+            if (e != hipSuccess) return hip_fail(e, "reduce launch");
+        }
+        return MK_OK;
+    }
+
+    const int nwg = set.num_wg ? set.num_wg : (d.num_cu < kMaxWG ? d.num_cu : kMaxWG);
+    if (nwg < 2 || nwg > d.num_cu)
+        return fail(MK_ERR_INVALID_ARG, "workgroups %d outside [2, %d compute units]", nwg, d.num_cu);
+    int ns_init = set.n_reduce;
+    if (set.mode == MK_PART_ADAPTIVE) {
+        if (ns_init == 0) ns_init = 2;
+        if (ns_init > nwg - 1) ns_init = nwg - 1;
+        if (ns_init < 1) ns_init = 1;
+    } else if (ns_init < 1 || ns_init > nwg - 1) {
+        return fail(MK_ERR_INVALID_ARG, "static reduce count %d outside [1, %d]", ns_init, nwg - 1);
+    }
+
+    rc = ensure_workspace(d, T, Ch, s);
+    if (rc) return rc;
+    WsView v = view_of(d);
+    hipError_t e;
+    if (d.dirty) {
+        // a launch ended early: control block and counters are not trustworthy
+        e = launch_ws_init(v.live, v.snap, s);
+        if (e != hipSuccess) return hip_fail(e, "workspace reinit launch");
+        d.shape_T = 0;
+        d.dirty = false;
+    }
+    if (T != d.shape_T || (uint32_t)tpc != d.shape_tpc) {
+        // new shape: per-call counters restart from zero (flags are epoch
+        // valued and need no clearing)
+        e = launch_fill_u32(v.tile_cnt, 0, d.Tcap, s);
+        if (e == hipSuccess) e = launch_fill_u32(v.chunk_cnt, 0, d.Chcap, s);
+        if (e != hipSuccess) return hip_fail(e, "counter clear launch");
+        d.calls = 0;
+        d.shape_T = T;
+        d.shape_tpc = (uint32_t)tpc;
+    }
+    if (d.epoch == 0xFFFFFFFFu) {
+        e = launch_fill_u32(v.tile_flag, 0, d.Tcap, s);
+        if (e == hipSuccess) e = launch_fill_u32(v.chunk_flag, 0, d.Chcap, s);
+        if (e != hipSuccess) return hip_fail(e, "flag clear launch");
+        d.epoch = 0;
+    }
+    d.epoch += 1;
+    d.calls += 1;
+
+    FusedArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.A = (const uint16_t *)A;
+    a.B = (const uint16_t *)B;
+    a.peers = peers;
+    a.C = C;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.P = num_peers;
+    a.tiles_m = tiles_m;
+    a.tiles_n = tiles_n;
+    a.T = T;
+    a.tpc = (uint32_t)tpc;
+    a.Ch = Ch;
+    a.epoch = d.epoch;
+    a.calls = d.calls;
+    a.mode = set.mode;
+    a.ns_init = ns_init;
+    a.ns_floor = set.floor;
+    a.nwg = nwg;
+    a.group_m = set.group_m;
+    a.timeout_ticks = set.timeout_us * (d.timer_hz / 1000000ull);
+    a.skip_publish = set.skip_publish;
+    a.ws = v;
+    e = launch_fused(tile_m, tile_n, a, s);
+    if (e != hipSuccess) {
+        d.dirty = true;
+        return hip_fail(e, "fused launch");
+    }
+    d.last.valid = true;
+    d.last.epoch = d.epoch;
+    d.last.calls = d.calls;
+    d.last.nwg = (uint32_t)nwg;
+    d.last.T = T;
+    d.last.Ch = Ch;
+    d.last.tpc = (uint32_t)tpc;
+    d.last.tm = (uint32_t)tile_m;
+    d.last.tn = (uint32_t)tile_n;
+    d.last.mode = (uint32_t)set.mode;
+    d.last.ns_init = (uint32_t)ns_init;
+    return MK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mk_gemm_reduce_local(const void *A, const void *B, const float *peers, int num_peers, float *C,
+                         int64_t M, int64_t N, int64_t K, int tile_m, int tile_n,
+                         int tiles_per_chunk, void *stream) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    return run(true, A, B, peers, num_peers, C, M, N, K, tile_m, tile_n, tiles_per_chunk, stream);
+}
+
+int mk_gemm_reduce_unfused(const void *A, const void *B, const float *peers, int num_peers,
+                           float *C, int64_t M, int64_t N, int64_t K, int tile_m, int tile_n,
+                           int tiles_per_chunk, void *stream) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    return run(false, A, B, peers, num_peers, C, M, N, K, tile_m, tile_n, tiles_per_chunk, stream);
+}
+
+int mk_set_partition(int mode, int n_reduce) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (mode != MK_PART_ADAPTIVE && mode != MK_PART_STATIC && mode != MK_PART_STATIC_DETERMINISTIC)
+        return fail(MK_ERR_INVALID_ARG, "unknown partition mode %d", mode);
+    if (n_reduce < 0 || n_reduce > kMaxWG) return fail(MK_ERR_INVALID_ARG, "n_reduce out of range");
+    if (mode != MK_PART_ADAPTIVE && n_reduce == 0)
+        return fail(MK_ERR_INVALID_ARG, "a static partition needs n_reduce >= 1");
+    g_set.mode = mode;
+    g_set.n_reduce = n_reduce;
+    return MK_OK;
+}
+
+int mk_set_controller_floor(int floor) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (floor < 1 || floor > kMaxWG) return fail(MK_ERR_INVALID_ARG, "floor must be in [1, 1024]");
+    g_set.floor = floor;
+    return MK_OK;
+}
+
+int mk_set_num_workgroups(int num_wg) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (num_wg != 0 && (num_wg < 2 || num_wg > kMaxWG))
+        return fail(MK_ERR_INVALID_ARG, "num_wg must be 0 or in [2, 1024]");
+    g_set.num_wg = num_wg;
+    return MK_OK;
+}
+
+int mk_set_timeout_us(uint64_t timeout_us) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (timeout_us == 0 || timeout_us > 600000000ull)
+        return fail(MK_ERR_INVALID_ARG, "timeout must be in (0, 600 s]");
+    g_set.timeout_us = timeout_us;
+    return MK_OK;
+}
+
+int mk_set_fault_skip_publish(int64_t tile) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (tile < -1) return fail(MK_ERR_INVALID_ARG, "tile must be >= -1");
+    g_set.skip_publish = tile;
+    return MK_OK;
+}
+
+int mk_get_stats(mk_stats *out, uint32_t *maps, size_t maps_len) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!out) return fail(MK_ERR_INVALID_ARG, "out is NULL");
+    if (out->struct_size != sizeof(mk_stats))
+        return fail(MK_ERR_INVALID_ARG, "struct_size %u != %zu", out->struct_size, sizeof(mk_stats));
+    DevState *dp = nullptr;
+    int rc = device_state(&dp);
+    if (rc) return rc;
+    DevState &d = *dp;
+    if (!d.last.valid || !d.ws) return fail(MK_ERR_INVALID_ARG, "no fused launch on this device yet");
+    const Launch &l = d.last;
+    const size_t need = 4ull * l.T + 2ull * l.Ch + 2ull * kTraceCap;
+    if (maps && maps_len < need)
+        return fail(MK_ERR_INVALID_ARG, "maps_len %zu < %zu words", maps_len, need);
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        d.dirty = true;
+        return hip_fail(e, "hipDeviceSynchronize");
+    }
+    const WsView v = view_of(d);
+    Live snap;
+    e = hipMemcpy(&snap, v.snap, sizeof snap, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy(stats)");
+
+    const uint32_t size = out->struct_size;
+    std::memset(out, 0, sizeof *out);
+    out->struct_size = size;
+    out->epoch = l.epoch;
+    out->calls_since_reset = l.calls;
+    out->num_wg = l.nwg;
+    out->num_tiles = l.T;
+    out->num_chunks = l.Ch;
+    out->tiles_per_chunk = l.tpc;
+    out->tile_m = l.tm;
+    out->tile_n = l.tn;
+    out->mode = l.mode;
+    out->n_reduce_initial = l.ns_init;
+    out->n_reduce_final = snap.ns_final;
+    out->n_reduce_min_seen = snap.ns_min < l.ns_init ? snap.ns_min : l.ns_init;
+    out->n_reduce_max_seen = snap.ns_max > l.ns_init ? snap.ns_max : l.ns_init;
+    out->role_switches = snap.role_switches;
+    out->compute_tasks = (uint32_t)(snap.role_compute & kCountMask);
+    out->reduce_tasks = (uint32_t)(snap.role_reduce & kCountMask);
+    out->chunks_released = snap.chunks_released;
+    out->invariant_violations = snap.violations;
+    out->ns_trace_len = snap.trace_len < (uint32_t)kTraceCap ? snap.trace_len : (uint32_t)kTraceCap;
+    out->sum_cycles_compute = snap.role_compute >> kCountBits;
+    out->sum_cycles_reduce = snap.role_reduce >> kCountBits;
+    out->kernel_ticks_start = snap.t_start;
+    out->kernel_ticks_end = snap.t_end;
+    out->reduce_ticks_start = snap.r_start;
+    out->reduce_ticks_end = snap.r_end;
+    out->timer_hz = d.timer_hz;
+
+    if (maps) {
+        uint32_t *p = maps;
+        struct { const uint32_t *src; size_t n; } parts[] = {
+            {v.tile_flag, l.T}, {v.tile_cnt, l.T}, {v.chunk_cnt, l.Ch}, {v.chunk_flag, l.Ch},
+            {v.cowner, l.T}, {v.rowner, l.T}, {v.trace, 2ull * kTraceCap}};
+        for (auto &pt : parts) {
+            e = hipMemcpy(p, pt.src, 4 * pt.n, hipMemcpyDeviceToHost);
+            if (e != hipSuccess) return hip_fail(e, "hipMemcpy(maps)");
+            p += pt.n;
+        }
+    }
+    if (snap.error == kErrTimeout) {
+        d.dirty = true;
+        out->status = MK_ERR_TIMEOUT;
+        fail(MK_ERR_TIMEOUT, "a bounded wait in the fused kernel expired");
+        return MK_ERR_TIMEOUT;
+    }
+    if (snap.violations) {
+        out->status = MK_ERR_PROTOCOL;
+        fail(MK_ERR_PROTOCOL, "%u flag/counter violations", snap.violations);
+        return MK_ERR_PROTOCOL;
+    }
+    out->status = MK_OK;
+    return MK_OK;
+}
+
+int mk_controller_eval(const uint64_t *in, uint32_t *out, int n, void *stream) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (n < 0) return fail(MK_ERR_INVALID_ARG, "n < 0");
+    if (n == 0) return MK_OK;
+    if (!in || !out) return fail(MK_ERR_INVALID_ARG, "NULL table");
+    int dev = 0;
+    int rc = current_device(&dev);
+    if (rc) return rc;
+    hipError_t e = launch_controller_eval(in, out, n, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "controller eval launch");
+    return MK_OK;
+}
+
+int mk_device_cu_count(void) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    DevState *dp = nullptr;
+    int rc = device_state(&dp);
+    if (rc) return rc;
+    return dp->num_cu;
+}
+
+int mk_release_workspace(void) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    int dev = 0;
+    int rc = current_device(&dev);
+    if (rc) return rc;
+    DevState &d = g_dev[dev];
+    if (d.ws) {
+        hipError_t e = hipDeviceSynchronize();
+        if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+        e = hipFree(d.ws);
+        if (e != hipSuccess) return hip_fail(e, "hipFree");
+    }
+    d.ws = nullptr;
+    d.ws_bytes = 0;
+    d.Tcap = d.Chcap = 0;
+    d.last.valid = false;
+    return MK_OK;
+}
+
+const char *mk_last_error(void) { return g_last_error.c_str(); }
+
+int mk_abi_version(void) { return MK_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// Internal definitions shared by the kernels (mk_kernels.hip) and the C ABI
+// (mk_api.hip).  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mk {
+
+constexpr int kThreads = 256;         // 4 wave64 per workgroup, one workgroup per CU
+constexpr int kBK = 64;               // K slab staged in LDS per pipeline step
+constexpr int kMaxWG = 1024;
+constexpr uint32_t kMaxTiles = 1u << 22;
+constexpr uint64_t kCostCap = (1ull << 26) - 1;   // per-task mean cycles saturate here
+constexpr int kTraceCap = 1024;
+constexpr int kFusedLdsBytes = 96 * 1024;         // > half of the 160 KiB LDS: 1 WG per CU
+
+enum Mode : int32_t { kAdaptive = 0, kStatic = 1, kDeterministic = 2 };
+enum Err : uint32_t { kErrNone = 0, kErrTimeout = 1 };
+
+// Per-launch control block in device memory.  The last workgroup to leave a
+// launch copies it into the snapshot and restores the initial values below,
+// so every launch starts from the same state without a host-side clear.
+// Each role's progress is one 64-bit word, (cycle sum << kCountBits) | tasks,
+// so one atomic both records a finished task and returns what the controller
+// needs.
+constexpr int kCountBits = 22;
+constexpr uint64_t kCountMask = (1ull << kCountBits) - 1;
+
+struct alignas(256) Live {
+    uint32_t compute_claim;    // next compute claim index           (init 0)
+    uint32_t reduce_claim;     // next reduce ticket                 (init 0)
+    uint32_t exit_count;       // workgroups that left               (init 0)
+    uint32_t target_ns;        // controller target, 0 = unset       (init 0)
+    uint32_t role_switches;    //                                    (init 0)
+    uint32_t chunks_released;  //                                    (init 0)
+    uint32_t violations;       //                                    (init 0)
+    uint32_t error;            // Err                                (init 0)
+    uint32_t ns_min;           //                                    (init ~0)
+    uint32_t ns_max;           //                                    (init 0)
+    uint32_t trace_len;        //                                    (init 0)
+    uint32_t ns_final;         // written at exit                    (init 0)
+    uint32_t pad0[4];
+    uint64_t role_compute;     // (cycles << kCountBits) | tasks     (init 0)
+    uint64_t role_reduce;      //                                    (init 0)
+    uint64_t t_start;          // min over workgroups                (init ~0)
+    uint64_t t_end;            // max                                (init 0)
+    uint64_t r_start;          // min over reduce tasks              (init ~0)
+    uint64_t r_end;            // max                                (init 0)
+};
+
+// Workspace: one device allocation per device.
+//   [Live][Live snapshot][trace 2*kTraceCap u32]
+//   [tile_flag Tcap][tile_cnt Tcap][chunk_cnt Chcap][chunk_flag Chcap]
+//   [compute_owner Tcap][reduce_owner Tcap]
+struct WsView {
+    Live *live;
+    Live *snap;
+    uint32_t *trace;
+    uint32_t *tile_flag;
+    uint32_t *tile_cnt;
+    uint32_t *chunk_cnt;
+    uint32_t *chunk_flag;
+    uint32_t *cowner;
+    uint32_t *rowner;
+};
+
+struct FusedArgs {
+    const uint16_t *A;        // bf16 [M,K]
+    const uint16_t *B;        // bf16 [K,N]
+    const float *peers;       // fp32 [P,M,N]
+    float *C;                 // fp32 [M,N]
+    int64_t M, N, K;
+    int32_t P;
+    int32_t tiles_m, tiles_n;
+    uint32_t T, tpc, Ch;
+    uint32_t epoch;           // value written into flags this launch
+    uint32_t calls;           // launches of this shape since the counters were cleared
+    int32_t mode;
+    int32_t ns_init;          // static count, or initial adaptive target
+    int32_t ns_floor;
+    int32_t nwg;              // B
+    int32_t group_m;          // tile-row band height of the claim order
+    int32_t pad0;
+    uint64_t timeout_ticks;   // bound on any wait, constant-clock ticks
+    int64_t skip_publish;     // fault injection: tile whose flag is never set (-1 none)
+    WsView ws;
+};
+
+struct GemmArgs {
+    const uint16_t *A;
+    const uint16_t *B;
+    float *C;
+    int64_t M, N, K;
+    int32_t tiles_m, tiles_n;
+    int32_t tpc, group_m;
+};
+
+struct ReduceArgs {
+    const float *peers;
+    float *C;
+    int64_t count4;           // M*N/4 float4 elements
+    int64_t MN;
+    int32_t P;
+};
+
+// Host-side launchers (defined in mk_kernels.hip).  Return hipSuccess or the
+// launch error.
+hipError_t launch_fused(int tile_m, int tile_n, const FusedArgs &a, hipStream_t s);
+hipError_t launch_gemm(int tile_m, int tile_n, const GemmArgs &a, hipStream_t s);
+hipError_t launch_reduce(const ReduceArgs &a, int num_cu, hipStream_t s);
+hipError_t launch_ws_init(Live *live, Live *snap, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t *p, uint32_t value, int64_t n, hipStream_t s);
+hipError_t launch_controller_eval(const uint64_t *in, uint32_t *out, int n, hipStream_t s);
+bool tile_supported(int tile_m, int tile_n);
+
+}  // namespace mk

@@ -1,0 +1,232 @@
+/*
+ * mk.h -- C ABI of the fused GEMM + tile-reduce library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The library computes one GPU's share of a GEMM+AllReduce in a single
+ * persistent kernel: the local partial C_r = A.B (bfloat16 operands, fp32
+ * accumulation on MFMA) and, as soon as each output tile of C_r exists, the
+ * sum of that tile with the R-1 other ranks' partial tiles.  On one GPU the
+ * other ranks' partials are fp32 buffers in local HBM ("peers").
+ *
+ * Sources (the method's pages; no code was published with them):
+ *  - "mKernel: Fast Multi-GPU, Multi-Node Fused Kernels", abstract: one
+ *    persistent kernel whose workgroups are split into compute and
+ *    communication roles, with an on-GPU controller that tunes the split at
+ *    run time; tiles are forwarded as soon as they are produced.
+ *  - MarkTechPost / chathome pages, five-kernel table, GEMM + AllReduce row:
+ *    C = A @ B with the partial outputs reduced across all ranks in one launch.
+ *  - "【学习】mKernel 分析": section 2.2 (Figure 2: compute blocks write a tile
+ *    and its readiness flag), section 2.3 (4 locally reduced tiles form a
+ *    chunk; a per-chunk counter lets the last tile release the chunk),
+ *    section 2.4 (static sweep of 2-64 communication SMs; adaptive controller
+ *    n_s* = B (R_s C_s) / (R_p C_p + R_s C_s); blocks re-check the target at
+ *    task boundaries), section 2.5 (a ready signal must name a completed
+ *    payload), section 4.1 (role by block index, ready flags, chunks).
+ *
+ * Conventions for every call:
+ *  - Returns an int status (mk_status).  No call aborts or throws.
+ *  - Argument checks run before any HIP call, so a bad argument is reported
+ *    without touching the GPU.
+ *  - Device pointers are plain HIP device addresses owned by the caller.
+ *    `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *  - Launches are asynchronous and stream ordered.  The library keeps one
+ *    workspace per device (flags, counters, owner maps, controller block);
+ *    calls on one device must not overlap in time (the library is not
+ *    reentrant across concurrent streams of one device).
+ *  - Timer ticks are from the GPU's constant-rate clock (s_memrealtime,
+ *    100 MHz on MI355X); cycle sums are from the shader clock (s_memtime).
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MK_ABI_VERSION 1
+
+typedef enum {
+    MK_OK = 0,
+    MK_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad tile, bad mode     */
+    MK_ERR_SHAPE = -2,       /* N or K not a multiple of 8, or too many tiles   */
+    MK_ERR_HIP = -3,         /* a HIP runtime call failed (see mk_last_error)   */
+    MK_ERR_TIMEOUT = -4,     /* a bounded wait in the kernel expired            */
+    MK_ERR_NO_DEVICE = -5,   /* no HIP device is visible                        */
+    MK_ERR_PROTOCOL = -6     /* the kernel counted a flag/counter violation     */
+} mk_status;
+
+typedef enum {
+    /* On-GPU controller sets the reduce-workgroup count from measured
+     * per-task cycle costs ("【学习】mKernel 分析" section 2.4).            */
+    MK_PART_ADAPTIVE = 0,
+    /* Fixed count of reduce workgroups; tasks are claimed dynamically.     */
+    MK_PART_STATIC = 1,
+    /* Fixed count; workgroup w < n reduces tiles t = w (mod n), workgroup
+     * w >= n computes tiles t = w - n (mod B - n), each in increasing t.   */
+    MK_PART_STATIC_DETERMINISTIC = 2
+} mk_part_mode;
+
+/*
+ * mk_gemm_reduce_local -- one persistent launch computing
+ *     C[i][j] = sum_k A[i][k] * B[k][j]  +  sum_{p < num_peers} peers[p][i][j]
+ * (GEMM + AllReduce row of the five-kernel table; fusion and tile-granular
+ * overlap per the abstract and the analysis page's Figure 2).
+ *
+ *   A          bfloat16 [M, K], row-major, 16-byte aligned (device).
+ *   B          bfloat16 [K, N], row-major, 16-byte aligned (device).
+ *   peers      fp32 [num_peers, M, N], contiguous, 16-byte aligned (device);
+ *              may be NULL only when num_peers == 0.  Read only.
+ *   num_peers  R - 1 >= 0.
+ *   C          fp32 [M, N], row-major, 16-byte aligned (device).  Receives the
+ *              local partial of each tile first, then the reduced tile.  Must
+ *              not overlap A, B or peers.
+ *   M, N, K    >= 0; N and K must be multiples of 8 (16-byte rows).  M, N
+ *              need not be multiples of the tile: edge tiles are masked.
+ *              K == 0 gives C = sum of peers; M == 0 or N == 0 returns MK_OK
+ *              without a launch.
+ *   tile_m, tile_n   output tile (the compute and reduce unit): one of
+ *              64x64, 128x128, 256x128.
+ *   tiles_per_chunk  tiles per chunk (1..64; 4 in the method's
+ *              GEMM+AllReduce).  Chunk c holds tiles [c*tpc, (c+1)*tpc) in
+ *              row-major tile order; the last chunk may be short.
+ *   stream     hipStream_t or NULL.
+ *
+ * Uses the partition set by mk_set_partition.  Errors: MK_ERR_INVALID_ARG,
+ * MK_ERR_SHAPE (nothing launched), MK_ERR_NO_DEVICE, MK_ERR_HIP.  Kernel-side
+ * timeouts and protocol violations are reported by mk_get_stats.
+ */
+int mk_gemm_reduce_local(const void *A, const void *B, const float *peers, int num_peers,
+                         float *C, int64_t M, int64_t N, int64_t K,
+                         int tile_m, int tile_n, int tiles_per_chunk, void *stream);
+
+/*
+ * mk_gemm_reduce_unfused -- the unfused two-kernel baseline with the same
+ * arguments and result: a GEMM kernel writes the fp32 partial into C, then a
+ * separate reduce kernel adds the peers (the host-driven, kernel-granular
+ * overlap the abstract contrasts with fused kernels).  tiles_per_chunk is
+ * checked but unused.  Touches no workspace state.
+ */
+int mk_gemm_reduce_unfused(const void *A, const void *B, const float *peers, int num_peers,
+                           float *C, int64_t M, int64_t N, int64_t K,
+                           int tile_m, int tile_n, int tiles_per_chunk, void *stream);
+
+/*
+ * mk_set_partition -- partition of the persistent workgroups into reduce and
+ * compute roles for subsequent mk_gemm_reduce_local launches (process-wide).
+ *   mode       mk_part_mode.
+ *   n_reduce   STATIC*: reduce-workgroup count, must lie in [1, B-1] at launch
+ *              time (B = workgroups of the launch).  ADAPTIVE: initial count
+ *              (0 selects 2, the low end of the page's 2-64 sweep).
+ * Errors: MK_ERR_INVALID_ARG for an unknown mode or negative n_reduce.
+ */
+int mk_set_partition(int mode, int n_reduce);
+
+/*
+ * mk_set_controller_floor -- smallest reduce count the adaptive controller
+ * may choose while compute remains (default 2; clamped to B-1 at run time).
+ */
+int mk_set_controller_floor(int floor);
+
+/*
+ * mk_set_num_workgroups -- persistent workgroups per launch (B).  0 (default)
+ * = one per compute unit (256 on MI355X).  Valid: 0 or 2..1024, and at most
+ * the compute-unit count at launch time (one workgroup per CU is required for
+ * every workgroup to be resident).
+ */
+int mk_set_num_workgroups(int num_wg);
+
+/*
+ * mk_set_timeout_us -- bound on every wait inside the fused kernel, in
+ * microseconds of GPU constant-rate clock (default 2 000 000).  A workgroup
+ * whose wait expires records MK_ERR_TIMEOUT and leaves the kernel; the others
+ * see the error and leave too, so the kernel always ends.
+ */
+int mk_set_timeout_us(uint64_t timeout_us);
+
+/*
+ * mk_set_fault_skip_publish -- fault injection for tests: the compute task of
+ * tile `tile` writes its partial but never sets its readiness flag, so the
+ * launch must end with MK_ERR_TIMEOUT.  -1 (default) disables it.
+ */
+int mk_set_fault_skip_publish(int64_t tile);
+
+/* Statistics of the most recent completed mk_gemm_reduce_local launch. */
+typedef struct mk_stats {
+    uint32_t struct_size;         /* in: sizeof(mk_stats) as the caller knows it */
+    int32_t status;               /* MK_OK, MK_ERR_TIMEOUT or MK_ERR_PROTOCOL    */
+    uint32_t epoch;               /* epoch value the launch wrote into flags     */
+    uint32_t calls_since_reset;   /* launches of this shape since counters reset */
+    uint32_t num_wg;              /* B                                           */
+    uint32_t num_tiles;           /* T                                           */
+    uint32_t num_chunks;          /* ceil(T / tiles_per_chunk)                   */
+    uint32_t tiles_per_chunk;
+    uint32_t tile_m, tile_n;
+    uint32_t mode;                /* mk_part_mode                                */
+    uint32_t n_reduce_initial;
+    uint32_t n_reduce_final;      /* target when the last workgroup left         */
+    uint32_t n_reduce_min_seen;   /* over controller updates and the initial    */
+    uint32_t n_reduce_max_seen;
+    uint32_t role_switches;       /* workgroups changing role between tasks      */
+    uint32_t compute_tasks;       /* compute tasks finished (== T)               */
+    uint32_t reduce_tasks;        /* reduce tasks finished (== T)                */
+    uint32_t chunks_released;     /* chunks whose last tile was reduced (== Ch)  */
+    uint32_t invariant_violations;/* flag/counter mismatches seen on the device  */
+    uint32_t ns_trace_len;        /* entries in the controller trace             */
+    uint32_t reserved0;
+    uint64_t sum_cycles_compute;  /* shader-clock cycles over compute tasks      */
+    uint64_t sum_cycles_reduce;   /* shader-clock cycles over reduce tasks       */
+    uint64_t kernel_ticks_start;  /* first workgroup start (constant clock)      */
+    uint64_t kernel_ticks_end;    /* last workgroup end                          */
+    uint64_t reduce_ticks_start;  /* first reduce task start                     */
+    uint64_t reduce_ticks_end;    /* last reduce task end                        */
+    uint64_t timer_hz;            /* constant clock frequency                    */
+} mk_stats;
+
+/* Words per map in the optional `maps` output of mk_get_stats, in order:
+ *   tile_flag[T] | tile_reduce_cnt[T] | chunk_cnt[Ch] | chunk_flag[Ch] |
+ *   compute_owner[T] | reduce_owner[T] | ns_trace[2 * MK_TRACE_CAP]
+ * Owner words are (reduce target seen << 16) | workgroup.  Trace entries are
+ * pairs (ticks since kernel start, new target). */
+#define MK_TRACE_CAP 1024
+
+/*
+ * mk_get_stats -- waits for the last fused launch on the current device
+ * (hipStreamSynchronize of its stream), then fills *out.  If maps is non-NULL
+ * it receives the maps above (maps_len is its capacity in uint32 words; it
+ * must hold 4T + 2Ch + 2*MK_TRACE_CAP words).  out->struct_size must be set.
+ * Returns out->status (MK_OK when the launch was clean), or an argument/HIP
+ * error.  A launch that ended in a timeout leaves the workspace to be cleared
+ * at the next launch.
+ */
+int mk_get_stats(mk_stats *out, uint32_t *maps, size_t maps_len);
+
+/*
+ * mk_controller_eval -- evaluates the device's controller step on a table,
+ * for parity tests against the host closed form.  `in` holds n rows of eight
+ * uint64 (device memory): B, T, compute_done, reduce_done,
+ * sum_cycles_compute, sum_cycles_reduce, current_target, floor.  `out`
+ * (device, n uint32) receives the new target for each row.  Limits: B in
+ * [2, 1024], T < 2^22.  Asynchronous on `stream`.
+ */
+int mk_controller_eval(const uint64_t *in, uint32_t *out, int n, void *stream);
+
+/* Number of compute units of the current device, or a negative mk_status. */
+int mk_device_cu_count(void);
+
+/* Frees the current device's workspace (the next launch allocates anew). */
+int mk_release_workspace(void);
+
+/* Text of the last error on the calling thread ("" if none). */
+const char *mk_last_error(void);
+
+/* MK_ABI_VERSION of the built library. */
+int mk_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MK_H */

@@ -1,0 +1,149 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/mk.h declares, its stats struct matches the binding, and argument
+checks answer before any HIP call (no compute is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mk.h")
+
+
+@pytest.fixture(scope="module")
+def mk():
+    from gemm_tile_granular_amd import build
+    if build.is_stale():
+        build.build()
+    import gemm_tile_granular_amd as mk
+    return mk
+
+
+def _header():
+    with open(HEADER) as f:
+        return f.read()
+
+
+def _declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", _header(), flags=re.S)
+    return sorted(set(re.findall(r"\b(mk_[a-z_0-9]+)\s*\(", text)))
+
+
+def _gpu_present():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+def test_every_declared_symbol_is_exported(mk):
+    names = _declared_functions()
+    assert "mk_gemm_reduce_local" in names and "mk_get_stats" in names
+    lib = ctypes.CDLL(mk.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    # and the binding declares a signature for each one
+    assert sorted(mk.SIGNATURES) == names
+
+
+def test_stats_struct_matches_header(mk):
+    text = _header()
+    body = re.search(r"typedef struct mk_stats \{(.*?)\} mk_stats;", text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if not decl:
+            continue
+        ctype, names = decl.split(None, 1)
+        for n in names.split(","):
+            fields.append((n.strip(), ctype))
+    want = {"uint32_t": ctypes.c_uint32, "int32_t": ctypes.c_int32, "uint64_t": ctypes.c_uint64}
+    got = [(n, t) for n, t in mk.Stats._fields_]
+    assert [n for n, _ in got] == [n for n, _ in fields]
+    assert all(t == want[c] for (_, t), (_, c) in zip(got, fields))
+    assert ctypes.sizeof(mk.Stats) == 144
+
+
+def test_abi_version_and_trace_cap(mk):
+    assert mk.abi_version() == int(re.search(r"#define MK_ABI_VERSION (\d+)", _header()).group(1))
+    assert mk.TRACE_CAP == int(re.search(r"#define MK_TRACE_CAP (\d+)", _header()).group(1))
+
+
+# fake, never dereferenced addresses (16-byte aligned unless stated)
+A, B, P, C = 0x10000, 0x20000, 0x30000, 0x40000
+
+
+def _call(mk, **kw):
+    args = dict(A=A, B=B, peers=P, num_peers=3, C=C, M=256, N=256, K=512, tm=64, tn=64, tpc=4)
+    args.update(kw)
+    return mk.lib.mk_gemm_reduce_local(args["A"], args["B"], args["peers"], args["num_peers"],
+                                       args["C"], args["M"], args["N"], args["K"], args["tm"],
+                                       args["tn"], args["tpc"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), -1), (dict(K=-8), -1), (dict(num_peers=-1), -1),
+    (dict(tm=32, tn=32), -1), (dict(tm=128, tn=64), -1), (dict(tpc=0), -1), (dict(tpc=65), -1),
+    (dict(N=260), -2), (dict(K=100), -2), (dict(M=1 << 31), -2),
+    (dict(M=1 << 22, N=1 << 16), -2),
+    (dict(C=0), -1), (dict(A=0), -1), (dict(B=0), -1), (dict(peers=0), -1),
+    (dict(num_peers=0), -1),                 # peers given but num_peers == 0
+    (dict(A=A + 8), -1), (dict(C=C + 4), -1), (dict(peers=P + 2), -1),
+])
+def test_argument_errors_before_any_gpu_call(mk, kw, code):
+    assert _call(mk, **kw) == code
+    assert mk.lib.mk_last_error().decode()
+    # the unfused entry point applies the same checks
+    args = dict(A=A, B=B, peers=P, num_peers=3, C=C, M=256, N=256, K=512, tm=64, tn=64, tpc=4)
+    args.update(kw)
+    assert mk.lib.mk_gemm_reduce_unfused(args["A"], args["B"], args["peers"], args["num_peers"],
+                                         args["C"], args["M"], args["N"], args["K"], args["tm"],
+                                         args["tn"], args["tpc"], None) == code
+
+
+def test_empty_output_is_a_no_op(mk):
+    assert _call(mk, M=0) == 0
+    assert _call(mk, N=0) == 0
+    assert _call(mk, M=0, A=0, B=0, C=0, peers=0, num_peers=0) == 0
+
+
+@pytest.mark.skipif(_gpu_present(), reason="fake pointers must never reach a real GPU")
+def test_valid_arguments_without_a_device_report_no_device(mk):
+    assert _call(mk) == mk.MK_ERR_NO_DEVICE
+    assert mk.lib.mk_device_cu_count() == mk.MK_ERR_NO_DEVICE
+
+
+def test_setting_calls_validate(mk):
+    lib = mk.lib
+    assert lib.mk_set_partition(7, 2) == -1
+    assert lib.mk_set_partition(mk.PART_STATIC, 0) == -1
+    assert lib.mk_set_partition(mk.PART_STATIC, -3) == -1
+    assert lib.mk_set_partition(mk.PART_ADAPTIVE, 0) == 0
+    assert lib.mk_set_num_workgroups(1) == -1
+    assert lib.mk_set_num_workgroups(4096) == -1
+    assert lib.mk_set_num_workgroups(0) == 0
+    assert lib.mk_set_timeout_us(0) == -1
+    assert lib.mk_set_timeout_us(2000000) == 0
+    assert lib.mk_set_fault_skip_publish(-2) == -1
+    assert lib.mk_set_fault_skip_publish(-1) == 0
+    assert lib.mk_set_controller_floor(0) == -1
+    assert lib.mk_set_controller_floor(2) == 0
+    assert lib.mk_controller_eval(None, None, -1, None) == -1
+    assert lib.mk_controller_eval(None, None, 0, None) == 0
+
+
+def test_get_stats_rejects_bad_struct(mk):
+    assert mk.lib.mk_get_stats(None, None, 0) == -1
+    st = mk.Stats()
+    st.struct_size = 12
+    assert mk.lib.mk_get_stats(ctypes.byref(st), None, 0) == -1
+
+
+def test_binding_rejects_wrong_tensor_types(mk):
+    torch = pytest.importorskip("torch")
+    a = torch.zeros(4, 8, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        mk.gemm_reduce_local(a, a, None, a, 64, 64)
