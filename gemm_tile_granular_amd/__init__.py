@@ -213,7 +213,7 @@ def get_stats(maps: bool = False, raise_on_error: bool = True) -> Dict:
         if rc0 not in (MK_OK, MK_ERR_TIMEOUT, MK_ERR_PROTOCOL):
             _check(rc0)
         T, Ch = st.num_tiles, st.num_chunks
-        n = 4 * T + 2 * Ch + 2 * TRACE_CAP
+        n = 10 * T + 2 * Ch + 2 * TRACE_CAP
         buf = np.zeros(n, dtype=np.uint32)
         st = Stats()
         st.struct_size = ctypes.sizeof(Stats)
@@ -225,10 +225,20 @@ def get_stats(maps: bool = False, raise_on_error: bool = True) -> Dict:
         o = 0
         for key, cnt in (("tile_flag", T), ("tile_reduce_cnt", T), ("chunk_cnt", Ch),
                          ("chunk_flag", Ch), ("compute_owner", T), ("reduce_owner", T),
-                         ("ns_trace", 2 * TRACE_CAP)):
+                         ("ns_trace", 2 * TRACE_CAP), ("compute_start", T), ("compute_end", T),
+                         ("reduce_start", T), ("reduce_end", T), ("compute_choice_ticks", T),
+                         ("reduce_choice_ticks", T)):
             out[key] = buf[o:o + cnt].copy()
             o += cnt
         out["ns_trace"] = out["ns_trace"].reshape(TRACE_CAP, 2)[: st.ns_trace_len]
+        # timeline in microseconds since the kernel started
+        t0 = np.uint32(st.kernel_ticks_start & 0xFFFFFFFF)
+        us = 1e6 / float(st.timer_hz or 100_000_000)
+        for key in ("compute_start", "compute_end", "reduce_start", "reduce_end"):
+            out[key + "_us"] = (out[key] - t0).astype(np.uint32).astype(np.float64) * us
+        out["ns_trace_us"] = (out["ns_trace"][:, 0] - t0).astype(np.uint32).astype(np.float64) * us
+        out["compute_choice_us"] = out["compute_choice_ticks"].astype(np.float64) * us
+        out["reduce_choice_us"] = out["reduce_choice_ticks"].astype(np.float64) * us
     if raise_on_error and rc not in (MK_OK,):
         _check(rc)
     out["rc"] = rc

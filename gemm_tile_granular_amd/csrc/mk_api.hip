@@ -71,7 +71,7 @@ DevState g_dev[kMaxDevices];
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Layout {
-    size_t live, snap, trace, tile_flag, tile_cnt, chunk_cnt, chunk_flag, cowner, rowner, total;
+    size_t live, snap, trace, tile_flag, tile_cnt, chunk_cnt, chunk_flag, cowner, rowner, timeline, total;
 };
 
 Layout layout_for(uint32_t Tcap, uint32_t Chcap) {
@@ -86,6 +86,7 @@ Layout layout_for(uint32_t Tcap, uint32_t Chcap) {
     L.chunk_flag = o; o = align_up(o + 4ull * Chcap, 256);
     L.cowner = o; o = align_up(o + 4ull * Tcap, 256);
     L.rowner = o; o = align_up(o + 4ull * Tcap, 256);
+    L.timeline = o; o = align_up(o + 24ull * Tcap, 256);
     L.total = o;
     return L;
 }
@@ -102,10 +103,17 @@ WsView view_of(const DevState &d) {
     v.chunk_flag = (uint32_t *)(d.ws + L.chunk_flag);
     v.cowner = (uint32_t *)(d.ws + L.cowner);
     v.rowner = (uint32_t *)(d.ws + L.rowner);
+    v.timeline = (uint32_t *)(d.ws + L.timeline);
     return v;
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Partitions of the claim order: one per XCD (workgroup w runs on XCD w mod 8
+// on MI355X) when the grid spans whole XCDs, else a single partition.
+int xcd_partitions(int nwg, int num_cu) {
+    return (num_cu % kMaxXcd == 0 && nwg >= 2 * kMaxXcd && nwg % kMaxXcd == 0) ? kMaxXcd : 1;
+}
 
 // All argument checks that do not need the GPU.
 int check_args(const void *A, const void *B, const float *peers, int num_peers, const float *C,
@@ -122,9 +130,12 @@ int check_args(const void *A, const void *B, const float *peers, int num_peers, 
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
         return fail(MK_ERR_SHAPE, "dimension exceeds 2^31-1");
     if (M == 0 || N == 0) return MK_OK;
-    // byte offsets inside one tile row band stay below 2^31 (32-bit buffer offsets)
-    if ((int64_t)tile_m * N * 4 >= (int64_t)INT32_MAX)
-        return fail(MK_ERR_SHAPE, "N (%lld) too large for tile_m %d", (long long)N, tile_m);
+    // byte offsets inside one tile's row band (and one K slab) stay below 2^31
+    // (32-bit buffer offsets)
+    if ((int64_t)tile_m * N * 4 >= (int64_t)INT32_MAX || (int64_t)tile_m * K * 2 >= (int64_t)INT32_MAX ||
+        (int64_t)64 * N * 2 >= (int64_t)INT32_MAX)
+        return fail(MK_ERR_SHAPE, "N (%lld) or K (%lld) too large for 32-bit in-tile offsets",
+                    (long long)N, (long long)K);
     const int64_t T = ((M + tile_m - 1) / tile_m) * ((N + tile_n - 1) / tile_n);
     if (T >= (int64_t)kMaxTiles) return fail(MK_ERR_SHAPE, "too many tiles (%lld)", (long long)T);
     if (!C) return fail(MK_ERR_INVALID_ARG, "C is NULL");
@@ -236,7 +247,8 @@ int run(bool fused, const void *A, const void *B, const float *peers, int num_pe
         g.tiles_n = tiles_n;
         g.tpc = tpc;
         g.group_m = set.group_m;
-        hipError_t e = launch_gemm(tile_m, tile_n, g, s);
+        g.nxcd = xcd_partitions(d.num_cu, d.num_cu);
+        hipError_t e = launch_gemm(tile_m, tile_n, g, d.num_cu, s);
         if (e != hipSuccess) return hip_fail(e, "GEMM launch");
         if (num_peers > 0) {
             ReduceArgs r;
@@ -308,6 +320,7 @@ int run(bool fused, const void *A, const void *B, const float *peers, int num_pe
     a.T = T;
     a.tpc = (uint32_t)tpc;
     a.Ch = Ch;
+    a.Tcap = d.Tcap;
     a.epoch = d.epoch;
     a.calls = d.calls;
     a.mode = set.mode;
@@ -315,6 +328,7 @@ int run(bool fused, const void *A, const void *B, const float *peers, int num_pe
     a.ns_floor = set.floor;
     a.nwg = nwg;
     a.group_m = set.group_m;
+    a.nxcd = xcd_partitions(nwg, d.num_cu);
     a.timeout_ticks = set.timeout_us * (d.timer_hz / 1000000ull);
     a.skip_publish = set.skip_publish;
     a.ws = v;
@@ -408,7 +422,7 @@ int mk_get_stats(mk_stats *out, uint32_t *maps, size_t maps_len) {
     DevState &d = *dp;
     if (!d.last.valid || !d.ws) return fail(MK_ERR_INVALID_ARG, "no fused launch on this device yet");
     const Launch &l = d.last;
-    const size_t need = 4ull * l.T + 2ull * l.Ch + 2ull * kTraceCap;
+    const size_t need = 10ull * l.T + 2ull * l.Ch + 2ull * kTraceCap;
     if (maps && maps_len < need)
         return fail(MK_ERR_INVALID_ARG, "maps_len %zu < %zu words", maps_len, need);
     hipError_t e = hipDeviceSynchronize();
@@ -455,7 +469,10 @@ int mk_get_stats(mk_stats *out, uint32_t *maps, size_t maps_len) {
         uint32_t *p = maps;
         struct { const uint32_t *src; size_t n; } parts[] = {
             {v.tile_flag, l.T}, {v.tile_cnt, l.T}, {v.chunk_cnt, l.Ch}, {v.chunk_flag, l.Ch},
-            {v.cowner, l.T}, {v.rowner, l.T}, {v.trace, 2ull * kTraceCap}};
+            {v.cowner, l.T}, {v.rowner, l.T}, {v.trace, 2ull * kTraceCap},
+            {v.timeline, l.T}, {v.timeline + d.Tcap, l.T}, {v.timeline + 2ull * d.Tcap, l.T},
+            {v.timeline + 3ull * d.Tcap, l.T}, {v.timeline + 4ull * d.Tcap, l.T},
+            {v.timeline + 5ull * d.Tcap, l.T}};
         for (auto &pt : parts) {
             e = hipMemcpy(p, pt.src, 4 * pt.n, hipMemcpyDeviceToHost);
             if (e != hipSuccess) return hip_fail(e, "hipMemcpy(maps)");

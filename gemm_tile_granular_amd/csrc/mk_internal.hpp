@@ -7,12 +7,12 @@
 
 namespace mk {
 
-constexpr int kThreads = 256;         // 4 wave64 per workgroup, one workgroup per CU
 constexpr int kBK = 64;               // K slab staged in LDS per pipeline step
 constexpr int kMaxWG = 1024;
 constexpr uint32_t kMaxTiles = 1u << 22;
 constexpr uint64_t kCostCap = (1ull << 26) - 1;   // per-task mean cycles saturate here
 constexpr int kTraceCap = 1024;
+constexpr int kMaxXcd = 8;            // XCDs on MI355X (tile partitions)
 constexpr int kFusedLdsBytes = 96 * 1024;         // > half of the 160 KiB LDS: 1 WG per CU
 
 enum Mode : int32_t { kAdaptive = 0, kStatic = 1, kDeterministic = 2 };
@@ -28,7 +28,7 @@ constexpr int kCountBits = 22;
 constexpr uint64_t kCountMask = (1ull << kCountBits) - 1;
 
 struct alignas(256) Live {
-    uint32_t compute_claim;    // next compute claim index           (init 0)
+    uint32_t compute_claim[kMaxXcd];  // next compute claim per partition (init 0)
     uint32_t reduce_claim;     // next reduce ticket                 (init 0)
     uint32_t exit_count;       // workgroups that left               (init 0)
     uint32_t target_ns;        // controller target, 0 = unset       (init 0)
@@ -40,7 +40,7 @@ struct alignas(256) Live {
     uint32_t ns_max;           //                                    (init 0)
     uint32_t trace_len;        //                                    (init 0)
     uint32_t ns_final;         // written at exit                    (init 0)
-    uint32_t pad0[4];
+    uint32_t pad0[5];
     uint64_t role_compute;     // (cycles << kCountBits) | tasks     (init 0)
     uint64_t role_reduce;      //                                    (init 0)
     uint64_t t_start;          // min over workgroups                (init ~0)
@@ -52,7 +52,7 @@ struct alignas(256) Live {
 // Workspace: one device allocation per device.
 //   [Live][Live snapshot][trace 2*kTraceCap u32]
 //   [tile_flag Tcap][tile_cnt Tcap][chunk_cnt Chcap][chunk_flag Chcap]
-//   [compute_owner Tcap][reduce_owner Tcap]
+//   [compute_owner Tcap][reduce_owner Tcap][timeline 6*Tcap]
 struct WsView {
     Live *live;
     Live *snap;
@@ -63,6 +63,7 @@ struct WsView {
     uint32_t *chunk_flag;
     uint32_t *cowner;
     uint32_t *rowner;
+    uint32_t *timeline;   // [6][Tcap]: compute start/end, reduce start/end, choice time compute/reduce
 };
 
 struct FusedArgs {
@@ -74,6 +75,7 @@ struct FusedArgs {
     int32_t P;
     int32_t tiles_m, tiles_n;
     uint32_t T, tpc, Ch;
+    uint32_t Tcap;            // workspace tile capacity (stride of the timeline rows)
     uint32_t epoch;           // value written into flags this launch
     uint32_t calls;           // launches of this shape since the counters were cleared
     int32_t mode;
@@ -81,7 +83,7 @@ struct FusedArgs {
     int32_t ns_floor;
     int32_t nwg;              // B
     int32_t group_m;          // tile-row band height of the claim order
-    int32_t pad0;
+    int32_t nxcd;             // tile partitions (XCDs) for the claim order
     uint64_t timeout_ticks;   // bound on any wait, constant-clock ticks
     int64_t skip_publish;     // fault injection: tile whose flag is never set (-1 none)
     WsView ws;
@@ -94,6 +96,7 @@ struct GemmArgs {
     int64_t M, N, K;
     int32_t tiles_m, tiles_n;
     int32_t tpc, group_m;
+    int32_t nxcd;
 };
 
 struct ReduceArgs {
@@ -107,7 +110,7 @@ struct ReduceArgs {
 // Host-side launchers (defined in mk_kernels.hip).  Return hipSuccess or the
 // launch error.
 hipError_t launch_fused(int tile_m, int tile_n, const FusedArgs &a, hipStream_t s);
-hipError_t launch_gemm(int tile_m, int tile_n, const GemmArgs &a, hipStream_t s);
+hipError_t launch_gemm(int tile_m, int tile_n, const GemmArgs &a, int num_cu, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs &a, int num_cu, hipStream_t s);
 hipError_t launch_ws_init(Live *live, Live *snap, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t *p, uint32_t value, int64_t n, hipStream_t s);

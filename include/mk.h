@@ -187,16 +187,21 @@ typedef struct mk_stats {
 
 /* Words per map in the optional `maps` output of mk_get_stats, in order:
  *   tile_flag[T] | tile_reduce_cnt[T] | chunk_cnt[Ch] | chunk_flag[Ch] |
- *   compute_owner[T] | reduce_owner[T] | ns_trace[2 * MK_TRACE_CAP]
+ *   compute_owner[T] | reduce_owner[T] | ns_trace[2 * MK_TRACE_CAP] |
+ *   compute_start[T] | compute_end[T] | reduce_start[T] | reduce_end[T] |
+ *   compute_choice_ticks[T] | reduce_choice_ticks[T]
  * Owner words are (reduce target seen << 16) | workgroup.  Trace entries are
- * pairs (ticks since kernel start, new target). */
+ * pairs (low 32 bits of the constant clock, new target).  The four timeline
+ * maps hold the low 32 bits of the constant clock at each task's start and
+ * end (compare with kernel_ticks_start modulo 2^32); the last two, the ticks
+ * the workgroup spent choosing the task (claim and readiness wait). */
 #define MK_TRACE_CAP 1024
 
 /*
  * mk_get_stats -- waits for the last fused launch on the current device
  * (hipStreamSynchronize of its stream), then fills *out.  If maps is non-NULL
  * it receives the maps above (maps_len is its capacity in uint32 words; it
- * must hold 4T + 2Ch + 2*MK_TRACE_CAP words).  out->struct_size must be set.
+ * must hold 10T + 2Ch + 2*MK_TRACE_CAP words).  out->struct_size must be set.
  * Returns out->status (MK_OK when the launch was clean), or an argument/HIP
  * error.  A launch that ended in a timeout leaves the workspace to be cleared
  * at the next launch.
