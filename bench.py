@@ -77,9 +77,9 @@ def summary(ms):
 
 
 def cpu_baseline(w, a, b, p, seconds):
-    """The oracle, as it stands, on row blocks of the workload until `seconds`
-    of CPU time have been spent (at least one block)."""
-    import numpy as np
+    """The oracle, as it stands, on row blocks of the workload, wrapping round
+    to the first row block, until `seconds` of wall time have been spent (at
+    least one block).  Scaled to TFLOP/s of the GEMM part, like `value`."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -88,29 +88,60 @@ def cpu_baseline(w, a, b, p, seconds):
         threads = os.cpu_count() or 1
     rb = max(1, min(w.M, 512))
     rows_done = 0
+    blocks = 0
     t_total = 0.0
     r0 = 0
-    while r0 < w.M and (t_total < seconds or rows_done == 0):
+    while t_total < seconds or rows_done == 0:
         r1 = min(w.M, r0 + rb)
-        sub_p = p[:, r0:r1, :]
         t = time.perf_counter()
-        oracle.gemm_reduce(a[r0:r1], b, sub_p)
+        oracle.gemm_reduce(a[r0:r1], b, p[:, r0:r1, :])
         t_total += time.perf_counter() - t
         rows_done += r1 - r0
-        r0 = r1
+        blocks += 1
+        r0 = 0 if r1 >= w.M else r1
     flops = 2.0 * rows_done * w.N * w.K
     return {
         "value": flops / t_total / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"float64 oracle (numpy/OpenBLAS) on rows [0, {rows_done}) of {w.M} "
-                  f"({w.name}: {rows_done}x{w.N}x{w.K} GEMM + {w.peers}-peer sum), "
-                  f"{t_total:.2f} s",
+        "sample": f"float64 oracle (numpy/OpenBLAS, {threads} threads) on {blocks} blocks of "
+                  f"{rb} rows ({rows_done} rows = {rows_done / w.M:.2f} passes over the "
+                  f"{w.M}x{w.N}x{w.K} GEMM + {w.peers}-peer sum of {w.name}), {t_total:.1f} s",
         "seconds": t_total,
         "host_cpus": os.cpu_count(),
         "affinity_cpus": len(os.sched_getaffinity(0)),
     }
+
+
+def kernel_source_hash():
+    """sha256[:16] of the HIP sources that make up the fused kernel."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in ("gemm_tile_granular_amd/csrc/mk_kernels.hip",
+                "gemm_tile_granular_amd/csrc/mk_internal.hpp"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the fused kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE passes (profiles/traffic.json), scaled by the
+    plain-copy calibration stored with them.  None when the kernel sources
+    changed since the counters were taken, or the workload was not profiled."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None, "no profiles/traffic.json"
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None, "kernel changed since the counters were taken"
+    wrec = rec.get("workloads", {}).get(workload)
+    if wrec is None:
+        return None, f"{workload} not profiled"
+    return float(wrec["hbm_bytes_per_launch"]), "rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated"
 
 
 def main():
@@ -222,7 +253,12 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS}
-    roof["traffic"] = None
+    traffic, traffic_note = measured_traffic(w.name)
+    roof["traffic"] = traffic
+    roof["traffic_unit"] = "bytes/launch"
+    roof["traffic_note"] = traffic_note
+    roof["algorithmic_bytes"] = w.algorithmic_bytes
+    roof["algorithmic_flops"] = w.flops
     roof["kernel"] = f"mk::fused_gemm_reduce_kernel<{w.tile_m}, {w.tile_n}>"
     roof["max_roofline_frac"] = max(t_mfma, t_hbm) / sec
 
