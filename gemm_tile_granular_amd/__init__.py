@@ -65,7 +65,7 @@ class Stats(ctypes.Structure):
         ("chunks_released", ctypes.c_uint32),
         ("invariant_violations", ctypes.c_uint32),
         ("ns_trace_len", ctypes.c_uint32),
-        ("reserved0", ctypes.c_uint32),
+        ("tiles_per_task", ctypes.c_uint32),
         ("sum_cycles_compute", ctypes.c_uint64),
         ("sum_cycles_reduce", ctypes.c_uint64),
         ("kernel_ticks_start", ctypes.c_uint64),

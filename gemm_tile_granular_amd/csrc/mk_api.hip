@@ -446,6 +446,7 @@ int mk_get_stats(mk_stats *out, uint32_t *maps, size_t maps_len) {
     out->tiles_per_chunk = l.tpc;
     out->tile_m = l.tm;
     out->tile_n = l.tn;
+    out->tiles_per_task = (uint32_t)tiles_per_block((int)l.tm, (int)l.tn);
     out->mode = l.mode;
     out->n_reduce_initial = l.ns_init;
     out->n_reduce_final = snap.ns_final;

@@ -116,5 +116,6 @@ hipError_t launch_ws_init(Live *live, Live *snap, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t *p, uint32_t value, int64_t n, hipStream_t s);
 hipError_t launch_controller_eval(const uint64_t *in, uint32_t *out, int n, hipStream_t s);
 bool tile_supported(int tile_m, int tile_n);
+int tiles_per_block(int tile_m, int tile_n);   // output tiles per compute task
 
 }  // namespace mk

@@ -62,6 +62,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, kNumRecords, 0x00020000);
 }
 
+// Buffer resource of a workgroup-uniform address, built in scalar registers
+// at the point of use.  The empty asm pins the address there, so the compiler
+// neither hoists many resources out of a loop (crowding the scalar register
+// file) nor moves them to vector registers (which would need a waterfall
+// loop around every access).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t scalar_rsrc(const void *p) {
+    const uint64_t p64 = (uint64_t)p;
+    uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p64);
+    uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p64 >> 32));
+    asm volatile("" : "+s"(lo), "+s"(hi));
+    return make_rsrc((const void *)(((uint64_t)hi << 32) | lo));
+}
+
 // Wait until every vector memory operation of this wave has completed
 // (s_waitcnt vmcnt(0); expcnt and lgkmcnt left unconstrained).
 __device__ __forceinline__ void drain_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -246,72 +259,95 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
-template <int TM, int TN, int NS, int WGM, int WGN, int kStorePolicy>
+// Instruction schedule of one K slab: the wave issues its NMF MFMAs one at a
+// time and slips the NDS LDS reads of the next slab's operands in between,
+// spread over the first three quarters of the MFMAs, so the reads complete
+// under the matrix work instead of in front of it.
+template <int I, int NMF, int NDS>
+struct Interleave {
+    static constexpr int kSpan = NMF * 3 / 4 > 0 ? NMF * 3 / 4 : NMF;
+    static constexpr int kDs = I < kSpan ? ((I + 1) * NDS / kSpan - I * NDS / kSpan) : 0;
+    static __device__ __forceinline__ void run() {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        if constexpr (kDs > 0) __builtin_amdgcn_sched_group_barrier(0x100, kDs, 0);   // LDS reads
+        if constexpr (I + 1 < NMF) Interleave<I + 1, NMF, NDS>::run();
+    }
+};
+
+template <int BM, int BN, int KB, int NS, int WGM, int WGN, int kStorePolicy>
 struct Gemm {
     static constexpr int NWAVES = WGM * WGN;
     static constexpr int NT = 64 * NWAVES;
-    static constexpr int WTM = TM / WGM, WTN = TN / WGN;   // wave tile
+    static constexpr int WTM = BM / WGM, WTN = BN / WGN;   // wave tile
     static constexpr int FM = WTM / 32, FN = WTN / 32;     // 32x32 blocks per wave
-    static constexpr int LDS_A = TM * kBK * 2, LDS_B = kBK * TN * 2;
+    static constexpr int KK = KB / 16;                     // MFMA k-steps per slab
+    static constexpr int A_ROW = KB * 2;                   // bytes of one A row in LDS
+    static constexpr int A_CHUNKS = KB / 8;                // 16-byte chunks per A row
+    static constexpr int A_ROWS = 1024 / A_ROW;            // A rows per 1 KiB load
+    static constexpr int LDS_A = BM * A_ROW, LDS_B = KB * BN * 2;
     static constexpr int STAGE = LDS_A + LDS_B;
     static constexpr int LDS_BYTES = NS * STAGE;
-    static constexpr int A_INST = TM / 8 / NWAVES;          // 1 KiB loads per wave per slab
-    static constexpr int B_ROWS = 1024 / (TN * 2);          // B rows per 1 KiB load
-    static constexpr int B_CHUNKS = TN / 8;                 // 16-byte chunks per B row
-    static constexpr int B_INST = kBK / B_ROWS / NWAVES;
-    static constexpr int L = A_INST + B_INST;               // loads per wave per slab
-    static_assert(FM >= 1 && FN >= 1 && A_INST >= 1 && B_INST >= 1, "tile/wave shape");
+    static constexpr int A_INST = BM / A_ROWS / NWAVES;    // 1 KiB loads per wave per slab
+    static constexpr int B_ROWS = 1024 / (BN * 2);         // B rows per 1 KiB load
+    static constexpr int B_CHUNKS = BN / 8;                // 16-byte chunks per B row
+    static constexpr int B_INST = KB / B_ROWS / NWAVES;
+    static constexpr int L = A_INST + B_INST;              // loads per wave per slab
+    static_assert(KB == 32 || KB == 64, "K slab");
+    static_assert(BN >= 64 && BN <= 512 && B_ROWS >= 1, "block width");
+    static_assert(FM >= 1 && FN >= 1 && A_INST >= 1 && B_INST >= 1, "block/wave shape");
+    static_assert(BM % (A_ROWS * NWAVES) == 0 && KB % (B_ROWS * NWAVES) == 0, "load split");
     static_assert(STAGE < 65536, "in-slab offsets must fit the LDS immediate");
     static_assert(NS >= 2 && NS <= 4, "ring depth");
 
-    static __device__ __forceinline__ int swz_a(int row) { return (row >> 1) & 7; }
+    // XOR swizzles of 16-byte chunks (conflict-free operand reads, see above)
+    static __device__ __forceinline__ int swz_a(int row) {
+        return A_CHUNKS == 8 ? (row >> 1) & 7 : (row >> 2) & 3;
+    }
     static __device__ __forceinline__ int swz_b(int k) {
-        return B_CHUNKS == 16 ? 4 * (k & 3) : 4 * ((k >> 1) & 1);
+        return B_CHUNKS >= 16 ? 4 * (k & 3) : 4 * ((k >> 1) & 1);
     }
 
     // per-lane constants, computed once per kernel
     struct Lane {
         uint32_t a_dma[A_INST];     // (row*K + c*8)*2 inside the A slab
-        int a_row[A_INST];
-        int a_col[A_INST];
         uint32_t b_dma[B_INST];     // (row*N + c*8)*2 inside the B slab
-        int b_row[B_INST];
-        int b_col[B_INST];
-        uint32_t a_frag[kBK / 16];  // LDS offset of this lane's A operand (fm = 0) per k-step
+        uint32_t a_frag[KK];        // LDS offset of this lane's A operand (fm = 0) per k-step
         uint32_t b_frag[FN];        // LDS offset of this lane's first B piece per fn
     };
+
+    // row and column (in elements) of the piece load i of this lane carries
+    static __device__ __forceinline__ int a_row(int i) {
+        return ((int)(threadIdx.x >> 6) * A_INST + i) * A_ROWS + (int)(threadIdx.x & 63) / A_CHUNKS;
+    }
+    static __device__ __forceinline__ int a_col(int i) {
+        return (((int)(threadIdx.x & 63) % A_CHUNKS) ^ swz_a(a_row(i))) * 8;
+    }
+    static __device__ __forceinline__ int b_row(int i) {
+        return ((int)(threadIdx.x >> 6) * B_INST + i) * B_ROWS + (int)(threadIdx.x & 63) / B_CHUNKS;
+    }
+    static __device__ __forceinline__ int b_col(int i) {
+        return (((int)(threadIdx.x & 63) % B_CHUNKS) ^ swz_b(b_row(i))) * 8;
+    }
 
     static __device__ __forceinline__ void init_lane(Lane &ln, int64_t N, int64_t K) {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-        for (int i = 0; i < A_INST; ++i) {
-            const int row = (wave * A_INST + i) * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ swz_a(row);
-            ln.a_row[i] = row;
-            ln.a_col[i] = c * 8;
-            ln.a_dma[i] = (uint32_t)((row * K + c * 8) * 2);
-        }
+        for (int i = 0; i < A_INST; ++i) ln.a_dma[i] = (uint32_t)((a_row(i) * K + a_col(i)) * 2);
 #pragma unroll
-        for (int i = 0; i < B_INST; ++i) {
-            const int row = (wave * B_INST + i) * B_ROWS + lane / B_CHUNKS;
-            const int c = (lane % B_CHUNKS) ^ swz_b(row);
-            ln.b_row[i] = row;
-            ln.b_col[i] = c * 8;
-            ln.b_dma[i] = (uint32_t)((row * N + c * 8) * 2);
-        }
+        for (int i = 0; i < B_INST; ++i) ln.b_dma[i] = (uint32_t)((b_row(i) * N + b_col(i)) * 2);
         const int wm = wave / WGN, wn = wave % WGN;
         const int m = wm * WTM + (lane & 31);
 #pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
+        for (int kk = 0; kk < KK; ++kk) {
             const int c = kk * 2 + (lane >> 5);
-            ln.a_frag[kk] = m * 128 + ((c ^ swz_a(m)) << 4);
+            ln.a_frag[kk] = m * A_ROW + ((c ^ swz_a(m)) << 4);
         }
         const int i = lane & 15;
         const int kl = 8 * (lane >> 5) + (i >> 2);
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             const int n = wn * WTN + fn * 32 + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
-            ln.b_frag[fn] = LDS_A + kl * (TN * 2) + (((n >> 3) ^ swz_b(kl)) << 4) + (n & 7) * 2;
+            ln.b_frag[fn] = LDS_A + kl * (BN * 2) + (((n >> 3) ^ swz_b(kl)) << 4) + (n & 7) * 2;
         }
     }
 
@@ -321,41 +357,49 @@ struct Gemm {
                                                  int64_t m0, int64_t n0, int64_t k0, bool a_full,
                                                  bool b_full) {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        const uint32_t sa = __builtin_amdgcn_readfirstlane(slot), sb = sa + LDS_A;
+        const uint32_t s0 = __builtin_amdgcn_readfirstlane(slot);
+        const uint32_t sa = s0 + wave * A_INST * 1024, sb = s0 + LDS_A + wave * B_INST * 1024;
         const u32x4 da = make_desc(A + m0 * K + k0), db = make_desc(B + k0 * N + n0);
-        const bool k_full = k0 + kBK <= K;
+        if (__builtin_amdgcn_readfirstlane((int)(a_full && b_full && k0 + KB <= K))) {
 #pragma unroll
-        for (int i = 0; i < A_INST; ++i) {
-            uint32_t off = ln.a_dma[i];
-            if (!(a_full && k_full)) off = (m0 + ln.a_row[i] < M && k0 + ln.a_col[i] < K) ? off : kOOB;
-            dma16(da, off, sa + (wave * A_INST + i) * 1024);
-        }
+            for (int i = 0; i < A_INST; ++i) dma16(da, ln.a_dma[i], sa + i * 1024);
 #pragma unroll
-        for (int i = 0; i < B_INST; ++i) {
-            uint32_t off = ln.b_dma[i];
-            if (!(b_full && k_full)) off = (k0 + ln.b_row[i] < K && n0 + ln.b_col[i] < N) ? off : kOOB;
-            dma16(db, off, sb + (wave * B_INST + i) * 1024);
+            for (int i = 0; i < B_INST; ++i) dma16(db, ln.b_dma[i], sb + i * 1024);
+        } else {
+            // edge block or last K slab: out-of-range pieces read as zeros
+#pragma unroll
+            for (int i = 0; i < A_INST; ++i) {
+                const bool ok = m0 + a_row(i) < M && k0 + a_col(i) < K;
+                dma16(da, ok ? ln.a_dma[i] : kOOB, sa + i * 1024);
+            }
+#pragma unroll
+            for (int i = 0; i < B_INST; ++i) {
+                const bool ok = k0 + b_row(i) < K && n0 + b_col(i) < N;
+                dma16(db, ok ? ln.b_dma[i] : kOOB, sb + i * 1024);
+            }
         }
     }
 
-    struct Frag {
+    // this lane's MFMA operands for one 16-deep k-step
+    struct KFrag {
         bf16x8 a[FM];
         bf16x8 b[FN];
     };
 
-    static __device__ __forceinline__ void frags(Frag &f, const Lane &ln, const lchar *st, int kk) {
+    static __device__ __forceinline__ void kfrags(KFrag &f, const Lane &ln, const lchar *st, int kk) {
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) f.a[fm] = *(const lbf16x8 *)(st + ln.a_frag[kk] + fm * 32 * 128);
+        for (int fm = 0; fm < FM; ++fm)
+            f.a[fm] = *(const lbf16x8 *)(st + ln.a_frag[kk] + fm * 32 * A_ROW);
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-            const lchar *p = st + ln.b_frag[fn] + kk * 16 * (TN * 2);
+            const lchar *p = st + ln.b_frag[fn] + kk * 16 * (BN * 2);
             const bf16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lbf16x4 *)p);
-            const bf16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lbf16x4 *)(p + 4 * (TN * 2)));
+            const bf16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lbf16x4 *)(p + 4 * (BN * 2)));
             f.b[fn] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
         }
     }
 
-    static __device__ __forceinline__ void mfma(f32x16 (&acc)[FM][FN], const Frag &f) {
+    static __device__ __forceinline__ void kmfma(f32x16 (&acc)[FM][FN], const KFrag &f) {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -363,12 +407,59 @@ struct Gemm {
                 acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[fn], f.a[fm], acc[fm][fn], 0, 0, 0);
     }
 
-    // Whole output tile (ti, tj): C[tile] = A[rows, :] . B[:, cols] in fp32.
-    static __device__ __forceinline__ void tile(const Lane &ln, const uint16_t *A, const uint16_t *B,
-                                                float *C, int64_t M, int64_t N, int64_t K, int ti,
-                                                int tj, lchar *lds) {
-        const int64_t m0 = (int64_t)ti * TM, n0 = (int64_t)tj * TN;
-        const bool a_full = m0 + TM <= M, b_full = n0 + TN <= N;
+    // wait until at most n slabs of this wave's loads are still in flight
+    static __device__ __forceinline__ void wait_slabs(int n) {
+        static_assert((NS - 1) * L < 64, "vmcnt range");
+        if (n <= 0) wait_vmcnt<0>();
+        else if (n == 1) wait_vmcnt<L>();
+        else if (n == 2) wait_vmcnt<(NS >= 3 ? 2 * L : 0)>();
+        else wait_vmcnt<(NS >= 4 ? 3 * L : 0)>();
+    }
+
+    static constexpr int NMF = FM * FN;         // MFMAs per k-step per wave
+    static constexpr int NDS = FM + 2 * FN;     // LDS reads per k-step per wave
+
+    // One K slab s whose k-step-0 operands are in f0.  Each k-step multiplies
+    // from registers while the next k-step's operands come out of LDS.  Before
+    // the last k-step (when slab s+1 exists) the workgroup waits for slab s+1
+    // to land, and slab s+NS starts streaming into the slot slab s leaves free
+    // (slab s+NS has about NS-1 slab times to arrive); the last k-step then
+    // overlaps the reads of slab s+1's first operands, which end in f0.
+    template <bool kNext>
+    static __device__ __forceinline__ void slab(const Lane &ln, int s, int S, KFrag &f0, KFrag &f1,
+                                                f32x16 (&acc)[FM][FN], const uint16_t *A,
+                                                const uint16_t *B, int64_t M, int64_t N, int64_t K,
+                                                int64_t m0, int64_t n0, bool a_full, bool b_full,
+                                                lchar *lds, uint32_t base) {
+        const lchar *st = lds + (s % NS) * STAGE;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            KFrag &cur = (kk & 1) ? f1 : f0;
+            KFrag &nxt = (kk & 1) ? f0 : f1;
+            if (kk + 1 < KK) {
+                kfrags(nxt, ln, st, kk + 1);
+            } else if (kNext) {
+                const int later = (S - 2 - s) < (NS - 2) ? (S - 2 - s) : (NS - 2);
+                wait_slabs(later);     // this wave's part of slab s+1 has landed
+                __syncthreads();       // every wave's has; slab s is no longer read
+                if (s + NS < S)
+                    issue(ln, base + (s % NS) * STAGE, A, B, M, N, K, m0, n0, (int64_t)(s + NS) * KB,
+                          a_full, b_full);
+                kfrags(nxt, ln, lds + ((s + 1) % NS) * STAGE, 0);
+            }
+            kmfma(acc, cur);
+            if (kk + 1 < KK || kNext) Interleave<0, NMF, NDS>::run();
+        }
+    }
+
+    // Whole block at rows m0.., columns n0..: C = A[rows, :] . B[:, cols] in
+    // fp32.  `hook()` runs once the products are complete, before the block
+    // is stored.
+    template <class Hook>
+    static __device__ __forceinline__ void block(const Lane &ln, const uint16_t *A, const uint16_t *B,
+                                                 float *C, int64_t M, int64_t N, int64_t K, int64_t m0,
+                                                 int64_t n0, lchar *lds, Hook &&hook) {
+        const bool a_full = m0 + BM <= M, b_full = n0 + BN <= N;
         const uint32_t base = (uint32_t)(uintptr_t)lds;
         f32x16 acc[FM][FN];
 #pragma unroll
@@ -378,58 +469,28 @@ struct Gemm {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[fm][fn][i] = 0.0f;
 
-        const int S = (int)((K + kBK - 1) / kBK);
-#pragma unroll
-        for (int s = 0; s < NS - 1; ++s)
-            if (s < S) issue(ln, base + s * STAGE, A, B, M, N, K, m0, n0, (int64_t)s * kBK, a_full, b_full);
+        const int S = (int)((K + KB - 1) / KB);
+        const int pre = S < NS ? S : NS;
+        for (int s = 0; s < pre; ++s)
+            issue(ln, base + s * STAGE, A, B, M, N, K, m0, n0, (int64_t)s * KB, a_full, b_full);
         if (S > 0) {
-            // slab 0 landed: up to NS-2 later slabs may still be loading
-            if (NS >= 4 && S - 1 >= 2) wait_vmcnt<(NS >= 4 ? 2 * L : 0)>();
-            else if (NS >= 3 && S - 1 >= 1) wait_vmcnt<(NS >= 3 ? L : 0)>();
-            else wait_vmcnt<0>();
+            wait_slabs(pre - 1);
             __syncthreads();
-            Frag cur, nxt;
-            frags(cur, ln, lds, 0);
-            int slot = 0;
-            for (int s = 0; s < S; ++s) {
-                const lchar *st = lds + slot * STAGE;
-                const int nslot = slot + 1 == NS ? 0 : slot + 1;
-#pragma unroll
-                for (int kk = 0; kk < kBK / 16; ++kk) {
-                    if (kk < kBK / 16 - 1) {
-                        // operands of the next k-step load while this one multiplies
-                        frags(nxt, ln, st, kk + 1);
-                        mfma(acc, cur);
-                    } else {
-                        mfma(acc, cur);
-                        if (s + 1 < S) {
-                            // slab s+1 landed (NS-3 later slabs may still load) and every
-                            // wave is past slab s-1, whose slot is refilled now
-                            const int later = (S - 2 - s) < (NS - 3) ? (S - 2 - s) : (NS - 3);
-                            if (NS >= 4 && later >= 1) wait_vmcnt<(NS >= 4 ? L : 0)>();
-                            else wait_vmcnt<0>();
-                            __syncthreads();
-                            if (s + NS - 1 < S) {
-                                const int fslot = slot == 0 ? NS - 1 : slot - 1;
-                                issue(ln, base + fslot * STAGE, A, B, M, N, K, m0, n0,
-                                      (int64_t)(s + NS - 1) * kBK, a_full, b_full);
-                            }
-                            frags(nxt, ln, lds + nslot * STAGE, 0);
-                        }
-                    }
-                    cur = nxt;
-                }
-                slot = nslot;
-            }
+            KFrag f0, f1;
+            kfrags(f0, ln, lds, 0);
+            for (int s = 0; s + 1 < S; ++s)
+                slab<true>(ln, s, S, f0, f1, acc, A, B, M, N, K, m0, n0, a_full, b_full, lds, base);
+            slab<false>(ln, S - 1, S, f0, f1, acc, A, B, M, N, K, m0, n0, a_full, b_full, lds, base);
         }
-        // the ring is refilled by the next tile only after every wave is done with it
+        // the ring is refilled by the next block only after every wave is done with it
         __syncthreads();
+        hook();
 
         // epilogue: 16-byte stores; rows >= M and columns >= N masked by an
         // out-of-range offset
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const int wm = wave / WGN, wn = wave % WGN;
-        const auto rc = make_rsrc(C + m0 * N + n0);
+        const auto rc = scalar_rsrc(C + m0 * N + n0);
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
             const int r = wm * WTM + fm * 32 + (lane & 31);
@@ -450,98 +511,161 @@ struct Gemm {
     }
 };
 
-// Tile configurations: ring depth and wave grid per output tile.
+// Compute blocks per tile shape.  One MI355X CU fetches operands at a bounded
+// rate, so a compute task covers TPB output tiles side by side (one block of
+// BM x (TPB*TN)) when that lowers the operand bytes per flop: two 128-wide
+// tiles share their A rows.  Tiles of one block always lie in one chunk.
 template <int TM, int TN> struct TileCfg;
-template <> struct TileCfg<64, 64> { static constexpr int NS = 4, WGM = 2, WGN = 2; };
-template <> struct TileCfg<128, 128> { static constexpr int NS = 4, WGM = 2, WGN = 4; };
-template <> struct TileCfg<256, 128> { static constexpr int NS = 3, WGM = 4, WGN = 2; };
+template <> struct TileCfg<64, 64> {
+    static constexpr int TPB = 1, KB = 64, NS = 4, WGM = 2, WGN = 2;
+};
+template <> struct TileCfg<128, 128> {
+    static constexpr int TPB = 2, KB = 64, NS = 3, WGM = 2, WGN = 2;
+};
+template <> struct TileCfg<256, 128> {
+    static constexpr int TPB = 2, KB = 32, NS = 4, WGM = 4, WGN = 2;
+};
 
 template <int TM, int TN, int kStorePolicy>
-using GemmFor = Gemm<TM, TN, TileCfg<TM, TN>::NS, TileCfg<TM, TN>::WGM, TileCfg<TM, TN>::WGN, kStorePolicy>;
+using GemmFor = Gemm<TM, TN * TileCfg<TM, TN>::TPB, TileCfg<TM, TN>::KB, TileCfg<TM, TN>::NS,
+                     TileCfg<TM, TN>::WGM, TileCfg<TM, TN>::WGN, kStorePolicy>;
 
 // ---------------------------------------------------------------------------
 // tile reduce: C[tile] = C[tile] (the local partial) + sum_p peers[p][tile]
 //
-// Each lane owns one float4 column of a strip of rows; U row passes are in
-// flight together and every load of a pass group (the partial and all PP
-// peers) is issued before the first add, so a 4-wave workgroup keeps
-// (PP+1)*U 16-byte loads per lane outstanding.  Per-tile uniform buffer bases
-// keep lane offsets in 32 bits.  Ragged tiles use out-of-range offsets.
+// Each lane owns one float4 column of a strip of rows.  The tile is walked in
+// groups of U row passes; a group's loads (the partial and every peer) are
+// all issued before its first add, and the loads of group g+1 are issued
+// before group g is summed, so two groups stay in flight.  Per-tile uniform buffer bases keep lane offsets in 32
+// bits; ragged tiles use out-of-range offsets.
 // ---------------------------------------------------------------------------
-// about 128 KiB of loads in flight per workgroup: 32 per lane with 4 waves,
-// 16 per lane with 8
+// loads of one group per lane: about 64 KiB per workgroup, so two groups keep
+// about 128 KiB in flight (a CU's streaming rate does not grow beyond that)
 template <int PP, int NT>
 struct ReducePlan {
-    static constexpr int kLoads = 8192 / NT;   // target loads in flight per lane
+    static constexpr int kLoads = 4096 / NT;
     static constexpr int U = (kLoads / (PP + 1)) >= 16 ? 16
                            : (kLoads / (PP + 1)) >= 8 ? 8
                            : (kLoads / (PP + 1)) >= 4 ? 4
                            : (kLoads / (PP + 1)) >= 2 ? 2 : 1;
 };
 
-// PP > 0 peers starting at peers0 (compile-time count); accumulate into acc
-template <int TM, int TN, int PP, int U>
-__device__ __forceinline__ void add_peers(f32x4 (&acc)[U], const float *peers0, int64_t MN,
-                                          int64_t base, const uint32_t (&off)[U]) {
-    f32x4 v[PP][U];
-#pragma unroll
-    for (int q = 0; q < PP; ++q) {
-        const auto rp = make_rsrc(peers0 + q * MN + base);
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            v[q][u] = __builtin_amdgcn_raw_buffer_load_b128(rp, off[u], 0, kPolicyStream);
-    }
-#pragma unroll
-    for (int q = 0; q < PP; ++q)
-#pragma unroll
-        for (int u = 0; u < U; ++u) acc[u] += v[q][u];
-}
+template <int TM, int TN, int NT>
+struct ReduceGeom {
+    static constexpr int C4 = TN / 4;              // float4 per tile row
+    static constexpr int RP = NT / C4;             // rows per pass
+    static constexpr int PASSES = TM / RP;
+    static_assert(NT % C4 == 0 && TM % RP == 0, "reduce layout");
+};
+
+// one group of U row passes: the partial and PP peers per pass, in registers
+template <int PP, int U>
+struct ReduceGroup {
+    f32x4 v[PP + 1][U];
+    uint32_t off[U];
+};
 
 template <int TM, int TN, int NT, int PP>
-__device__ void reduce_tile_pp(const float *__restrict__ peers, float *__restrict__ C, int64_t M,
+__device__ __forceinline__ void reduce_tile_pp(const float *__restrict__ peers, float *__restrict__ C, int64_t M,
                                int64_t N, int P, int ti, int tj) {
-    constexpr int C4 = TN / 4;              // float4 per tile row
-    constexpr int RP = NT / C4;             // rows per pass
-    constexpr int PASSES = TM / RP;
+    using RG = ReduceGeom<TM, TN, NT>;
     constexpr int PB = 8;                   // peer block when PP is the generic 0
     constexpr int UP = ReducePlan<(PP > 0 ? PP : PB), NT>::U;
-    constexpr int U = UP < PASSES ? UP : PASSES;
-    static_assert(NT % C4 == 0 && TM % RP == 0 && PASSES % U == 0, "reduce layout");
+    constexpr int U = UP < RG::PASSES ? UP : RG::PASSES;
+    constexpr int G = RG::PASSES / U;
+    static_assert(RG::PASSES % U == 0, "reduce layout");
     const int tid = threadIdx.x;
     const int64_t m0 = (int64_t)ti * TM, n0 = (int64_t)tj * TN;
     const int64_t base = m0 * N + n0;
     const int64_t MN = M * N;
-    const int cc = (tid % C4) * 4;
-    const int r0 = tid / C4;
+    const int cc = (tid % RG::C4) * 4;
+    const int r0 = tid / RG::C4;
     const bool col_ok = n0 + cc < N;
-    const auto rc = make_rsrc(C + base);
-    for (int ps = 0; ps < PASSES; ps += U) {
-        f32x4 acc[U];
-        uint32_t off[U];
+
+    if constexpr (PP > 0) {
+        // one peer's buffer resource at a time: a resource per peer held
+        // across the tile would crowd out the scalar registers
+        auto load = [&](ReduceGroup<PP, U> &g, int gi) {
+            const auto rc = scalar_rsrc(C + base);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int r = (ps + u) * RP + r0;
-            off[u] = (col_ok && m0 + r < M) ? (uint32_t)((r * N + cc) * 4) : kOOB;
-            acc[u] = __builtin_amdgcn_raw_buffer_load_b128(rc, off[u], 0, kPolicyCoherentLoad);
+            for (int u = 0; u < U; ++u) {
+                const int r = (gi * U + u) * RG::RP + r0;
+                g.off[u] = (col_ok && m0 + r < M) ? (uint32_t)((r * N + cc) * 4) : kOOB;
+                g.v[0][u] = __builtin_amdgcn_raw_buffer_load_b128(rc, g.off[u], 0, kPolicyCoherentLoad);
+            }
+#pragma unroll
+            for (int q = 0; q < PP; ++q) {
+                const auto rq = scalar_rsrc(peers + q * MN + base);
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    g.v[q + 1][u] = __builtin_amdgcn_raw_buffer_load_b128(rq, g.off[u], 0, kPolicyStream);
+            }
+        };
+        auto sum_store = [&](const ReduceGroup<PP, U> &g) {
+            const auto rc = scalar_rsrc(C + base);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                f32x4 acc = g.v[0][u];
+#pragma unroll
+                for (int q = 0; q < PP; ++q) acc += g.v[q + 1][u];
+                __builtin_amdgcn_raw_buffer_store_b128(acc, rc, g.off[u], 0, kPolicyCoherentStream);
+            }
+        };
+        ReduceGroup<PP, U> g0, g1;
+        load(g0, 0);
+#pragma unroll
+        for (int gi = 0; gi < G; gi += 2) {
+            if (gi + 1 < G) load(g1, gi + 1);
+            sum_store(g0);
+            if (gi + 1 < G) {
+                if (gi + 2 < G) load(g0, gi + 2);
+                sum_store(g1);
+            }
         }
-        if constexpr (PP > 0) {
-            add_peers<TM, TN, PP, U>(acc, peers, MN, base, off);
-        } else {
-            // generic peer count: blocks of PB, then one at a time
+    } else {
+        // generic peer count: one group at a time, peers in blocks of PB
+        for (int gi = 0; gi < G; ++gi) {
+            const auto rc = scalar_rsrc(C + base);
+            f32x4 acc[U];
+            uint32_t off[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int r = (gi * U + u) * RG::RP + r0;
+                off[u] = (col_ok && m0 + r < M) ? (uint32_t)((r * N + cc) * 4) : kOOB;
+                acc[u] = __builtin_amdgcn_raw_buffer_load_b128(rc, off[u], 0, kPolicyCoherentLoad);
+            }
             int p = 0;
-            for (; p + PB <= P; p += PB) add_peers<TM, TN, PB, U>(acc, peers + p * MN, MN, base, off);
-            for (; p < P; ++p) add_peers<TM, TN, 1, U>(acc, peers + p * MN, MN, base, off);
-        }
+            for (; p + PB <= P; p += PB) {
+                f32x4 v[PB][U];
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            __builtin_amdgcn_raw_buffer_store_b128(acc[u], rc, off[u], 0, kPolicyCoherentStream);
+                for (int q = 0; q < PB; ++q) {
+                    const auto rq = scalar_rsrc(peers + (p + q) * MN + base);
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        v[q][u] = __builtin_amdgcn_raw_buffer_load_b128(rq, off[u], 0, kPolicyStream);
+                }
+#pragma unroll
+                for (int q = 0; q < PB; ++q)
+#pragma unroll
+                    for (int u = 0; u < U; ++u) acc[u] += v[q][u];
+            }
+            for (; p < P; ++p) {
+                const auto rq = scalar_rsrc(peers + p * MN + base);
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    acc[u] += __builtin_amdgcn_raw_buffer_load_b128(rq, off[u], 0, kPolicyStream);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                __builtin_amdgcn_raw_buffer_store_b128(acc[u], rc, off[u], 0, kPolicyCoherentStream);
+        }
     }
 }
 
 // Dispatch on the peer count so that every load of a pass group is a
 // straight-line instruction (counts above 16 take the blocked loop).
 template <int TM, int TN, int NT>
-__device__ void reduce_tile(const float *__restrict__ peers, float *__restrict__ C, int64_t M,
+__device__ __forceinline__ void reduce_tile(const float *__restrict__ peers, float *__restrict__ C, int64_t M,
                             int64_t N, int P, int ti, int tj) {
     switch (P) {
 #define MK_REDUCE_CASE(k) \
@@ -563,9 +687,50 @@ enum Role : int { kRoleCompute = 0, kRoleReduce = 1, kRoleExit = 2, kRoleNone = 
 
 struct Decision {
     int role;
-    uint32_t tile;
+    uint32_t tile;      // compute: block index; reduce: tile index
     uint32_t ns_seen;   // reduce target the claim was made under (logged in owner maps)
 };
+
+// Compute tasks are blocks of tpb adjacent tiles of one tile row (a ragged
+// last block holds fewer).  Reduce tickets run over tpb slots per block in
+// the order blocks are claimed; the slot of a missing tile is skipped.
+struct Blocks {
+    uint32_t tpb;       // tiles per block
+    uint32_t bn;        // blocks per tile row
+    uint32_t TB;        // blocks
+    uint32_t slots;     // reduce ticket slots, TB * tpb
+    uint32_t tiles_n;
+    __device__ __forceinline__ uint32_t first_tile(uint32_t b) const {
+        return (b / bn) * tiles_n + (b % bn) * tpb;
+    }
+    __device__ __forceinline__ uint32_t count(uint32_t b) const {
+        const uint32_t c0 = (b % bn) * tpb;
+        return tiles_n - c0 < tpb ? tiles_n - c0 : tpb;
+    }
+};
+
+__device__ __forceinline__ Blocks make_blocks(uint32_t tpb, uint32_t tiles_m, uint32_t tiles_n) {
+    Blocks k;
+    k.tpb = tpb;
+    k.bn = (tiles_n + tpb - 1) / tpb;
+    k.TB = tiles_m * k.bn;
+    k.slots = k.TB * tpb;
+    k.tiles_n = tiles_n;
+    return k;
+}
+
+// chunk size in blocks for the claim order (1 when blocks do not divide chunks)
+__device__ __forceinline__ uint32_t chunk_blocks(uint32_t tpc, uint32_t tpb) {
+    return (tpc % tpb) == 0 ? tpc / tpb : 1u;
+}
+
+// tile of reduce ticket q; false for the empty slot of a ragged block
+__device__ __forceinline__ bool ticket_tile(const Parts &pt, const Blocks &bk, uint32_t q, uint32_t &t) {
+    const uint32_t b = pt.ticket(q / bk.tpb), k = q % bk.tpb;
+    if (k >= bk.count(b)) return false;
+    t = bk.first_tile(b) + k;
+    return true;
+}
 
 // Scheduling state kept by thread 0 of each workgroup.
 struct Sched {
@@ -612,7 +777,8 @@ __device__ bool wait_ready(const FusedArgs &a, Live *L, uint32_t t) {
 // in one common order, so compute and reduce walk the tiles in step.  A claim
 // taken ahead of time (prefetched during the previous task) is a commitment
 // and is honoured first, so a role change takes effect one task later.
-__device__ Decision next_task(const FusedArgs &a, const Parts &pt, Live *L, uint32_t wg, Sched &s) {
+__device__ Decision next_task(const FusedArgs &a, const Parts &pt, const Blocks &bk, Live *L, uint32_t wg,
+                             Sched &s) {
     const uint32_t B = (uint32_t)a.nwg, T = a.T;
     if (a.mode == kDeterministic) {
         const uint32_t ns = (uint32_t)a.ns_init;
@@ -623,10 +789,10 @@ __device__ Decision next_task(const FusedArgs &a, const Parts &pt, Live *L, uint
             ++s.det_i;
             return {kRoleReduce, t, ns};
         }
-        const uint32_t t = (wg - ns) + s.det_i * (B - ns);
-        if (t >= T) return {kRoleExit, 0, ns};
+        const uint32_t b = (wg - ns) + s.det_i * (B - ns);
+        if (b >= bk.TB) return {kRoleExit, 0, ns};
         ++s.det_i;
-        return {kRoleCompute, t, ns};
+        return {kRoleCompute, b, ns};
     }
     if (s.early_claim) {
         // a compute claim taken while the previous task's stores drained
@@ -641,8 +807,9 @@ __device__ Decision next_task(const FusedArgs &a, const Parts &pt, Live *L, uint
             s.pending_role = kRoleNone;
             const bool seen = s.early_flag && s.early_flag_value == a.epoch;
             s.early_flag = false;
-            if (q < T) {
-                const uint32_t t = pt.ticket(q);
+            if (q < bk.slots) {
+                uint32_t t;
+                if (!ticket_tile(pt, bk, q, t)) continue;   // empty slot: take another ticket
                 if (!seen && !wait_ready(a, L, t)) return {kRoleExit, 0, ns_seen};
                 return {kRoleReduce, t, ns_seen};
             }
@@ -697,15 +864,16 @@ __device__ __forceinline__ void prefetch_claim(const FusedArgs &a, Live *L, uint
 
 // Thread 0, at the end of a task and before its stores drain: start the
 // round trips the next boundary needs, so they overlap the drain.  A compute
-// workgroup that is still in the compute role claims its next tile; a
+// workgroup that is still in the compute role claims its next block; a
 // reducer holding a ticket reads that tile's readiness flag.
-__device__ __forceinline__ void early_next(const FusedArgs &a, const Parts &pt, Live *L, uint32_t wg,
-                                           Sched &s) {
+__device__ __forceinline__ void early_next(const FusedArgs &a, const Parts &pt, const Blocks &bk,
+                                           Live *L, uint32_t wg, Sched &s) {
     if (a.mode == kDeterministic) return;
     if (s.pending_role == kRoleReduce) {
-        if (s.pending_q < a.T) {
+        uint32_t t;
+        if (s.pending_q < bk.slots && ticket_tile(pt, bk, s.pending_q, t)) {
             s.early_flag = true;
-            s.early_flag_value = ld_relaxed(&a.ws.tile_flag[pt.ticket(s.pending_q)]);
+            s.early_flag_value = ld_relaxed(&a.ws.tile_flag[t]);
         }
         return;
     }
@@ -794,67 +962,80 @@ __device__ void finish_launch(const FusedArgs &a, Live *L) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
 }
 
-// A finished task whose bookkeeping is still to be done, and the values its
-// atomics return.
-struct Booked {
-    bool valid;
-    int role;
-    uint32_t tile;
-    uint64_t dt;       // shader cycles of the task
-    uint64_t r0, r1;   // constant-clock start and end
-};
-struct BookResult {
-    uint64_t mine, other;   // role words: this task's role before the add, the other role
-    uint32_t old_t, old_c;  // tile and chunk counters before the add
+// Controller inputs read as a task's work completes: this role's progress
+// word with the task added, the other role's word, the published target.
+struct CtlRead {
+    uint64_t mine, other;
     uint32_t raw_target;
 };
 
-// Thread 0: issue the bookkeeping atomics of task b (results are read later).
-__device__ __forceinline__ BookResult book_issue(const FusedArgs &a, Live *L, const Booked &b) {
-    BookResult r;
-    const uint64_t inc = (b.dt << kCountBits) | 1ull;
-    r.old_t = 0;
-    r.old_c = 0;
-    if (b.role == kRoleCompute) {
-        r.mine = add_relaxed(&L->role_compute, inc);
-        r.other = ld_relaxed(&L->role_reduce);
+// Thread 0, when a task's products are complete (its stores may still be in
+// flight): record the task in its role word ((cycles << kCountBits) | tiles)
+// and read what the controller needs.  The returns are consumed by ctl_finish
+// after the tile's stores have been issued, so the round trip overlaps them.
+__device__ __forceinline__ CtlRead ctl_issue(const FusedArgs &a, Live *L, int role, uint32_t units,
+                                             uint64_t dt, uint64_t r0, uint64_t r1) {
+    CtlRead c;
+    const uint64_t inc = (dt << kCountBits) | units;
+    if (role == kRoleCompute) {
+        c.mine = add_relaxed(&L->role_compute, inc) + inc;
+        c.other = ld_relaxed(&L->role_reduce);
     } else {
-        const uint32_t c = b.tile / a.tpc;
-        r.old_t = add_relaxed(&a.ws.tile_cnt[b.tile], 1u);
-        r.old_c = add_relaxed(&a.ws.chunk_cnt[c], 1u);
-        r.mine = add_relaxed(&L->role_reduce, inc);
-        r.other = ld_relaxed(&L->role_compute);
-        min_relaxed(&L->r_start, b.r0);
-        max_relaxed(&L->r_end, b.r1);
+        c.mine = add_relaxed(&L->role_reduce, inc) + inc;
+        c.other = ld_relaxed(&L->role_compute);
+        min_relaxed(&L->r_start, r0);
+        max_relaxed(&L->r_end, r1);
     }
-    r.raw_target = a.mode == kAdaptive ? ld_relaxed(&L->target_ns) : 0u;
-    return r;
+    c.raw_target = a.mode == kAdaptive ? ld_relaxed(&L->target_ns) : 0u;
+    return c;
 }
 
-// Thread 0: act on the returned values -- exactly-once check, release of a
-// chunk whose last tile this was ("【学习】mKernel 分析" section 2.3), one
-// controller step (section 2.4).
-__device__ __forceinline__ void book_finish(const FusedArgs &a, Live *L, const Booked &b,
-                                            const BookResult &r, Sched &s) {
-    const uint64_t inc = (b.dt << kCountBits) | 1ull;
-    if (b.role == kRoleReduce) {
-        const uint32_t c = b.tile / a.tpc;
-        const uint32_t first = c * a.tpc;
-        const uint32_t size = (a.T - first) < a.tpc ? (a.T - first) : a.tpc;
-        const uint32_t want = size * a.calls;
-        if (r.old_t != a.calls - 1) add_relaxed(&L->violations, 1u);
-        if (r.old_c + 1 == want) {
-            // where a network send of the chunk would be posted
-            st_relaxed(&a.ws.chunk_flag[c], a.epoch);
-            add_relaxed(&L->chunks_released, 1u);
-        } else if (r.old_c + 1 > want) {
-            add_relaxed(&L->violations, 1u);
-        }
+// Thread 0: one controller step ("【学习】mKernel 分析" section 2.4) from the
+// words ctl_issue read; the role of the next task follows from its result.
+__device__ __forceinline__ void ctl_finish(const FusedArgs &a, Live *L, int role, const CtlRead &c,
+                                           Sched &s) {
+    if (a.mode != kAdaptive) return;
+    const uint64_t cw = role == kRoleCompute ? c.mine : c.other;
+    const uint64_t rw = role == kRoleCompute ? c.other : c.mine;
+    s.target = controller_step(a, L, cw, rw, c.raw_target);
+}
+
+// Exactly-once and chunk counters of a reduced tile.  They are taken only
+// after the tile's stores have drained (a released chunk must be complete),
+// at the end of the workgroup's next task, where their round trip overlaps
+// that task's own store drain.
+struct CntRead {
+    uint32_t tile;     // ~0u: nothing pending
+    uint32_t old_t, old_c;
+};
+constexpr uint32_t kNoTile = 0xFFFFFFFFu;
+
+__device__ __forceinline__ CntRead cnt_issue(const FusedArgs &a, uint32_t tile) {
+    CntRead k;
+    k.tile = tile;
+    k.old_t = k.old_c = 0;
+    if (tile != kNoTile) {
+        k.old_t = add_relaxed(&a.ws.tile_cnt[tile], 1u);
+        k.old_c = add_relaxed(&a.ws.chunk_cnt[tile / a.tpc], 1u);
     }
-    if (a.mode == kAdaptive) {
-        const uint64_t cw = b.role == kRoleCompute ? r.mine + inc : r.other;
-        const uint64_t rw = b.role == kRoleCompute ? r.other : r.mine + inc;
-        s.target = controller_step(a, L, cw, rw, r.raw_target);
+    return k;
+}
+
+// Thread 0: exactly-once check, and release of a chunk whose last tile this
+// was ("【学习】mKernel 分析" section 2.3).
+__device__ __forceinline__ void cnt_finish(const FusedArgs &a, Live *L, const CntRead &k) {
+    if (k.tile == kNoTile) return;
+    const uint32_t c = k.tile / a.tpc;
+    const uint32_t first = c * a.tpc;
+    const uint32_t size = (a.T - first) < a.tpc ? (a.T - first) : a.tpc;
+    const uint32_t want = size * a.calls;
+    if (k.old_t != a.calls - 1) add_relaxed(&L->violations, 1u);
+    if (k.old_c + 1 == want) {
+        // where a network send of the chunk would be posted
+        st_relaxed(&a.ws.chunk_flag[c], a.epoch);
+        add_relaxed(&L->chunks_released, 1u);
+    } else if (k.old_c + 1 > want) {
+        add_relaxed(&L->violations, 1u);
     }
 }
 
@@ -870,6 +1051,10 @@ __global__ __launch_bounds__((GemmFor<TM, TN, kPolicyCoherentStore>::NT)) void f
     using G = GemmFor<TM, TN, kPolicyCoherentStore>;
     __shared__ __attribute__((aligned(1024))) char lds_raw[fused_lds_bytes<TM, TN>()];
     __shared__ Decision sh_dec;
+    // thread 0's scheduling state lives in LDS, not in registers every lane
+    // would have to reserve next to the GEMM's
+    __shared__ Sched sh_sched;
+    __shared__ uint64_t sh_c0, sh_r0;
     lchar *lds = (lchar *)lds_raw;
 
     const int tid = threadIdx.x;
@@ -878,100 +1063,119 @@ __global__ __launch_bounds__((GemmFor<TM, TN, kPolicyCoherentStore>::NT)) void f
     typename G::Lane ln;
     G::init_lane(ln, a.N, a.K);
 
-    Sched s;
-    s.det_i = 0;
-    s.last_role = kRoleNone;
-    s.compute_exhausted = false;
-    s.parts_done = 0;
-    s.reduce_exhausted = false;
-    const Parts pt = make_parts((uint32_t)a.nxcd, (uint32_t)a.tiles_m, (uint32_t)a.tiles_n, a.tpc,
+    constexpr int TPB = TileCfg<TM, TN>::TPB;
+    const Blocks bk = make_blocks(TPB, (uint32_t)a.tiles_m, (uint32_t)a.tiles_n);
+    const Parts pt = make_parts((uint32_t)a.nxcd, (uint32_t)a.tiles_m, bk.bn, chunk_blocks(a.tpc, TPB),
                                 (uint32_t)a.group_m);
-    s.pending_role = kRoleNone;
-    s.pending_q = 0;
-    s.pending_ns = 0;
-    s.wait_start = 0;
-    s.target = (uint32_t)a.ns_init;   // the launch starts with the target unset
-    s.early_claim = false;
-    s.early_x = s.early_i = s.early_ns = 0;
-    s.early_flag = false;
-    s.early_flag_value = 0;
-    s.decide_t0 = s.decide_t1 = 0;
-    if (tid == 0) min_relaxed(&L->t_start, ticks_now());
+    Sched &s = sh_sched;
+    if (tid == 0) {
+        s.det_i = 0;
+        s.last_role = kRoleNone;
+        s.compute_exhausted = false;
+        s.parts_done = 0;
+        s.reduce_exhausted = false;
+        s.pending_role = kRoleNone;
+        s.pending_q = 0;
+        s.pending_ns = 0;
+        s.wait_start = 0;
+        s.target = (uint32_t)a.ns_init;   // the launch starts with the target unset
+        s.early_claim = false;
+        s.early_x = s.early_i = s.early_ns = 0;
+        s.early_flag = false;
+        s.early_flag_value = 0;
+        s.decide_t0 = s.decide_t1 = 0;
+        min_relaxed(&L->t_start, ticks_now());
+    }
 
-    // Bookkeeping of a finished task (progress word, exactly-once counters,
-    // chunk counter, controller inputs) is issued by thread 0 right after the
-    // next task starts and read back when that task ends, so its device-scope
-    // round trips overlap work instead of stalling the workgroup.  Readiness
-    // flags are not deferred: they are stored as soon as the tile is complete.
-    Booked bk;
-    bk.valid = false;
-    BookResult br;
+    // At the end of every task thread 0 records it in its role word and runs
+    // one controller step on fresh values, so the role of the next task is
+    // decided on current progress; the round trips of these atomics overlap
+    // the task's store drain.  The counters of a reduced tile wait for the end
+    // of the workgroup's next task (see CntRead).
+    __shared__ uint32_t sh_pend;
+    if (tid == 0) sh_pend = kNoTile;
     for (;;) {
         if (tid == 0) {
             s.decide_t0 = ticks_now();
-            const Decision d = next_task(a, pt, L, wg, s);
+            const Decision d = next_task(a, pt, bk, L, wg, s);
             s.decide_t1 = ticks_now();
             if (d.role == kRoleReduce) prefetch_claim(a, L, wg, s, d);
             sh_dec = d;
+            sh_c0 = cycles_now();
+            sh_r0 = ticks_now();
         }
         __syncthreads();
-        const Decision d = sh_dec;
+        // the decision is workgroup-uniform: keep it in scalar registers, so
+        // tile bases and buffer resources derived from it are scalar too
+        Decision d;
+        d.role = __builtin_amdgcn_readfirstlane(sh_dec.role);
+        d.tile = __builtin_amdgcn_readfirstlane(sh_dec.tile);
+        d.ns_seen = __builtin_amdgcn_readfirstlane(sh_dec.ns_seen);
         if (d.role == kRoleExit) break;
-        if (tid == 0 && bk.valid) br = book_issue(a, L, bk);
-        const uint64_t c0 = tid == 0 ? cycles_now() : 0;
-        const uint64_t r0 = tid == 0 ? ticks_now() : 0;
-        const int ti = (int)(d.tile / (uint32_t)a.tiles_n);
-        const int tj = (int)(d.tile % (uint32_t)a.tiles_n);
+        // compute: tiles [t0, t0 + nt) of block d.tile; reduce: tile t0
+        const uint32_t t0 = d.role == kRoleCompute ? bk.first_tile(d.tile) : d.tile;
+        const uint32_t nt = d.role == kRoleCompute ? bk.count(d.tile) : 1u;
+        const int ti = (int)(t0 / (uint32_t)a.tiles_n);
+        const int tj = (int)(t0 % (uint32_t)a.tiles_n);
 
-        if (d.role == kRoleCompute) {
-            G::tile(ln, a.A, a.B, a.C, a.M, a.N, a.K, ti, tj, lds);
-            if (tid == 0) early_next(a, pt, L, wg, s);
-            // payload before flag ("【学习】mKernel 分析" section 2.5): every wave's
-            // device-coherent tile stores have completed before thread 0
-            // publishes the tile
-            drain_vmem();
-            __syncthreads();
+        CtlRead ctl;
+        CntRead cnt;
+        // progress is counted in tiles for both roles, so the controller's
+        // R_p C_p is the same remaining time whatever the block size
+        auto work_done = [&](int role) {
             if (tid == 0) {
-                if ((int64_t)d.tile != a.skip_publish) st_relaxed(&a.ws.tile_flag[d.tile], a.epoch);
-                a.ws.cowner[d.tile] = (d.ns_seen << 16) | wg;
+                cnt = cnt_issue(a, sh_pend);
+                ctl = ctl_issue(a, L, role, nt, cycles_now() - sh_c0, sh_r0, ticks_now());
             }
+        };
+        if (d.role == kRoleCompute) {
+            G::block(ln, a.A, a.B, a.C, a.M, a.N, a.K, (int64_t)ti * TM, (int64_t)tj * TN, lds,
+                     [&] { work_done(kRoleCompute); });
         } else {
             // thread 0 saw the flag before the barrier; the partial is read
             // with device-coherent loads, after it
             if (a.P > 0) reduce_tile<TM, TN, G::NT>(a.peers, a.C, a.M, a.N, a.P, ti, tj);
-            if (tid == 0) early_next(a, pt, L, wg, s);
-            // the reduced tile is complete before its chunk can be released
-            drain_vmem();
-            __syncthreads();
-            if (tid == 0) a.ws.rowner[d.tile] = (d.ns_seen << 16) | wg;
+            work_done(kRoleReduce);
         }
         if (tid == 0) {
-            if (bk.valid) book_finish(a, L, bk, br, s);
-            bk.valid = true;
-            bk.role = d.role;
-            bk.tile = d.tile;
-            bk.dt = cycles_now() - c0;
-            bk.r0 = r0;
-            bk.r1 = ticks_now();
-            // per-tile timeline (low 32 bits of the constant clock)
-            uint32_t *tl = a.ws.timeline + (d.role == kRoleCompute ? 0u : 2u * a.Tcap);
-            tl[d.tile] = (uint32_t)r0;
-            tl[a.Tcap + d.tile] = (uint32_t)bk.r1;
-            // how long choosing this task took (claim, readiness wait)
-            a.ws.timeline[(d.role == kRoleCompute ? 4u : 5u) * a.Tcap + d.tile] =
-                (uint32_t)(s.decide_t1 - s.decide_t0);
+            cnt_finish(a, L, cnt);
+            ctl_finish(a, L, d.role, ctl, s);
+            early_next(a, pt, bk, L, wg, s);
+        }
+        // payload before flag ("【学习】mKernel 分析" section 2.5): every wave's
+        // device-coherent tile stores have completed before thread 0
+        // publishes the tile (compute) or counts it toward its chunk (reduce)
+        drain_vmem();
+        __syncthreads();
+        if (tid == 0) {
+            const uint32_t t_end = (uint32_t)ticks_now();
+            for (uint32_t k = 0; k < nt; ++k) {
+                const uint32_t t = t0 + k;
+                if (d.role == kRoleCompute) {
+                    if ((int64_t)t != a.skip_publish) st_relaxed(&a.ws.tile_flag[t], a.epoch);
+                    a.ws.cowner[t] = (d.ns_seen << 16) | wg;
+                } else {
+                    a.ws.rowner[t] = (d.ns_seen << 16) | wg;
+                }
+                // per-tile timeline (low 32 bits of the constant clock)
+                uint32_t *tl = a.ws.timeline + (d.role == kRoleCompute ? 0u : 2u * a.Tcap);
+                tl[t] = (uint32_t)sh_r0;
+                tl[a.Tcap + t] = t_end;
+                // how long choosing this task took (claim, readiness wait)
+                a.ws.timeline[(d.role == kRoleCompute ? 4u : 5u) * a.Tcap + t] =
+                    (uint32_t)(s.decide_t1 - s.decide_t0);
+            }
+            sh_pend = d.role == kRoleCompute ? kNoTile : t0;
             if (s.last_role != kRoleNone && s.last_role != d.role) add_relaxed(&L->role_switches, 1u);
             s.last_role = d.role;
         }
         // sh_dec is rewritten only after every thread has read it
         __syncthreads();
     }
-    if (tid == 0 && bk.valid) {
-        br = book_issue(a, L, bk);
-        book_finish(a, L, bk, br, s);
-    }
-
     if (tid == 0) {
+        // counters of the last reduced tile; nothing else is in flight
+        const CntRead k = cnt_issue(a, sh_pend);
+        cnt_finish(a, L, k);
         max_relaxed(&L->t_end, ticks_now());
         const uint32_t old = add_acq_rel(&L->exit_count, 1u);
         if (old == (uint32_t)a.nwg - 1) finish_launch(a, L);
@@ -982,21 +1186,22 @@ __global__ __launch_bounds__((GemmFor<TM, TN, kPolicyCoherentStore>::NT)) void f
 // unfused baseline: a GEMM kernel writes C_r, then a reduce kernel adds peers
 // ---------------------------------------------------------------------------
 
-// persistent GEMM over all tiles in the same claim order, same MFMA core
+// persistent GEMM over all blocks in the same claim order, same MFMA core
 template <int TM, int TN>
 __global__ __launch_bounds__((GemmFor<TM, TN, kPolicyDefault>::NT)) void gemm_kernel(GemmArgs a) {
     using G = GemmFor<TM, TN, kPolicyDefault>;
+    constexpr int TPB = TileCfg<TM, TN>::TPB;
     __shared__ __attribute__((aligned(1024))) char lds_raw[G::LDS_BYTES];
     lchar *lds = (lchar *)lds_raw;
     typename G::Lane ln;
     G::init_lane(ln, a.N, a.K);
-    const uint32_t T = (uint32_t)a.tiles_m * (uint32_t)a.tiles_n;
-    const Parts pt = make_parts((uint32_t)a.nxcd, (uint32_t)a.tiles_m, (uint32_t)a.tiles_n,
-                                (uint32_t)a.tpc, (uint32_t)a.group_m);
-    for (uint32_t q = blockIdx.x; q < T; q += gridDim.x) {
-        const uint32_t t = pt.ticket(q);
-        G::tile(ln, a.A, a.B, a.C, a.M, a.N, a.K, (int)(t / (uint32_t)a.tiles_n),
-                (int)(t % (uint32_t)a.tiles_n), lds);
+    const Blocks bk = make_blocks(TPB, (uint32_t)a.tiles_m, (uint32_t)a.tiles_n);
+    const Parts pt = make_parts((uint32_t)a.nxcd, (uint32_t)a.tiles_m, bk.bn,
+                                chunk_blocks((uint32_t)a.tpc, TPB), (uint32_t)a.group_m);
+    for (uint32_t q = blockIdx.x; q < bk.TB; q += gridDim.x) {
+        const uint32_t t0 = bk.first_tile(pt.ticket(q));
+        G::block(ln, a.A, a.B, a.C, a.M, a.N, a.K, (int64_t)(t0 / (uint32_t)a.tiles_n) * TM,
+                 (int64_t)(t0 % (uint32_t)a.tiles_n) * TN, lds, [] {});
     }
 }
 
@@ -1090,6 +1295,13 @@ __global__ void controller_eval_kernel(const uint64_t *in, uint32_t *out, int n)
 // launchers
 // ---------------------------------------------------------------------------
 
+int tiles_per_block(int tm, int tn) {
+    if (tm == 64 && tn == 64) return TileCfg<64, 64>::TPB;
+    if (tm == 128 && tn == 128) return TileCfg<128, 128>::TPB;
+    if (tm == 256 && tn == 128) return TileCfg<256, 128>::TPB;
+    return 0;
+}
+
 bool tile_supported(int tm, int tn) {
     return (tm == 64 && tn == 64) || (tm == 128 && tn == 128) || (tm == 256 && tn == 128);
 }
@@ -1111,9 +1323,10 @@ hipError_t launch_fused(int tm, int tn, const FusedArgs &a, hipStream_t s) {
 template <int TM, int TN>
 static hipError_t launch_gemm_t(const GemmArgs &a, int num_cu, hipStream_t s) {
     using G = GemmFor<TM, TN, kPolicyDefault>;
+    constexpr int TPB = TileCfg<TM, TN>::TPB;
     const int per_cu = (160 * 1024) / G::LDS_BYTES >= 2 ? 2 : 1;
-    const int64_t T = (int64_t)a.tiles_m * a.tiles_n;
-    const int64_t grid = T < (int64_t)num_cu * per_cu ? T : (int64_t)num_cu * per_cu;
+    const int64_t TB = (int64_t)a.tiles_m * ((a.tiles_n + TPB - 1) / TPB);
+    const int64_t grid = TB < (int64_t)num_cu * per_cu ? TB : (int64_t)num_cu * per_cu;
     hipLaunchKernelGGL((gemm_kernel<TM, TN>), dim3((unsigned)grid), dim3(G::NT), 0, s, a);
     return hipGetLastError();
 }

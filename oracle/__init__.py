@@ -257,14 +257,33 @@ def chunk_sizes(T: int, tiles_per_chunk: int) -> np.ndarray:
     return sizes
 
 
-def deterministic_owners(T: int, B: int, n_reduce: int) -> Tuple[np.ndarray, np.ndarray]:
+def compute_task_of_tile(T: int, tiles_n: Optional[int], tiles_per_task: int) -> np.ndarray:
+    """Index of the compute task that produces each tile.
+
+    A compute task covers `tiles_per_task` adjacent tiles of one tile row
+    (the last task of a row may hold fewer); tasks are numbered row by row.
+    With one tile per task this is the tile index itself.
+    """
+    t = np.arange(T, dtype=np.int64)
+    if tiles_per_task == 1:
+        return t
+    tn = int(tiles_n)
+    per_row = -(-tn // tiles_per_task)
+    return (t // tn) * per_row + (t % tn) // tiles_per_task
+
+
+def deterministic_owners(T: int, B: int, n_reduce: int, tiles_n: Optional[int] = None,
+                         tiles_per_task: int = 1) -> Tuple[np.ndarray, np.ndarray]:
     """Owner maps of the deterministic static schedule.
 
     Workgroups [0, n_reduce) reduce and the rest compute (roles by workgroup
-    index); each takes its tiles round-robin in increasing tile order.
+    index).  Reducers take tiles round-robin in increasing tile order;
+    compute workgroups take compute tasks round-robin in increasing task
+    order, and every tile of a task has that task's owner.
     """
     t = np.arange(T, dtype=np.int64)
-    return n_reduce + t % (B - n_reduce), t % n_reduce
+    task = compute_task_of_tile(T, tiles_n, tiles_per_task)
+    return n_reduce + task % (B - n_reduce), t % n_reduce
 
 
 OWNER_WG_MASK = 0xFFFF
@@ -283,11 +302,13 @@ def expected_state(T: int, tiles_per_chunk: int, epoch: int, calls: int) -> Dict
 
 
 def check_state(maps: Dict[str, np.ndarray], T: int, tiles_per_chunk: int, epoch: int,
-                calls: int, B: int, mode: str, n_reduce: int) -> List[str]:
+                calls: int, B: int, mode: str, n_reduce: int, tiles_n: Optional[int] = None,
+                tiles_per_task: int = 1) -> List[str]:
     """Compare the protocol state against its closed form.
 
     Returns a list of human-readable violations (empty when all holds).
-    `mode` is "deterministic", "static" or "adaptive".
+    `mode` is "deterministic", "static" or "adaptive"; `tiles_n` (tiles per
+    tile row) and `tiles_per_task` describe the compute tasks.
     """
     bad: List[str] = []
     exp = expected_state(T, tiles_per_chunk, epoch, calls)
@@ -306,13 +327,20 @@ def check_state(maps: Dict[str, np.ndarray], T: int, tiles_per_chunk: int, epoch
     co_wg, co_ns = co & OWNER_WG_MASK, co >> 16
     ro_wg, ro_ns = ro & OWNER_WG_MASK, ro >> 16
     if mode == "deterministic":
-        dc, dr = deterministic_owners(T, B, n_reduce)
+        dc, dr = deterministic_owners(T, B, n_reduce, tiles_n, tiles_per_task)
         if not np.array_equal(co_wg, dc):
             i = int(np.nonzero(co_wg != dc)[0][0])
             bad.append(f"compute_owner[{i}] = {int(co_wg[i])}, expected {int(dc[i])}")
         if not np.array_equal(ro_wg, dr):
             i = int(np.nonzero(ro_wg != dr)[0][0])
             bad.append(f"reduce_owner[{i}] = {int(ro_wg[i])}, expected {int(dr[i])}")
+    if tiles_per_task > 1 and T:
+        task = compute_task_of_tile(T, tiles_n, tiles_per_task)
+        first = np.zeros(int(task.max()) + 1, dtype=np.int64)
+        first[task[::-1]] = co[::-1]
+        if np.any(co != first[task]):
+            i = int(np.nonzero(co != first[task])[0][0])
+            bad.append(f"tile {i}: owner word differs from the rest of its compute task")
     if np.any(co_wg >= B):
         bad.append("compute owner outside [0, B)")
     if np.any(ro_wg >= B):

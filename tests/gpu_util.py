@@ -88,7 +88,8 @@ def check_sampled(C, a, b, p, rng, n_samples=4096, tiles=(), tile=(128, 128)):
 
 def check_protocol(st, w, mode, n_reduce):
     bad = oracle.check_state(st, w.tiles, w.tiles_per_chunk, st["epoch"], st["calls_since_reset"],
-                             st["num_wg"], mode, n_reduce)
+                             st["num_wg"], mode, n_reduce, tiles_n=-(-w.N // w.tile_n),
+                             tiles_per_task=st["tiles_per_task"])
     assert not bad, bad
     assert st["status"] == 0, st["status_name"]
     assert st["compute_tasks"] == w.tiles and st["reduce_tasks"] == w.tiles

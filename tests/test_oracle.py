@@ -280,6 +280,36 @@ def test_deterministic_owners_partition_tiles():
         np.testing.assert_array_equal(np.nonzero(ro == w)[0], np.arange(w, T, ns))
 
 
+def test_compute_task_of_tile_hand_example():
+    # 2 tile rows of 5 tiles, 2 tiles per task: the last task of a row is short
+    np.testing.assert_array_equal(oracle.compute_task_of_tile(10, 5, 2),
+                                  [0, 0, 1, 1, 2, 3, 3, 4, 4, 5])
+    np.testing.assert_array_equal(oracle.compute_task_of_tile(6, 3, 1), np.arange(6))
+
+
+def test_deterministic_owners_with_blocks():
+    tiles_n, tiles_m, B, ns = 6, 4, 5, 2
+    T = tiles_n * tiles_m
+    co, ro = oracle.deterministic_owners(T, B, ns, tiles_n, 2)
+    # tasks (0..11, three per row) go round-robin to workgroups 2, 3, 4
+    want = [2, 2, 3, 3, 4, 4, 2, 2, 3, 3, 4, 4, 2, 2, 3, 3, 4, 4, 2, 2, 3, 3, 4, 4]
+    np.testing.assert_array_equal(co, want)
+    np.testing.assert_array_equal(ro, np.arange(T) % ns)
+
+
+def test_check_state_rejects_split_task_owner():
+    T, tiles_n, B, ns = 12, 4, 8, 2
+    exp = oracle.expected_state(T, 4, 1, 1)
+    co, ro = oracle.deterministic_owners(T, B, ns, tiles_n, 2)
+    maps = {k: v.copy() for k, v in exp.items()}
+    maps["compute_owner"] = co | (ns << 16)
+    maps["reduce_owner"] = ro | (ns << 16)
+    assert oracle.check_state(maps, T, 4, 1, 1, B, "static", ns, tiles_n, 2) == []
+    assert oracle.check_state(maps, T, 4, 1, 1, B, "deterministic", ns, tiles_n, 2) == []
+    maps["compute_owner"][5] = (ns << 16) | 7     # the other tile of its task stays with 4
+    assert oracle.check_state(maps, T, 4, 1, 1, B, "static", ns, tiles_n, 2)
+
+
 def _good_maps(T, tpc, epoch, calls, B, ns):
     exp = oracle.expected_state(T, tpc, epoch, calls)
     co, ro = oracle.deterministic_owners(T, B, ns)
