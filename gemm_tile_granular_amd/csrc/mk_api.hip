@@ -263,9 +263,14 @@ int run(bool fused, const void *A, const void *B, const float *peers, int num_pe
         return MK_OK;
     }
 
-    const int nwg = set.num_wg ? set.num_wg : (d.num_cu < kMaxWG ? d.num_cu : kMaxWG);
-    if (nwg < 2 || nwg > d.num_cu)
-        return fail(MK_ERR_INVALID_ARG, "workgroups %d outside [2, %d compute units]", nwg, d.num_cu);
+    // every workgroup of the persistent grid must be resident at once
+    const int per_cu = workgroups_per_cu(tile_m, tile_n);
+    if (per_cu < 1) return fail(MK_ERR_HIP, "occupancy query for the fused kernel failed");
+    const int resident = d.num_cu * per_cu;
+    const int nwg = set.num_wg ? set.num_wg : (resident < kMaxWG ? resident : kMaxWG);
+    if (nwg < 2 || nwg > resident)
+        return fail(MK_ERR_INVALID_ARG, "workgroups %d outside [2, %d resident workgroups]", nwg,
+                    resident);
     int ns_init = set.n_reduce;
     if (set.mode == MK_PART_ADAPTIVE) {
         if (ns_init == 0) ns_init = 2;

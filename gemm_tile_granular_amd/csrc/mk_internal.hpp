@@ -13,7 +13,6 @@ constexpr uint32_t kMaxTiles = 1u << 22;
 constexpr uint64_t kCostCap = (1ull << 26) - 1;   // per-task mean cycles saturate here
 constexpr int kTraceCap = 1024;
 constexpr int kMaxXcd = 8;            // XCDs on MI355X (tile partitions)
-constexpr int kFusedLdsBytes = 96 * 1024;         // > half of the 160 KiB LDS: 1 WG per CU
 
 enum Mode : int32_t { kAdaptive = 0, kStatic = 1, kDeterministic = 2 };
 enum Err : uint32_t { kErrNone = 0, kErrTimeout = 1 };
@@ -117,5 +116,6 @@ hipError_t launch_fill_u32(uint32_t *p, uint32_t value, int64_t n, hipStream_t s
 hipError_t launch_controller_eval(const uint64_t *in, uint32_t *out, int n, hipStream_t s);
 bool tile_supported(int tile_m, int tile_n);
 int tiles_per_block(int tile_m, int tile_n);   // output tiles per compute task
+int workgroups_per_cu(int tile_m, int tile_n); // fused workgroups resident per CU
 
 }  // namespace mk

@@ -42,8 +42,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // Tile data crosses XCDs (a tile computed on one XCD is reduced on another),
 // but only the tile hand-off needs device-scope coherence: A, B and the peers
 // are read-only during a launch.  So the partial tile is stored with sc1
-// (coherent at device scope) and read back with sc0|sc1 (bypassing the CU's
-// L1, coherent at device scope); the writer drains its stores (vmcnt) before
+// (coherent at device scope) and read back with sc1 loads (device scope: not
+// served from a stale line of the reader's caches); the writer drains its stores (vmcnt) before
 // the flag is set.  This replaces agent-scope release/acquire fences, whose
 // whole-L2 writeback and invalidate per tile cost 2-3x in reduce bandwidth.
 // Buffer resources also give branch-free edge masking: an offset at or past
@@ -53,7 +53,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kPolicyDefault = 0;
 constexpr int kPolicyStream = 2;            // nt: read-once / write-once data
 constexpr int kPolicyCoherentStore = 16;    // sc1: visible at device scope
-constexpr int kPolicyCoherentLoad = 17;     // sc0 sc1: bypass L1, device-coherent
+constexpr int kPolicyCoherentLoad = 16;     // sc1: coherent at device (agent) scope
 constexpr int kPolicyCoherentStream = 18;   // nt sc1
 constexpr uint32_t kOOB = 0x80000000u;
 constexpr uint32_t kNumRecords = 0x7FFFFFFFu;
@@ -514,16 +514,18 @@ struct Gemm {
 // Compute blocks per tile shape.  One MI355X CU fetches operands at a bounded
 // rate, so a compute task covers TPB output tiles side by side (one block of
 // BM x (TPB*TN)) when that lowers the operand bytes per flop: two 128-wide
-// tiles share their A rows.  Tiles of one block always lie in one chunk.
+// tiles share their A rows.  WPC workgroups share one CU (LDS and registers
+// sized for it); one per CU measured best for every shape here (a second
+// workgroup per CU slowed both the GEMM and the fused schedule).
 template <int TM, int TN> struct TileCfg;
 template <> struct TileCfg<64, 64> {
-    static constexpr int TPB = 1, KB = 64, NS = 4, WGM = 2, WGN = 2;
+    static constexpr int TPB = 1, KB = 64, NS = 4, WGM = 2, WGN = 2, WPC = 1;
 };
 template <> struct TileCfg<128, 128> {
-    static constexpr int TPB = 2, KB = 64, NS = 3, WGM = 2, WGN = 2;
+    static constexpr int TPB = 2, KB = 64, NS = 3, WGM = 2, WGN = 2, WPC = 1;
 };
 template <> struct TileCfg<256, 128> {
-    static constexpr int TPB = 2, KB = 32, NS = 4, WGM = 4, WGN = 2;
+    static constexpr int TPB = 2, KB = 32, NS = 4, WGM = 4, WGN = 2, WPC = 1;
 };
 
 template <int TM, int TN, int kStorePolicy>
@@ -550,9 +552,9 @@ struct ReducePlan {
                            : (kLoads / (PP + 1)) >= 2 ? 2 : 1;
 };
 
-template <int TM, int TN, int NT>
+template <int TM, int BW, int NT>
 struct ReduceGeom {
-    static constexpr int C4 = TN / 4;              // float4 per tile row
+    static constexpr int C4 = BW / 4;              // float4 per row of the region
     static constexpr int RP = NT / C4;             // rows per pass
     static constexpr int PASSES = TM / RP;
     static_assert(NT % C4 == 0 && TM % RP == 0, "reduce layout");
@@ -565,17 +567,17 @@ struct ReduceGroup {
     uint32_t off[U];
 };
 
-template <int TM, int TN, int NT, int PP>
-__device__ __forceinline__ void reduce_tile_pp(const float *__restrict__ peers, float *__restrict__ C, int64_t M,
-                               int64_t N, int P, int ti, int tj) {
-    using RG = ReduceGeom<TM, TN, NT>;
+// Region of TM rows x BW columns at (m0, n0): the tiles of one compute block.
+template <int TM, int BW, int NT, int PP>
+__device__ __forceinline__ void reduce_tile_pp(const float *__restrict__ peers, float *__restrict__ C,
+                                               int64_t M, int64_t N, int P, int64_t m0, int64_t n0) {
+    using RG = ReduceGeom<TM, BW, NT>;
     constexpr int PB = 8;                   // peer block when PP is the generic 0
     constexpr int UP = ReducePlan<(PP > 0 ? PP : PB), NT>::U;
     constexpr int U = UP < RG::PASSES ? UP : RG::PASSES;
     constexpr int G = RG::PASSES / U;
     static_assert(RG::PASSES % U == 0, "reduce layout");
     const int tid = threadIdx.x;
-    const int64_t m0 = (int64_t)ti * TM, n0 = (int64_t)tj * TN;
     const int64_t base = m0 * N + n0;
     const int64_t MN = M * N;
     const int cc = (tid % RG::C4) * 4;
@@ -590,7 +592,7 @@ __device__ __forceinline__ void reduce_tile_pp(const float *__restrict__ peers, 
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int r = (gi * U + u) * RG::RP + r0;
-                g.off[u] = (col_ok && m0 + r < M) ? (uint32_t)((r * N + cc) * 4) : kOOB;
+                g.off[u] = ((int)col_ok & (int)(m0 + r < M)) ? (uint32_t)((r * N + cc) * 4) : kOOB;
                 g.v[0][u] = __builtin_amdgcn_raw_buffer_load_b128(rc, g.off[u], 0, kPolicyCoherentLoad);
             }
 #pragma unroll
@@ -631,7 +633,7 @@ __device__ __forceinline__ void reduce_tile_pp(const float *__restrict__ peers, 
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int r = (gi * U + u) * RG::RP + r0;
-                off[u] = (col_ok && m0 + r < M) ? (uint32_t)((r * N + cc) * 4) : kOOB;
+                off[u] = ((int)col_ok & (int)(m0 + r < M)) ? (uint32_t)((r * N + cc) * 4) : kOOB;
                 acc[u] = __builtin_amdgcn_raw_buffer_load_b128(rc, off[u], 0, kPolicyCoherentLoad);
             }
             int p = 0;
@@ -664,18 +666,18 @@ __device__ __forceinline__ void reduce_tile_pp(const float *__restrict__ peers, 
 
 // Dispatch on the peer count so that every load of a pass group is a
 // straight-line instruction (counts above 16 take the blocked loop).
-template <int TM, int TN, int NT>
-__device__ __forceinline__ void reduce_tile(const float *__restrict__ peers, float *__restrict__ C, int64_t M,
-                            int64_t N, int P, int ti, int tj) {
+template <int TM, int BW, int NT>
+__device__ __forceinline__ void reduce_tile(const float *__restrict__ peers, float *__restrict__ C,
+                                            int64_t M, int64_t N, int P, int64_t m0, int64_t n0) {
     switch (P) {
 #define MK_REDUCE_CASE(k) \
-    case k: reduce_tile_pp<TM, TN, NT, k>(peers, C, M, N, P, ti, tj); break;
+    case k: reduce_tile_pp<TM, BW, NT, k>(peers, C, M, N, P, m0, n0); break;
         MK_REDUCE_CASE(1) MK_REDUCE_CASE(2) MK_REDUCE_CASE(3) MK_REDUCE_CASE(4)
         MK_REDUCE_CASE(5) MK_REDUCE_CASE(6) MK_REDUCE_CASE(7) MK_REDUCE_CASE(8)
         MK_REDUCE_CASE(9) MK_REDUCE_CASE(10) MK_REDUCE_CASE(11) MK_REDUCE_CASE(12)
         MK_REDUCE_CASE(13) MK_REDUCE_CASE(14) MK_REDUCE_CASE(15) MK_REDUCE_CASE(16)
 #undef MK_REDUCE_CASE
-        default: reduce_tile_pp<TM, TN, NT, 0>(peers, C, M, N, P, ti, tj); break;
+        default: reduce_tile_pp<TM, BW, NT, 0>(peers, C, M, N, P, m0, n0); break;
     }
 }
 
@@ -692,13 +694,15 @@ struct Decision {
 };
 
 // Compute tasks are blocks of tpb adjacent tiles of one tile row (a ragged
-// last block holds fewer).  Reduce tickets run over tpb slots per block in
-// the order blocks are claimed; the slot of a missing tile is skipped.
+// last block holds fewer).  A reduce task takes the same block once every
+// tile of it is published: the tiles become ready together, and the wider
+// region streams from HBM in longer contiguous runs.
+constexpr int kMaxTpb = 2;   // largest tiles-per-block of any tile configuration
+
 struct Blocks {
     uint32_t tpb;       // tiles per block
     uint32_t bn;        // blocks per tile row
     uint32_t TB;        // blocks
-    uint32_t slots;     // reduce ticket slots, TB * tpb
     uint32_t tiles_n;
     __device__ __forceinline__ uint32_t first_tile(uint32_t b) const {
         return (b / bn) * tiles_n + (b % bn) * tpb;
@@ -714,7 +718,6 @@ __device__ __forceinline__ Blocks make_blocks(uint32_t tpb, uint32_t tiles_m, ui
     k.tpb = tpb;
     k.bn = (tiles_n + tpb - 1) / tpb;
     k.TB = tiles_m * k.bn;
-    k.slots = k.TB * tpb;
     k.tiles_n = tiles_n;
     return k;
 }
@@ -724,13 +727,6 @@ __device__ __forceinline__ uint32_t chunk_blocks(uint32_t tpc, uint32_t tpb) {
     return (tpc % tpb) == 0 ? tpc / tpb : 1u;
 }
 
-// tile of reduce ticket q; false for the empty slot of a ragged block
-__device__ __forceinline__ bool ticket_tile(const Parts &pt, const Blocks &bk, uint32_t q, uint32_t &t) {
-    const uint32_t b = pt.ticket(q / bk.tpb), k = q % bk.tpb;
-    if (k >= bk.count(b)) return false;
-    t = bk.first_tile(b) + k;
-    return true;
-}
 
 // Scheduling state kept by thread 0 of each workgroup.
 struct Sched {
@@ -748,8 +744,8 @@ struct Sched {
     // taken at the end of the previous task, while its stores drained:
     bool early_claim;          // a compute claim on partition early_x returned early_i
     uint32_t early_x, early_i, early_ns;
-    bool early_flag;           // the readiness flag of the pending ticket's tile
-    uint32_t early_flag_value;
+    bool early_flag;           // the readiness flags of the pending ticket's block
+    uint32_t early_flag_value; // their common value (0 if they differ)
 };
 
 __device__ __forceinline__ bool timed_out(const FusedArgs &a, Live *L, uint64_t since) {
@@ -771,6 +767,15 @@ __device__ bool wait_ready(const FusedArgs &a, Live *L, uint32_t t) {
     }
 }
 
+// Wait until every tile of block b is published (tiles after the first are
+// checked once the first is: one compute task stores their flags together).
+__device__ bool wait_block(const FusedArgs &a, const Blocks &bk, Live *L, uint32_t b) {
+    const uint32_t t0 = bk.first_tile(b), n = bk.count(b);
+    for (uint32_t k = 0; k < n; ++k)
+        if (!wait_ready(a, L, t0 + k)) return false;
+    return true;
+}
+
 // Thread 0 only: the next task.  Roles follow the workgroup index against the
 // current target and are re-read here, at every task boundary ("【学习】mKernel
 // 分析" sections 2.4 and 4.1).  Claims are tickets from device-scope counters
@@ -779,15 +784,15 @@ __device__ bool wait_ready(const FusedArgs &a, Live *L, uint32_t t) {
 // and is honoured first, so a role change takes effect one task later.
 __device__ Decision next_task(const FusedArgs &a, const Parts &pt, const Blocks &bk, Live *L, uint32_t wg,
                              Sched &s) {
-    const uint32_t B = (uint32_t)a.nwg, T = a.T;
+    const uint32_t B = (uint32_t)a.nwg;
     if (a.mode == kDeterministic) {
         const uint32_t ns = (uint32_t)a.ns_init;
         if (wg < ns) {
-            const uint32_t t = wg + s.det_i * ns;
-            if (t >= T) return {kRoleExit, 0, ns};
-            if (!wait_ready(a, L, t)) return {kRoleExit, 0, ns};
+            const uint32_t b = wg + s.det_i * ns;
+            if (b >= bk.TB) return {kRoleExit, 0, ns};
+            if (!wait_block(a, bk, L, b)) return {kRoleExit, 0, ns};
             ++s.det_i;
-            return {kRoleReduce, t, ns};
+            return {kRoleReduce, b, ns};
         }
         const uint32_t b = (wg - ns) + s.det_i * (B - ns);
         if (b >= bk.TB) return {kRoleExit, 0, ns};
@@ -807,11 +812,10 @@ __device__ Decision next_task(const FusedArgs &a, const Parts &pt, const Blocks 
             s.pending_role = kRoleNone;
             const bool seen = s.early_flag && s.early_flag_value == a.epoch;
             s.early_flag = false;
-            if (q < bk.slots) {
-                uint32_t t;
-                if (!ticket_tile(pt, bk, q, t)) continue;   // empty slot: take another ticket
-                if (!seen && !wait_ready(a, L, t)) return {kRoleExit, 0, ns_seen};
-                return {kRoleReduce, t, ns_seen};
+            if (q < bk.TB) {
+                const uint32_t b = pt.ticket(q);
+                if (!seen && !wait_block(a, bk, L, b)) return {kRoleExit, 0, ns_seen};
+                return {kRoleReduce, b, ns_seen};
             }
             s.reduce_exhausted = true;
             continue;
@@ -870,10 +874,14 @@ __device__ __forceinline__ void early_next(const FusedArgs &a, const Parts &pt, 
                                            Live *L, uint32_t wg, Sched &s) {
     if (a.mode == kDeterministic) return;
     if (s.pending_role == kRoleReduce) {
-        uint32_t t;
-        if (s.pending_q < bk.slots && ticket_tile(pt, bk, s.pending_q, t)) {
+        if (s.pending_q < bk.TB) {
+            // the block is ready when its first and last tiles are
+            const uint32_t b = pt.ticket(s.pending_q);
+            const uint32_t t0 = bk.first_tile(b), t1 = t0 + bk.count(b) - 1;
+            const uint32_t f0 = ld_relaxed(&a.ws.tile_flag[t0]);
+            const uint32_t f1 = ld_relaxed(&a.ws.tile_flag[t1]);
             s.early_flag = true;
-            s.early_flag_value = ld_relaxed(&a.ws.tile_flag[t]);
+            s.early_flag_value = f0 == f1 ? f0 : 0u;
         }
         return;
     }
@@ -1000,23 +1008,27 @@ __device__ __forceinline__ void ctl_finish(const FusedArgs &a, Live *L, int role
     s.target = controller_step(a, L, cw, rw, c.raw_target);
 }
 
-// Exactly-once and chunk counters of a reduced tile.  They are taken only
-// after the tile's stores have drained (a released chunk must be complete),
+// Exactly-once and chunk counters of the tiles of a reduced block.  They are
+// taken only after the block's stores have drained (a released chunk must be
+// complete),
 // at the end of the workgroup's next task, where their round trip overlaps
 // that task's own store drain.
 struct CntRead {
-    uint32_t tile;     // ~0u: nothing pending
-    uint32_t old_t, old_c;
+    uint32_t t0, n;    // tiles [t0, t0 + n) of the block; n == 0: nothing pending
+    uint32_t old_t[kMaxTpb], old_c[kMaxTpb];
 };
-constexpr uint32_t kNoTile = 0xFFFFFFFFu;
 
-__device__ __forceinline__ CntRead cnt_issue(const FusedArgs &a, uint32_t tile) {
+__device__ __forceinline__ CntRead cnt_issue(const FusedArgs &a, uint32_t t0, uint32_t n) {
     CntRead k;
-    k.tile = tile;
-    k.old_t = k.old_c = 0;
-    if (tile != kNoTile) {
-        k.old_t = add_relaxed(&a.ws.tile_cnt[tile], 1u);
-        k.old_c = add_relaxed(&a.ws.chunk_cnt[tile / a.tpc], 1u);
+    k.t0 = t0;
+    k.n = n;
+#pragma unroll
+    for (int i = 0; i < kMaxTpb; ++i) {
+        k.old_t[i] = k.old_c[i] = 0;
+        if ((uint32_t)i < n) {
+            k.old_t[i] = add_relaxed(&a.ws.tile_cnt[t0 + i], 1u);
+            k.old_c[i] = add_relaxed(&a.ws.chunk_cnt[(t0 + i) / a.tpc], 1u);
+        }
     }
     return k;
 }
@@ -1024,29 +1036,38 @@ __device__ __forceinline__ CntRead cnt_issue(const FusedArgs &a, uint32_t tile) 
 // Thread 0: exactly-once check, and release of a chunk whose last tile this
 // was ("【学习】mKernel 分析" section 2.3).
 __device__ __forceinline__ void cnt_finish(const FusedArgs &a, Live *L, const CntRead &k) {
-    if (k.tile == kNoTile) return;
-    const uint32_t c = k.tile / a.tpc;
-    const uint32_t first = c * a.tpc;
-    const uint32_t size = (a.T - first) < a.tpc ? (a.T - first) : a.tpc;
-    const uint32_t want = size * a.calls;
-    if (k.old_t != a.calls - 1) add_relaxed(&L->violations, 1u);
-    if (k.old_c + 1 == want) {
-        // where a network send of the chunk would be posted
-        st_relaxed(&a.ws.chunk_flag[c], a.epoch);
-        add_relaxed(&L->chunks_released, 1u);
-    } else if (k.old_c + 1 > want) {
-        add_relaxed(&L->violations, 1u);
+#pragma unroll
+    for (int i = 0; i < kMaxTpb; ++i) {
+        if ((uint32_t)i >= k.n) break;
+        const uint32_t t = k.t0 + i;
+        const uint32_t c = t / a.tpc;
+        const uint32_t first = c * a.tpc;
+        const uint32_t size = (a.T - first) < a.tpc ? (a.T - first) : a.tpc;
+        const uint32_t want = size * a.calls;
+        if (k.old_t[i] != a.calls - 1) add_relaxed(&L->violations, 1u);
+        if (k.old_c[i] + 1 == want) {
+            // where a network send of the chunk would be posted
+            st_relaxed(&a.ws.chunk_flag[c], a.epoch);
+            add_relaxed(&L->chunks_released, 1u);
+        } else if (k.old_c[i] + 1 > want) {
+            add_relaxed(&L->violations, 1u);
+        }
     }
 }
 
+// static LDS of the fused kernel: at least the GEMM ring, and more than
+// 160 KiB / (WPC + 1), so exactly WPC workgroups fit on a CU
 template <int TM, int TN>
 constexpr int fused_lds_bytes() {
     using G = GemmFor<TM, TN, kPolicyCoherentStore>;
-    return G::LDS_BYTES > kFusedLdsBytes ? G::LDS_BYTES : kFusedLdsBytes;
+    constexpr int floor_bytes = (160 * 1024) / (TileCfg<TM, TN>::WPC + 1) + 1024;
+    return G::LDS_BYTES > floor_bytes ? G::LDS_BYTES : floor_bytes;
 }
 
 template <int TM, int TN>
-__global__ __launch_bounds__((GemmFor<TM, TN, kPolicyCoherentStore>::NT)) void fused_gemm_reduce_kernel(
+__global__ __launch_bounds__((GemmFor<TM, TN, kPolicyCoherentStore>::NT),
+                             (TileCfg<TM, TN>::WPC * GemmFor<TM, TN, kPolicyCoherentStore>::NWAVES / 4))
+void fused_gemm_reduce_kernel(
     FusedArgs a) {
     using G = GemmFor<TM, TN, kPolicyCoherentStore>;
     __shared__ __attribute__((aligned(1024))) char lds_raw[fused_lds_bytes<TM, TN>()];
@@ -1064,6 +1085,7 @@ __global__ __launch_bounds__((GemmFor<TM, TN, kPolicyCoherentStore>::NT)) void f
     G::init_lane(ln, a.N, a.K);
 
     constexpr int TPB = TileCfg<TM, TN>::TPB;
+    static_assert(TPB <= kMaxTpb, "tiles per block");
     const Blocks bk = make_blocks(TPB, (uint32_t)a.tiles_m, (uint32_t)a.tiles_n);
     const Parts pt = make_parts((uint32_t)a.nxcd, (uint32_t)a.tiles_m, bk.bn, chunk_blocks(a.tpc, TPB),
                                 (uint32_t)a.group_m);
@@ -1092,8 +1114,8 @@ __global__ __launch_bounds__((GemmFor<TM, TN, kPolicyCoherentStore>::NT)) void f
     // decided on current progress; the round trips of these atomics overlap
     // the task's store drain.  The counters of a reduced tile wait for the end
     // of the workgroup's next task (see CntRead).
-    __shared__ uint32_t sh_pend;
-    if (tid == 0) sh_pend = kNoTile;
+    __shared__ uint32_t sh_pend_t0, sh_pend_n;   // reduced tiles whose counters are pending
+    if (tid == 0) sh_pend_n = 0;
     for (;;) {
         if (tid == 0) {
             s.decide_t0 = ticks_now();
@@ -1112,9 +1134,9 @@ __global__ __launch_bounds__((GemmFor<TM, TN, kPolicyCoherentStore>::NT)) void f
         d.tile = __builtin_amdgcn_readfirstlane(sh_dec.tile);
         d.ns_seen = __builtin_amdgcn_readfirstlane(sh_dec.ns_seen);
         if (d.role == kRoleExit) break;
-        // compute: tiles [t0, t0 + nt) of block d.tile; reduce: tile t0
-        const uint32_t t0 = d.role == kRoleCompute ? bk.first_tile(d.tile) : d.tile;
-        const uint32_t nt = d.role == kRoleCompute ? bk.count(d.tile) : 1u;
+        // tiles [t0, t0 + nt) of block d.tile
+        const uint32_t t0 = bk.first_tile(d.tile);
+        const uint32_t nt = bk.count(d.tile);
         const int ti = (int)(t0 / (uint32_t)a.tiles_n);
         const int tj = (int)(t0 % (uint32_t)a.tiles_n);
 
@@ -1124,7 +1146,7 @@ __global__ __launch_bounds__((GemmFor<TM, TN, kPolicyCoherentStore>::NT)) void f
         // R_p C_p is the same remaining time whatever the block size
         auto work_done = [&](int role) {
             if (tid == 0) {
-                cnt = cnt_issue(a, sh_pend);
+                cnt = cnt_issue(a, sh_pend_t0, sh_pend_n);
                 ctl = ctl_issue(a, L, role, nt, cycles_now() - sh_c0, sh_r0, ticks_now());
             }
         };
@@ -1134,7 +1156,9 @@ __global__ __launch_bounds__((GemmFor<TM, TN, kPolicyCoherentStore>::NT)) void f
         } else {
             // thread 0 saw the flag before the barrier; the partial is read
             // with device-coherent loads, after it
-            if (a.P > 0) reduce_tile<TM, TN, G::NT>(a.peers, a.C, a.M, a.N, a.P, ti, tj);
+            if (a.P > 0)
+                reduce_tile<TM, TPB * TN, G::NT>(a.peers, a.C, a.M, a.N, a.P, (int64_t)ti * TM,
+                                                 (int64_t)tj * TN);
             work_done(kRoleReduce);
         }
         if (tid == 0) {
@@ -1165,7 +1189,8 @@ __global__ __launch_bounds__((GemmFor<TM, TN, kPolicyCoherentStore>::NT)) void f
                 a.ws.timeline[(d.role == kRoleCompute ? 4u : 5u) * a.Tcap + t] =
                     (uint32_t)(s.decide_t1 - s.decide_t0);
             }
-            sh_pend = d.role == kRoleCompute ? kNoTile : t0;
+            sh_pend_t0 = t0;
+            sh_pend_n = d.role == kRoleCompute ? 0u : nt;
             if (s.last_role != kRoleNone && s.last_role != d.role) add_relaxed(&L->role_switches, 1u);
             s.last_role = d.role;
         }
@@ -1174,7 +1199,7 @@ __global__ __launch_bounds__((GemmFor<TM, TN, kPolicyCoherentStore>::NT)) void f
     }
     if (tid == 0) {
         // counters of the last reduced tile; nothing else is in flight
-        const CntRead k = cnt_issue(a, sh_pend);
+        const CntRead k = cnt_issue(a, sh_pend_t0, sh_pend_n);
         cnt_finish(a, L, k);
         max_relaxed(&L->t_end, ticks_now());
         const uint32_t old = add_acq_rel(&L->exit_count, 1u);
@@ -1188,7 +1213,9 @@ __global__ __launch_bounds__((GemmFor<TM, TN, kPolicyCoherentStore>::NT)) void f
 
 // persistent GEMM over all blocks in the same claim order, same MFMA core
 template <int TM, int TN>
-__global__ __launch_bounds__((GemmFor<TM, TN, kPolicyDefault>::NT)) void gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__((GemmFor<TM, TN, kPolicyDefault>::NT),
+                             (TileCfg<TM, TN>::WPC * GemmFor<TM, TN, kPolicyDefault>::NWAVES / 4))
+void gemm_kernel(GemmArgs a) {
     using G = GemmFor<TM, TN, kPolicyDefault>;
     constexpr int TPB = TileCfg<TM, TN>::TPB;
     __shared__ __attribute__((aligned(1024))) char lds_raw[G::LDS_BYTES];
@@ -1295,6 +1322,26 @@ __global__ void controller_eval_kernel(const uint64_t *in, uint32_t *out, int n)
 // launchers
 // ---------------------------------------------------------------------------
 
+// Workgroups of the fused kernel that stay resident on one CU: the tile
+// configuration's target, bounded by what the runtime reports for the
+// compiled kernel (registers, LDS).  0 on error.
+template <int TM, int TN>
+static int fused_residency() {
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &blocks, reinterpret_cast<const void *>(&fused_gemm_reduce_kernel<TM, TN>),
+            GemmFor<TM, TN, kPolicyCoherentStore>::NT, 0) != hipSuccess)
+        return 0;
+    return blocks < TileCfg<TM, TN>::WPC ? blocks : TileCfg<TM, TN>::WPC;
+}
+
+int workgroups_per_cu(int tm, int tn) {
+    if (tm == 64 && tn == 64) return fused_residency<64, 64>();
+    if (tm == 128 && tn == 128) return fused_residency<128, 128>();
+    if (tm == 256 && tn == 128) return fused_residency<256, 128>();
+    return 0;
+}
+
 int tiles_per_block(int tm, int tn) {
     if (tm == 64 && tn == 64) return TileCfg<64, 64>::TPB;
     if (tm == 128 && tn == 128) return TileCfg<128, 128>::TPB;
@@ -1324,7 +1371,7 @@ template <int TM, int TN>
 static hipError_t launch_gemm_t(const GemmArgs &a, int num_cu, hipStream_t s) {
     using G = GemmFor<TM, TN, kPolicyDefault>;
     constexpr int TPB = TileCfg<TM, TN>::TPB;
-    const int per_cu = (160 * 1024) / G::LDS_BYTES >= 2 ? 2 : 1;
+    const int per_cu = TileCfg<TM, TN>::WPC;
     const int64_t TB = (int64_t)a.tiles_m * ((a.tiles_n + TPB - 1) / TPB);
     const int64_t grid = TB < (int64_t)num_cu * per_cu ? TB : (int64_t)num_cu * per_cu;
     hipLaunchKernelGGL((gemm_kernel<TM, TN>), dim3((unsigned)grid), dim3(G::NT), 0, s, a);

@@ -64,10 +64,10 @@ typedef enum {
     MK_PART_ADAPTIVE = 0,
     /* Fixed count of reduce workgroups; tasks are claimed dynamically.     */
     MK_PART_STATIC = 1,
-    /* Fixed count; workgroup w < n reduces tiles t = w (mod n), workgroup
+    /* Fixed count; workgroup w < n reduces tasks b = w (mod n), workgroup
      * w >= n computes tasks b = w - n (mod B - n), each in increasing order
-     * (a compute task is the block of mk_stats.tiles_per_task adjacent tiles
-     * of one tile row; tasks are numbered row by row).                     */
+     * (a task of either role is the block of mk_stats.tiles_per_task
+     * adjacent tiles of one tile row; tasks are numbered row by row).      */
     MK_PART_STATIC_DETERMINISTIC = 2
 } mk_part_mode;
 
@@ -89,11 +89,12 @@ typedef enum {
  *              need not be multiples of the tile: edge tiles are masked.
  *              K == 0 gives C = sum of peers; M == 0 or N == 0 returns MK_OK
  *              without a launch.
- *   tile_m, tile_n   output tile (the unit of readiness flags, reduce tasks
- *              and chunks): one of 64x64, 128x128, 256x128.  A compute task
- *              produces a block of adjacent tiles of one tile row (two for
- *              128x128 and 256x128, one for 64x64; see mk_stats.tiles_per_task)
- *              and publishes each tile's flag.
+ *   tile_m, tile_n   output tile (the unit of readiness flags and chunks):
+ *              one of 64x64, 128x128, 256x128.  A compute task produces a
+ *              block of adjacent tiles of one tile row (two for 128x128 and
+ *              256x128, one for 64x64; see mk_stats.tiles_per_task) and
+ *              publishes each tile's flag; a reduce task takes the same block
+ *              once all its tiles are published.
  *   tiles_per_chunk  tiles per chunk (1..64; 4 in the method's
  *              GEMM+AllReduce).  Chunk c holds tiles [c*tpc, (c+1)*tpc) in
  *              row-major tile order; the last chunk may be short.
@@ -137,9 +138,12 @@ int mk_set_controller_floor(int floor);
 
 /*
  * mk_set_num_workgroups -- persistent workgroups per launch (B).  0 (default)
- * = one per compute unit (256 on MI355X).  Valid: 0 or 2..1024, and at most
- * the compute-unit count at launch time (one workgroup per CU is required for
- * every workgroup to be resident).
+ * = every workgroup that can be resident: the compute-unit count (256 on
+ * MI355X) times the workgroups one CU holds for the tile configuration (1 for
+ * every configuration, as the runtime's occupancy query confirms).
+ * Valid: 0 or 2..1024; at launch time B must not exceed that resident count
+ * (every workgroup of the persistent grid must run at once), else the launch
+ * fails with MK_ERR_INVALID_ARG.
  */
 int mk_set_num_workgroups(int num_wg);
 
@@ -180,7 +184,7 @@ typedef struct mk_stats {
     uint32_t chunks_released;     /* chunks whose last tile was reduced (== Ch)  */
     uint32_t invariant_violations;/* flag/counter mismatches seen on the device  */
     uint32_t ns_trace_len;        /* entries in the controller trace             */
-    uint32_t tiles_per_task;      /* output tiles one compute task produces      */
+    uint32_t tiles_per_task;      /* output tiles of one compute/reduce task     */
     uint64_t sum_cycles_compute;  /* shader-clock cycles over compute tasks      */
     uint64_t sum_cycles_reduce;   /* shader-clock cycles over reduce tasks       */
     uint64_t kernel_ticks_start;  /* first workgroup start (constant clock)      */

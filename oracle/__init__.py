@@ -277,13 +277,12 @@ def deterministic_owners(T: int, B: int, n_reduce: int, tiles_n: Optional[int] =
     """Owner maps of the deterministic static schedule.
 
     Workgroups [0, n_reduce) reduce and the rest compute (roles by workgroup
-    index).  Reducers take tiles round-robin in increasing tile order;
-    compute workgroups take compute tasks round-robin in increasing task
-    order, and every tile of a task has that task's owner.
+    index).  A task of either role covers the tiles of one compute task;
+    each workgroup takes its tasks round-robin in increasing task order, and
+    every tile of a task has that task's owner.
     """
-    t = np.arange(T, dtype=np.int64)
     task = compute_task_of_tile(T, tiles_n, tiles_per_task)
-    return n_reduce + task % (B - n_reduce), t % n_reduce
+    return n_reduce + task % (B - n_reduce), task % n_reduce
 
 
 OWNER_WG_MASK = 0xFFFF
@@ -336,11 +335,12 @@ def check_state(maps: Dict[str, np.ndarray], T: int, tiles_per_chunk: int, epoch
             bad.append(f"reduce_owner[{i}] = {int(ro_wg[i])}, expected {int(dr[i])}")
     if tiles_per_task > 1 and T:
         task = compute_task_of_tile(T, tiles_n, tiles_per_task)
-        first = np.zeros(int(task.max()) + 1, dtype=np.int64)
-        first[task[::-1]] = co[::-1]
-        if np.any(co != first[task]):
-            i = int(np.nonzero(co != first[task])[0][0])
-            bad.append(f"tile {i}: owner word differs from the rest of its compute task")
+        for name, own in (("compute", co), ("reduce", ro)):
+            first = np.zeros(int(task.max()) + 1, dtype=np.int64)
+            first[task[::-1]] = own[::-1]
+            if np.any(own != first[task]):
+                i = int(np.nonzero(own != first[task])[0][0])
+                bad.append(f"tile {i}: {name} owner differs from the rest of its task")
     if np.any(co_wg >= B):
         bad.append("compute owner outside [0, B)")
     if np.any(ro_wg >= B):
