@@ -73,6 +73,8 @@ class Stats(ctypes.Structure):
         ("reduce_ticks_start", ctypes.c_uint64),
         ("reduce_ticks_end", ctypes.c_uint64),
         ("timer_hz", ctypes.c_uint64),
+        ("xcd_local", ctypes.c_uint32),
+        ("keep_compute", ctypes.c_uint32),
     ]
 
 
@@ -247,10 +249,10 @@ def get_stats(maps: bool = False, raise_on_error: bool = True) -> Dict:
 
 def controller_eval(rows: np.ndarray) -> np.ndarray:
     """Runs the device controller step on each row (B, T, compute_done,
-    reduce_done, sum_cycles_compute, sum_cycles_reduce, current, floor)."""
+    reduce_done, sum_cycles_compute, sum_cycles_reduce, current, floor, keep)."""
     torch = _torch()
     rows = np.ascontiguousarray(rows, dtype=np.uint64)
-    assert rows.ndim == 2 and rows.shape[1] == 8
+    assert rows.ndim == 2 and rows.shape[1] == 9
     n = rows.shape[0]
     dev_in = torch.from_numpy(rows.view(np.int64)).cuda()
     dev_out = torch.zeros(n, dtype=torch.int32, device=dev_in.device)

@@ -7,6 +7,7 @@
 #include <mutex>
 #include <string>
 #include <cstring>
+#include <vector>
 #include <cstdio>
 
 #include "mk.h"
@@ -51,6 +52,7 @@ struct Launch {
     bool valid = false;
     uint32_t epoch = 0, calls = 0, nwg = 0, T = 0, Ch = 0, tpc = 0, tm = 0, tn = 0;
     uint32_t mode = 0, ns_init = 0;
+    uint32_t local = 0, keep = 1;
 };
 
 struct DevState {
@@ -64,6 +66,7 @@ struct DevState {
     uint32_t calls = 0;
     uint32_t shape_T = 0, shape_tpc = 0;
     bool dirty = false;
+    bool xcd_ok = false;   // workgroup w of a one-per-CU grid runs on XCD w mod 8
     Launch last;
 };
 DevState g_dev[kMaxDevices];
@@ -160,6 +163,28 @@ int current_device(int *dev) {
     return MK_OK;
 }
 
+// Whether workgroups are dealt to XCDs round-robin (workgroup w on XCD
+// w mod 8), read from each workgroup's XCC id register once per device.
+// Tiles are kept on one XCD only when this holds.
+int probe_xcd_mapping(DevState &d) {
+    d.xcd_ok = false;
+    if (d.num_cu <= 0 || d.num_cu % kMaxXcd != 0) return MK_OK;
+    uint32_t *buf = nullptr;
+    hipError_t e = hipMalloc((void **)&buf, sizeof(uint32_t) * (size_t)d.num_cu);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(xcd probe)");
+    std::vector<uint32_t> host((size_t)d.num_cu, 0xFFFFFFFFu);
+    e = launch_xcc_probe(buf, d.num_cu, nullptr);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipMemcpy(host.data(), buf, sizeof(uint32_t) * host.size(), hipMemcpyDeviceToHost);
+    const hipError_t ef = hipFree(buf);
+    if (e != hipSuccess) return hip_fail(e, "xcd probe");
+    if (ef != hipSuccess) return hip_fail(ef, "hipFree(xcd probe)");
+    bool ok = true;
+    for (int w = 0; w < d.num_cu; ++w) ok = ok && host[(size_t)w] == (uint32_t)(w % kMaxXcd);
+    d.xcd_ok = ok;
+    return MK_OK;
+}
+
 int device_state(DevState **out) {
     int dev = 0;
     int rc = current_device(&dev);
@@ -173,6 +198,8 @@ int device_state(DevState **out) {
         int khz = 0;
         if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0)
             d.timer_hz = (uint64_t)khz * 1000ull;
+        rc = probe_xcd_mapping(d);
+        if (rc) return rc;
         d.init = true;
     }
     *out = &d;
@@ -272,12 +299,23 @@ int run(bool fused, const void *A, const void *B, const float *peers, int num_pe
         return fail(MK_ERR_INVALID_ARG, "workgroups %d outside [2, %d resident workgroups]", nwg,
                     resident);
     int ns_init = set.n_reduce;
+    if (set.mode != MK_PART_ADAPTIVE && (ns_init < 1 || ns_init > nwg - 1))
+        return fail(MK_ERR_INVALID_ARG, "static reduce count %d outside [1, %d]", ns_init, nwg - 1);
+    // Keep every tile on the XCD of its partition (write-back hand-off in one
+    // L2) when the grid spans whole XCDs dealt round-robin, every partition
+    // holds tiles, and every XCD keeps both roles: the controller keeps one
+    // compute workgroup per XCD, and a static partition must give each XCD a
+    // reducer and a compute workgroup (8 <= n_reduce <= B - 8).  Otherwise
+    // tiles cross XCDs with write-through hand-off.
+    const int nxcd = xcd_partitions(nwg, d.num_cu);
+    const bool local = d.xcd_ok && nxcd == kMaxXcd && tiles_m >= nxcd &&
+                       set.mode != MK_PART_STATIC_DETERMINISTIC &&
+                       (set.mode == MK_PART_ADAPTIVE || (ns_init >= nxcd && ns_init <= nwg - nxcd));
+    const int keep = local ? nxcd : 1;
     if (set.mode == MK_PART_ADAPTIVE) {
         if (ns_init == 0) ns_init = 2;
-        if (ns_init > nwg - 1) ns_init = nwg - 1;
+        if (ns_init > nwg - keep) ns_init = nwg - keep;
         if (ns_init < 1) ns_init = 1;
-    } else if (ns_init < 1 || ns_init > nwg - 1) {
-        return fail(MK_ERR_INVALID_ARG, "static reduce count %d outside [1, %d]", ns_init, nwg - 1);
     }
 
     rc = ensure_workspace(d, T, Ch, s);
@@ -333,7 +371,9 @@ int run(bool fused, const void *A, const void *B, const float *peers, int num_pe
     a.ns_floor = set.floor;
     a.nwg = nwg;
     a.group_m = set.group_m;
-    a.nxcd = xcd_partitions(nwg, d.num_cu);
+    a.nxcd = nxcd;
+    a.local = local ? 1 : 0;
+    a.keep = keep;
     a.timeout_ticks = set.timeout_us * (d.timer_hz / 1000000ull);
     a.skip_publish = set.skip_publish;
     a.ws = v;
@@ -353,6 +393,8 @@ int run(bool fused, const void *A, const void *B, const float *peers, int num_pe
     d.last.tn = (uint32_t)tile_n;
     d.last.mode = (uint32_t)set.mode;
     d.last.ns_init = (uint32_t)ns_init;
+    d.last.local = local ? 1u : 0u;
+    d.last.keep = (uint32_t)keep;
     return MK_OK;
 }
 
@@ -470,6 +512,8 @@ int mk_get_stats(mk_stats *out, uint32_t *maps, size_t maps_len) {
     out->reduce_ticks_start = snap.r_start;
     out->reduce_ticks_end = snap.r_end;
     out->timer_hz = d.timer_hz;
+    out->xcd_local = l.local;
+    out->keep_compute = l.keep;
 
     if (maps) {
         uint32_t *p = maps;
@@ -484,6 +528,15 @@ int mk_get_stats(mk_stats *out, uint32_t *maps, size_t maps_len) {
             if (e != hipSuccess) return hip_fail(e, "hipMemcpy(maps)");
             p += pt.n;
         }
+    }
+    if (snap.error == kErrXcd) {
+        // a workgroup ran on another XCD than its index implies: the launch's
+        // hand-off assumption failed, so tiles no longer stay on one XCD
+        d.dirty = true;
+        d.xcd_ok = false;
+        out->status = MK_ERR_PROTOCOL;
+        fail(MK_ERR_PROTOCOL, "a workgroup ran on an unexpected XCD; result not valid");
+        return MK_ERR_PROTOCOL;
     }
     if (snap.error == kErrTimeout) {
         d.dirty = true;

@@ -15,7 +15,7 @@ constexpr int kTraceCap = 1024;
 constexpr int kMaxXcd = 8;            // XCDs on MI355X (tile partitions)
 
 enum Mode : int32_t { kAdaptive = 0, kStatic = 1, kDeterministic = 2 };
-enum Err : uint32_t { kErrNone = 0, kErrTimeout = 1 };
+enum Err : uint32_t { kErrNone = 0, kErrTimeout = 1, kErrXcd = 2 };
 
 // Per-launch control block in device memory.  The last workgroup to leave a
 // launch copies it into the snapshot and restores the initial values below,
@@ -28,7 +28,7 @@ constexpr uint64_t kCountMask = (1ull << kCountBits) - 1;
 
 struct alignas(256) Live {
     uint32_t compute_claim[kMaxXcd];  // next compute claim per partition (init 0)
-    uint32_t reduce_claim;     // next reduce ticket                 (init 0)
+    uint32_t reduce_claim[kMaxXcd];   // next reduce ticket per partition (init 0)
     uint32_t exit_count;       // workgroups that left               (init 0)
     uint32_t target_ns;        // controller target, 0 = unset       (init 0)
     uint32_t role_switches;    //                                    (init 0)
@@ -39,7 +39,7 @@ struct alignas(256) Live {
     uint32_t ns_max;           //                                    (init 0)
     uint32_t trace_len;        //                                    (init 0)
     uint32_t ns_final;         // written at exit                    (init 0)
-    uint32_t pad0[5];
+    uint32_t pad0[6];
     uint64_t role_compute;     // (cycles << kCountBits) | tasks     (init 0)
     uint64_t role_reduce;      //                                    (init 0)
     uint64_t t_start;          // min over workgroups                (init ~0)
@@ -83,6 +83,8 @@ struct FusedArgs {
     int32_t nwg;              // B
     int32_t group_m;          // tile-row band height of the claim order
     int32_t nxcd;             // tile partitions (XCDs) for the claim order
+    int32_t local;            // 1: every tile is computed and reduced on its partition's XCD
+    int32_t keep;             // compute workgroups the controller keeps while compute remains
     uint64_t timeout_ticks;   // bound on any wait, constant-clock ticks
     int64_t skip_publish;     // fault injection: tile whose flag is never set (-1 none)
     WsView ws;
@@ -114,6 +116,7 @@ hipError_t launch_reduce(const ReduceArgs &a, int num_cu, hipStream_t s);
 hipError_t launch_ws_init(Live *live, Live *snap, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t *p, uint32_t value, int64_t n, hipStream_t s);
 hipError_t launch_controller_eval(const uint64_t *in, uint32_t *out, int n, hipStream_t s);
+hipError_t launch_xcc_probe(uint32_t *out, int nwg, hipStream_t s);   // XCD of each workgroup
 bool tile_supported(int tile_m, int tile_n);
 int tiles_per_block(int tile_m, int tile_n);   // output tiles per compute task
 int workgroups_per_cu(int tile_m, int tile_n); // fused workgroups resident per CU

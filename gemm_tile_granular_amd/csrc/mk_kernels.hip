@@ -112,16 +112,18 @@ template <class T> __device__ __forceinline__ void max_relaxed(T *p, T v) {
 // the predicted finish times R_s C_s / n_s and R_p C_p / (B - n_s) are equal.
 // R_x = tasks of role x not finished, C_x = cumulative mean shader cycles per
 // finished task.  Unsigned 64-bit arithmetic, nearest rounding with ties up;
-// clamp to [min(floor, B-1), B-1] while compute remains; B once it is done.
+// clamp to [min(floor, B-keep), B-keep] while compute remains (keep compute
+// workgroups stay: 1, or one per XCD when every XCD works on its own tiles);
+// B once it is done.
 // Limits B <= 1024, T < 2^22 and C_x <= 2^26-1 keep every product exact.
 // ---------------------------------------------------------------------------
 __device__ uint32_t controller_update(uint32_t B, uint32_t T, uint32_t compute_done,
                                       uint32_t reduce_done, uint64_t sum_p, uint64_t sum_s,
-                                      uint32_t current, uint32_t floor) {
+                                      uint32_t current, uint32_t floor, uint32_t keep) {
     const uint32_t R_p = T - compute_done;
     const uint32_t R_s = T - reduce_done;
     if (R_p == 0) return B;
-    const uint32_t hi = B - 1;
+    const uint32_t hi = B - keep;
     const uint32_t lo = floor < hi ? floor : hi;
     uint64_t n;
     if (compute_done == 0 || reduce_done == 0) {
@@ -568,7 +570,7 @@ struct ReduceGroup {
 };
 
 // Region of TM rows x BW columns at (m0, n0): the tiles of one compute block.
-template <int TM, int BW, int NT, int PP>
+template <int TM, int BW, int NT, int PP, int kLoadPol, int kStorePol>
 __device__ __forceinline__ void reduce_tile_pp(const float *__restrict__ peers, float *__restrict__ C,
                                                int64_t M, int64_t N, int P, int64_t m0, int64_t n0) {
     using RG = ReduceGeom<TM, BW, NT>;
@@ -593,7 +595,7 @@ __device__ __forceinline__ void reduce_tile_pp(const float *__restrict__ peers, 
             for (int u = 0; u < U; ++u) {
                 const int r = (gi * U + u) * RG::RP + r0;
                 g.off[u] = ((int)col_ok & (int)(m0 + r < M)) ? (uint32_t)((r * N + cc) * 4) : kOOB;
-                g.v[0][u] = __builtin_amdgcn_raw_buffer_load_b128(rc, g.off[u], 0, kPolicyCoherentLoad);
+                g.v[0][u] = __builtin_amdgcn_raw_buffer_load_b128(rc, g.off[u], 0, kLoadPol);
             }
 #pragma unroll
             for (int q = 0; q < PP; ++q) {
@@ -610,7 +612,7 @@ __device__ __forceinline__ void reduce_tile_pp(const float *__restrict__ peers, 
                 f32x4 acc = g.v[0][u];
 #pragma unroll
                 for (int q = 0; q < PP; ++q) acc += g.v[q + 1][u];
-                __builtin_amdgcn_raw_buffer_store_b128(acc, rc, g.off[u], 0, kPolicyCoherentStream);
+                __builtin_amdgcn_raw_buffer_store_b128(acc, rc, g.off[u], 0, kStorePol);
             }
         };
         ReduceGroup<PP, U> g0, g1;
@@ -634,7 +636,7 @@ __device__ __forceinline__ void reduce_tile_pp(const float *__restrict__ peers, 
             for (int u = 0; u < U; ++u) {
                 const int r = (gi * U + u) * RG::RP + r0;
                 off[u] = ((int)col_ok & (int)(m0 + r < M)) ? (uint32_t)((r * N + cc) * 4) : kOOB;
-                acc[u] = __builtin_amdgcn_raw_buffer_load_b128(rc, off[u], 0, kPolicyCoherentLoad);
+                acc[u] = __builtin_amdgcn_raw_buffer_load_b128(rc, off[u], 0, kLoadPol);
             }
             int p = 0;
             for (; p + PB <= P; p += PB) {
@@ -659,25 +661,22 @@ __device__ __forceinline__ void reduce_tile_pp(const float *__restrict__ peers, 
             }
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                __builtin_amdgcn_raw_buffer_store_b128(acc[u], rc, off[u], 0, kPolicyCoherentStream);
+                __builtin_amdgcn_raw_buffer_store_b128(acc[u], rc, off[u], 0, kStorePol);
         }
     }
 }
 
-// Dispatch on the peer count so that every load of a pass group is a
-// straight-line instruction (counts above 16 take the blocked loop).
-template <int TM, int BW, int NT>
+// Dispatch on the peer count: the R-1 of 2, 4, 8 and 16 ranks get straight-line
+// pipelined code; other counts take the blocked loop.
+template <int TM, int BW, int NT, int kLoadPol, int kStorePol>
 __device__ __forceinline__ void reduce_tile(const float *__restrict__ peers, float *__restrict__ C,
                                             int64_t M, int64_t N, int P, int64_t m0, int64_t n0) {
     switch (P) {
 #define MK_REDUCE_CASE(k) \
-    case k: reduce_tile_pp<TM, BW, NT, k>(peers, C, M, N, P, m0, n0); break;
-        MK_REDUCE_CASE(1) MK_REDUCE_CASE(2) MK_REDUCE_CASE(3) MK_REDUCE_CASE(4)
-        MK_REDUCE_CASE(5) MK_REDUCE_CASE(6) MK_REDUCE_CASE(7) MK_REDUCE_CASE(8)
-        MK_REDUCE_CASE(9) MK_REDUCE_CASE(10) MK_REDUCE_CASE(11) MK_REDUCE_CASE(12)
-        MK_REDUCE_CASE(13) MK_REDUCE_CASE(14) MK_REDUCE_CASE(15) MK_REDUCE_CASE(16)
+    case k: reduce_tile_pp<TM, BW, NT, k, kLoadPol, kStorePol>(peers, C, M, N, P, m0, n0); break;
+        MK_REDUCE_CASE(1) MK_REDUCE_CASE(3) MK_REDUCE_CASE(7) MK_REDUCE_CASE(15)
 #undef MK_REDUCE_CASE
-        default: reduce_tile_pp<TM, BW, NT, 0>(peers, C, M, N, P, m0, n0); break;
+        default: reduce_tile_pp<TM, BW, NT, 0, kLoadPol, kStorePol>(peers, C, M, N, P, m0, n0); break;
     }
 }
 
@@ -812,8 +811,9 @@ __device__ Decision next_task(const FusedArgs &a, const Parts &pt, const Blocks 
             s.pending_role = kRoleNone;
             const bool seen = s.early_flag && s.early_flag_value == a.epoch;
             s.early_flag = false;
-            if (q < bk.TB) {
-                const uint32_t b = pt.ticket(q);
+            const uint32_t home = wg % pt.nx;
+            if (a.local ? q < pt.size(home) : q < bk.TB) {
+                const uint32_t b = a.local ? pt.tile(home, q) : pt.ticket(q);
                 if (!seen && !wait_block(a, bk, L, b)) return {kRoleExit, 0, ns_seen};
                 return {kRoleReduce, b, ns_seen};
             }
@@ -823,9 +823,11 @@ __device__ Decision next_task(const FusedArgs &a, const Parts &pt, const Blocks 
         const uint32_t ns = s.target;
         const bool compute_role = wg >= ns;
         if (compute_role && !s.compute_exhausted) {
-            // own XCD's partition first, then the others
+            // own XCD's partition first, then (unless tiles stay on their
+            // XCD) the others
             const uint32_t home = wg % pt.nx;
-            for (uint32_t k = 0; k < pt.nx; ++k) {
+            const uint32_t parts = a.local ? 1u : pt.nx;
+            for (uint32_t k = 0; k < parts; ++k) {
                 const uint32_t x = home + k < pt.nx ? home + k : home + k - pt.nx;
                 if (s.parts_done & (1u << x)) continue;
                 const uint32_t i = add_relaxed(&L->compute_claim[x], 1u);
@@ -841,7 +843,7 @@ __device__ Decision next_task(const FusedArgs &a, const Parts &pt, const Blocks 
         // adaptive: a compute-role workgroup with no compute left reduces, as
         // every workgroup does once the controller's target reaches B
         s.pending_role = kRoleReduce;
-        s.pending_q = add_relaxed(&L->reduce_claim, 1u);
+        s.pending_q = add_relaxed(&L->reduce_claim[a.local ? wg % pt.nx : 0u], 1u);
         s.pending_ns = compute_role ? B : ns;
     }
 }
@@ -850,8 +852,8 @@ __device__ Decision next_task(const FusedArgs &a, const Parts &pt, const Blocks 
 // after it now, so its round trip overlaps this task (the result is read at
 // the next boundary), while the target still gives this workgroup the reduce
 // role.
-__device__ __forceinline__ void prefetch_claim(const FusedArgs &a, Live *L, uint32_t wg, Sched &s,
-                                               const Decision &d) {
+__device__ __forceinline__ void prefetch_claim(const FusedArgs &a, const Parts &pt, Live *L,
+                                               uint32_t wg, Sched &s, const Decision &d) {
     if (a.mode == kDeterministic || s.pending_role != kRoleNone) return;
     const uint32_t ns = s.target;
     const bool compute_role = wg >= ns;
@@ -861,42 +863,68 @@ __device__ __forceinline__ void prefetch_claim(const FusedArgs &a, Live *L, uint
     if (d.role == kRoleReduce && !s.reduce_exhausted &&
                (!compute_role || (a.mode == kAdaptive && s.compute_exhausted))) {
         s.pending_role = kRoleReduce;
-        s.pending_q = add_relaxed(&L->reduce_claim, 1u);
+        s.pending_q = add_relaxed(&L->reduce_claim[a.local ? wg % pt.nx : 0u], 1u);
         s.pending_ns = compute_role ? (uint32_t)a.nwg : ns;
     }
 }
 
-// Thread 0, at the end of a task and before its stores drain: start the
-// round trips the next boundary needs, so they overlap the drain.  A compute
-// workgroup that is still in the compute role claims its next block; a
-// reducer holding a ticket reads that tile's readiness flag.
-__device__ __forceinline__ void early_next(const FusedArgs &a, const Parts &pt, const Blocks &bk,
-                                           Live *L, uint32_t wg, Sched &s) {
-    if (a.mode == kDeterministic) return;
+// Round trips started as a task's work completes and read back after its
+// stores are issued (kept in registers meanwhile, not in the LDS-resident
+// scheduling state, so issuing them does not wait for their return).
+struct Early {
+    int kind;           // 0: none, 1: compute claim on partition x, 2: readiness flags
+    uint32_t x, ns;
+    uint32_t v0, v1;
+};
+
+// Thread 0: start the round trips the next boundary needs.  A compute
+// workgroup still in the compute role (under the target of its previous
+// controller step) claims its next block; a reducer holding a ticket reads
+// that block's readiness flags.
+__device__ __forceinline__ Early early_issue(const FusedArgs &a, const Parts &pt, const Blocks &bk,
+                                             Live *L, uint32_t wg, const Sched &s) {
+    Early e;
+    e.kind = 0;
+    e.x = e.ns = e.v0 = e.v1 = 0;
+    if (a.mode == kDeterministic) return e;
+    const uint32_t home = wg % pt.nx;
     if (s.pending_role == kRoleReduce) {
-        if (s.pending_q < bk.TB) {
+        if (a.local ? s.pending_q < pt.size(home) : s.pending_q < bk.TB) {
             // the block is ready when its first and last tiles are
-            const uint32_t b = pt.ticket(s.pending_q);
+            const uint32_t b = a.local ? pt.tile(home, s.pending_q) : pt.ticket(s.pending_q);
             const uint32_t t0 = bk.first_tile(b), t1 = t0 + bk.count(b) - 1;
-            const uint32_t f0 = ld_relaxed(&a.ws.tile_flag[t0]);
-            const uint32_t f1 = ld_relaxed(&a.ws.tile_flag[t1]);
-            s.early_flag = true;
-            s.early_flag_value = f0 == f1 ? f0 : 0u;
+            e.kind = 2;
+            e.v0 = ld_relaxed(&a.ws.tile_flag[t0]);
+            e.v1 = ld_relaxed(&a.ws.tile_flag[t1]);
         }
-        return;
+        return e;
     }
     const uint32_t ns = s.target;
     if (wg >= ns && !s.compute_exhausted) {
-        const uint32_t home = wg % pt.nx;
-        for (uint32_t k = 0; k < pt.nx; ++k) {
+        const uint32_t parts = a.local ? 1u : pt.nx;
+        for (uint32_t k = 0; k < parts; ++k) {
             const uint32_t x = home + k < pt.nx ? home + k : home + k - pt.nx;
             if (s.parts_done & (1u << x)) continue;
-            s.early_claim = true;
-            s.early_x = x;
-            s.early_ns = ns;
-            s.early_i = add_relaxed(&L->compute_claim[x], 1u);
-            return;
+            e.kind = 1;
+            e.x = x;
+            e.ns = ns;
+            e.v0 = add_relaxed(&L->compute_claim[x], 1u);
+            return e;
         }
+    }
+    return e;
+}
+
+// Thread 0: record what early_issue brought back.
+__device__ __forceinline__ void early_finish(Sched &s, const Early &e) {
+    if (e.kind == 1) {
+        s.early_claim = true;
+        s.early_x = e.x;
+        s.early_ns = e.ns;
+        s.early_i = e.v0;
+    } else if (e.kind == 2) {
+        s.early_flag = true;
+        s.early_flag_value = e.v0 == e.v1 ? e.v0 : 0u;
     }
 }
 
@@ -908,7 +936,7 @@ __device__ uint32_t controller_step(const FusedArgs &a, Live *L, uint64_t comput
     const uint32_t n = controller_update(
         (uint32_t)a.nwg, a.T, (uint32_t)(compute_word & kCountMask),
         (uint32_t)(reduce_word & kCountMask), compute_word >> kCountBits,
-        reduce_word >> kCountBits, cur, (uint32_t)a.ns_floor);
+        reduce_word >> kCountBits, cur, (uint32_t)a.ns_floor, (uint32_t)a.keep);
     if (n != cur || raw_target == 0) {
         st_relaxed(&L->target_ns, n);
         min_relaxed(&L->ns_min, n);
@@ -931,7 +959,7 @@ __device__ void finish_launch(const FusedArgs &a, Live *L) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const uint32_t raw = ld_relaxed(&L->target_ns);
     for (int x = 0; x < kMaxXcd; ++x) S->compute_claim[x] = ld_relaxed(&L->compute_claim[x]);
-    S->reduce_claim = ld_relaxed(&L->reduce_claim);
+    for (int x = 0; x < kMaxXcd; ++x) S->reduce_claim[x] = ld_relaxed(&L->reduce_claim[x]);
     S->exit_count = ld_relaxed(&L->exit_count);
     S->target_ns = raw;
     S->role_switches = ld_relaxed(&L->role_switches);
@@ -950,7 +978,7 @@ __device__ void finish_launch(const FusedArgs &a, Live *L) {
     S->r_end = ld_relaxed(&L->r_end);
 
     for (int x = 0; x < kMaxXcd; ++x) st_relaxed(&L->compute_claim[x], 0u);
-    st_relaxed(&L->reduce_claim, 0u);
+    for (int x = 0; x < kMaxXcd; ++x) st_relaxed(&L->reduce_claim[x], 0u);
     st_relaxed(&L->target_ns, 0u);
     st_relaxed(&L->role_switches, 0u);
     st_relaxed(&L->chunks_released, 0u);
@@ -1055,21 +1083,34 @@ __device__ __forceinline__ void cnt_finish(const FusedArgs &a, Live *L, const Cn
     }
 }
 
+// Cache policies of the tile hand-off.  When every tile is computed and
+// reduced on one XCD (LOCAL), producer and consumer share that XCD's L2: the
+// partial is stored write-back and read past the reader's L1 (sc0).  Across
+// XCDs, whose L2s are not coherent with each other, the partial is written
+// through (sc1) and read at device scope (sc1).  The reduced tile is streamed
+// out (nt).
+template <bool LOCAL> struct HandOff {
+    static constexpr int kPartialStore = LOCAL ? kPolicyDefault : kPolicyCoherentStore;
+    static constexpr int kPartialLoad = LOCAL ? 1 : kPolicyCoherentLoad;
+    static constexpr int kResultStore = LOCAL ? kPolicyStream : kPolicyCoherentStream;
+};
+
 // static LDS of the fused kernel: at least the GEMM ring, and more than
 // 160 KiB / (WPC + 1), so exactly WPC workgroups fit on a CU
 template <int TM, int TN>
 constexpr int fused_lds_bytes() {
-    using G = GemmFor<TM, TN, kPolicyCoherentStore>;
+    using G = GemmFor<TM, TN, kPolicyDefault>;
     constexpr int floor_bytes = (160 * 1024) / (TileCfg<TM, TN>::WPC + 1) + 1024;
     return G::LDS_BYTES > floor_bytes ? G::LDS_BYTES : floor_bytes;
 }
 
-template <int TM, int TN>
-__global__ __launch_bounds__((GemmFor<TM, TN, kPolicyCoherentStore>::NT),
-                             (TileCfg<TM, TN>::WPC * GemmFor<TM, TN, kPolicyCoherentStore>::NWAVES / 4))
+template <int TM, int TN, bool LOCAL>
+__global__ __launch_bounds__((GemmFor<TM, TN, kPolicyDefault>::NT),
+                             (TileCfg<TM, TN>::WPC * GemmFor<TM, TN, kPolicyDefault>::NWAVES / 4))
 void fused_gemm_reduce_kernel(
     FusedArgs a) {
-    using G = GemmFor<TM, TN, kPolicyCoherentStore>;
+    using H = HandOff<LOCAL>;
+    using G = GemmFor<TM, TN, H::kPartialStore>;
     __shared__ __attribute__((aligned(1024))) char lds_raw[fused_lds_bytes<TM, TN>()];
     __shared__ Decision sh_dec;
     // thread 0's scheduling state lives in LDS, not in registers every lane
@@ -1090,6 +1131,15 @@ void fused_gemm_reduce_kernel(
     const Parts pt = make_parts((uint32_t)a.nxcd, (uint32_t)a.tiles_m, bk.bn, chunk_blocks(a.tpc, TPB),
                                 (uint32_t)a.group_m);
     Sched &s = sh_sched;
+    if (LOCAL && tid == 0) {
+        // tiles stay on their XCD only if this workgroup runs where its index
+        // says (workgroup w on XCD w mod 8); otherwise stop everything
+        uint32_t xcc;
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+        if ((xcc & 0xFu) != wg % (uint32_t)a.nxcd)
+            __hip_atomic_fetch_max(&L->error, (uint32_t)kErrXcd, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    }
     if (tid == 0) {
         s.det_i = 0;
         s.last_role = kRoleNone;
@@ -1109,10 +1159,11 @@ void fused_gemm_reduce_kernel(
         min_relaxed(&L->t_start, ticks_now());
     }
 
-    // At the end of every task thread 0 records it in its role word and runs
-    // one controller step on fresh values, so the role of the next task is
-    // decided on current progress; the round trips of these atomics overlap
-    // the task's store drain.  The counters of a reduced tile wait for the end
+    // As every task's work completes, thread 0 records it in its role word,
+    // reads the controller inputs and claims its next task (under the target
+    // of its previous controller step), all at once; the round trips overlap
+    // the task's stores, and the controller step that follows sets the role
+    // for the task after.  The counters of a reduced tile wait for the end
     // of the workgroup's next task (see CntRead).
     __shared__ uint32_t sh_pend_t0, sh_pend_n;   // reduced tiles whose counters are pending
     if (tid == 0) sh_pend_n = 0;
@@ -1121,7 +1172,7 @@ void fused_gemm_reduce_kernel(
             s.decide_t0 = ticks_now();
             const Decision d = next_task(a, pt, bk, L, wg, s);
             s.decide_t1 = ticks_now();
-            if (d.role == kRoleReduce) prefetch_claim(a, L, wg, s, d);
+            if (d.role == kRoleReduce) prefetch_claim(a, pt, L, wg, s, d);
             sh_dec = d;
             sh_c0 = cycles_now();
             sh_r0 = ticks_now();
@@ -1142,12 +1193,14 @@ void fused_gemm_reduce_kernel(
 
         CtlRead ctl;
         CntRead cnt;
+        Early early;
         // progress is counted in tiles for both roles, so the controller's
         // R_p C_p is the same remaining time whatever the block size
         auto work_done = [&](int role) {
             if (tid == 0) {
                 cnt = cnt_issue(a, sh_pend_t0, sh_pend_n);
                 ctl = ctl_issue(a, L, role, nt, cycles_now() - sh_c0, sh_r0, ticks_now());
+                early = early_issue(a, pt, bk, L, wg, s);
             }
         };
         if (d.role == kRoleCompute) {
@@ -1157,14 +1210,14 @@ void fused_gemm_reduce_kernel(
             // thread 0 saw the flag before the barrier; the partial is read
             // with device-coherent loads, after it
             if (a.P > 0)
-                reduce_tile<TM, TPB * TN, G::NT>(a.peers, a.C, a.M, a.N, a.P, (int64_t)ti * TM,
-                                                 (int64_t)tj * TN);
+                reduce_tile<TM, TPB * TN, G::NT, H::kPartialLoad, H::kResultStore>(
+                    a.peers, a.C, a.M, a.N, a.P, (int64_t)ti * TM, (int64_t)tj * TN);
             work_done(kRoleReduce);
         }
         if (tid == 0) {
             cnt_finish(a, L, cnt);
             ctl_finish(a, L, d.role, ctl, s);
-            early_next(a, pt, bk, L, wg, s);
+            early_finish(s, early);
         }
         // payload before flag ("【学习】mKernel 分析" section 2.5): every wave's
         // device-coherent tile stores have completed before thread 0
@@ -1278,7 +1331,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
 
 __device__ void live_init(Live *L) {
     for (int x = 0; x < kMaxXcd; ++x) L->compute_claim[x] = 0;
-    L->reduce_claim = 0;
+    for (int x = 0; x < kMaxXcd; ++x) L->reduce_claim[x] = 0;
     L->exit_count = 0;
     L->target_ns = 0;
     L->role_switches = 0;
@@ -1310,12 +1363,20 @@ __global__ void fill_u32_kernel(uint32_t *p, uint32_t v, int64_t n) {
         p[i] = v;
 }
 
+// XCD of every workgroup of a one-per-CU grid (the launch asks for more
+// than half a CU's LDS, which forces one per CU, as in the fused kernel)
+__global__ __launch_bounds__(64) void xcc_probe_kernel(uint32_t *out) {
+    uint32_t xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    if (threadIdx.x == 0) out[blockIdx.x] = xcc & 0xFu;
+}
+
 __global__ void controller_eval_kernel(const uint64_t *in, uint32_t *out, int n) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    const uint64_t *r = in + 8 * (int64_t)i;
+    const uint64_t *r = in + 9 * (int64_t)i;
     out[i] = controller_update((uint32_t)r[0], (uint32_t)r[1], (uint32_t)r[2], (uint32_t)r[3], r[4],
-                               r[5], (uint32_t)r[6], (uint32_t)r[7]);
+                               r[5], (uint32_t)r[6], (uint32_t)r[7], (uint32_t)r[8]);
 }
 
 // ---------------------------------------------------------------------------
@@ -1329,8 +1390,8 @@ template <int TM, int TN>
 static int fused_residency() {
     int blocks = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &blocks, reinterpret_cast<const void *>(&fused_gemm_reduce_kernel<TM, TN>),
-            GemmFor<TM, TN, kPolicyCoherentStore>::NT, 0) != hipSuccess)
+            &blocks, reinterpret_cast<const void *>(&fused_gemm_reduce_kernel<TM, TN, true>),
+            GemmFor<TM, TN, kPolicyDefault>::NT, 0) != hipSuccess)
         return 0;
     return blocks < TileCfg<TM, TN>::WPC ? blocks : TileCfg<TM, TN>::WPC;
 }
@@ -1355,8 +1416,12 @@ bool tile_supported(int tm, int tn) {
 
 template <int TM, int TN>
 static hipError_t launch_fused_t(const FusedArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL((fused_gemm_reduce_kernel<TM, TN>), dim3(a.nwg),
-                       dim3(GemmFor<TM, TN, kPolicyCoherentStore>::NT), 0, s, a);
+    if (a.local)
+        hipLaunchKernelGGL((fused_gemm_reduce_kernel<TM, TN, true>), dim3(a.nwg),
+                           dim3(GemmFor<TM, TN, kPolicyDefault>::NT), 0, s, a);
+    else
+        hipLaunchKernelGGL((fused_gemm_reduce_kernel<TM, TN, false>), dim3(a.nwg),
+                           dim3(GemmFor<TM, TN, kPolicyDefault>::NT), 0, s, a);
     return hipGetLastError();
 }
 
@@ -1404,6 +1469,11 @@ hipError_t launch_fill_u32(uint32_t *p, uint32_t v, int64_t n, hipStream_t s) {
     int64_t blocks = (n + 255) / 256;
     if (blocks > 1024) blocks = 1024;
     hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, v, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_xcc_probe(uint32_t *out, int nwg, hipStream_t s) {
+    hipLaunchKernelGGL(xcc_probe_kernel, dim3(nwg), dim3(64), 96 * 1024, s, out);
     return hipGetLastError();
 }
 

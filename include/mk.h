@@ -192,6 +192,8 @@ typedef struct mk_stats {
     uint64_t reduce_ticks_start;  /* first reduce task start                     */
     uint64_t reduce_ticks_end;    /* last reduce task end                        */
     uint64_t timer_hz;            /* constant clock frequency                    */
+    uint32_t xcd_local;           /* 1: every tile stayed on its partition's XCD */
+    uint32_t keep_compute;        /* compute workgroups the controller kept      */
 } mk_stats;
 
 /* Words per map in the optional `maps` output of mk_get_stats, in order:
@@ -219,11 +221,13 @@ int mk_get_stats(mk_stats *out, uint32_t *maps, size_t maps_len);
 
 /*
  * mk_controller_eval -- evaluates the device's controller step on a table,
- * for parity tests against the host closed form.  `in` holds n rows of eight
+ * for parity tests against the host closed form.  `in` holds n rows of nine
  * uint64 (device memory): B, T, compute_done, reduce_done,
- * sum_cycles_compute, sum_cycles_reduce, current_target, floor.  `out`
- * (device, n uint32) receives the new target for each row.  Limits: B in
- * [2, 1024], T < 2^22.  Asynchronous on `stream`.
+ * sum_cycles_compute, sum_cycles_reduce, current_target, floor, keep (compute
+ * workgroups the clamp keeps while compute remains: 1, or one per XCD when
+ * tiles stay on their XCD).  `out` (device, n uint32) receives the new target
+ * for each row.  Limits: B in [2, 1024], T < 2^22, 1 <= keep < B.
+ * Asynchronous on `stream`.
  */
 int mk_controller_eval(const uint64_t *in, uint32_t *out, int n, void *stream);
 

@@ -173,7 +173,7 @@ COST_CAP = (1 << 26) - 1     # per-task cycle means saturate here (keeps the u64
 
 
 def controller_target(B: int, R_s: int, C_s: int, R_p: int, C_p: int,
-                      current: int, floor: int = 2) -> int:
+                      current: int, floor: int = 2, keep: int = 1) -> int:
     """Target reduce-workgroup count n_s*.
 
     Readings of the page's undefined symbols (applied here and on the GPU):
@@ -183,16 +183,19 @@ def controller_target(B: int, R_s: int, C_s: int, R_p: int, C_p: int,
     n_s* = B R_s C_s / (R_p C_p + R_s C_s) is the n at which the two roles'
     predicted finish times R_s C_s / n and R_p C_p / (B - n) are equal.
     Rounding: nearest, ties up, in unsigned 64-bit integers.
-    Clamp: while compute remains (R_p > 0) keep at least one compute
-    workgroup (n <= B-1) and at least `floor` reducers (2, the low end of the
-    page's static sweep); with no compute left the formula itself gives B.
+    Clamp: while compute remains (R_p > 0) keep at least `keep` compute
+    workgroups (n <= B - keep; one, or one per tile partition when every
+    partition is worked only by its own XCD's workgroups -- otherwise a
+    partition could be left without a producer) and at least `floor` reducers
+    (2, the low end of the page's static sweep); with no compute left the
+    formula itself gives B.
     A zero denominator carries no information: the current target stays.
     """
     if B < 2:
         raise ValueError("need at least two workgroups")
     if R_p == 0:
         return B
-    hi = B - 1
+    hi = B - keep
     lo = min(floor, hi)
     num = B * R_s * C_s
     den = R_p * C_p + R_s * C_s
@@ -212,7 +215,7 @@ def cycle_mean(total_cycles: int, tasks: int) -> int:
 
 def controller_update(B: int, T: int, compute_done: int, reduce_done: int,
                       sum_cycles_compute: int, sum_cycles_reduce: int,
-                      current: int, floor: int = 2) -> int:
+                      current: int, floor: int = 2, keep: int = 1) -> int:
     """One controller step from the progress counters.
 
     R_p counts compute tasks not yet finished (claimed-but-running tasks count
@@ -225,11 +228,11 @@ def controller_update(B: int, T: int, compute_done: int, reduce_done: int,
     if R_p == 0:
         return B
     if compute_done == 0 or reduce_done == 0:
-        hi = B - 1
+        hi = B - keep
         return min(max(current, min(floor, hi)), hi)
     C_p = cycle_mean(sum_cycles_compute, compute_done)
     C_s = cycle_mean(sum_cycles_reduce, reduce_done)
-    return controller_target(B, R_s, C_s, R_p, C_p, current, floor)
+    return controller_target(B, R_s, C_s, R_p, C_p, current, floor, keep)
 
 
 def controller_exact(B: int, R_s: int, C_s: int, R_p: int, C_p: int) -> Fraction:

@@ -64,7 +64,7 @@ def test_stats_struct_matches_header(mk):
     got = [(n, t) for n, t in mk.Stats._fields_]
     assert [n for n, _ in got] == [n for n, _ in fields]
     assert all(t == want[c] for (_, t), (_, c) in zip(got, fields))
-    assert ctypes.sizeof(mk.Stats) == 144
+    assert ctypes.sizeof(mk.Stats) == 152
 
 
 def test_abi_version_and_trace_cap(mk):

@@ -175,17 +175,19 @@ def test_controller_device_matches_host_closed_form(mk):
         ss = int(rng.integers(0, 1 << 40)) if rd else 0
         cur = int(rng.integers(1, B + 1))
         fl = int(rng.integers(1, 70))
-        rows.append((B, T, cd, rd, sp, ss, cur, fl))
+        kp = int(rng.choice([1, 8])) if B > 8 else 1
+        rows.append((B, T, cd, rd, sp, ss, cur, fl, kp))
     # the hand-worked table, expressed as progress counters with exact means
     with open(os.path.join(os.path.dirname(__file__), "golden", "controller_table.json")) as f:
         g = json.load(f)
     for B, R_s, C_s, R_p, C_p, _, _ in g["rows"]:
         T = max(R_s, R_p) + 5
-        rows.append((B, T, T - R_p, T - R_s, (T - R_p) * C_p, (T - R_s) * C_s, 7 if B > 7 else 1, 2))
+        rows.append((B, T, T - R_p, T - R_s, (T - R_p) * C_p, (T - R_s) * C_s, 7 if B > 7 else 1, 2, 1))
     table = np.array(rows, dtype=np.uint64)
     got = mk.controller_eval(table)
     want = np.array([oracle.controller_update(*[int(x) for x in r[:6]], current=int(r[6]),
-                                              floor=int(r[7])) for r in rows], dtype=np.uint32)
+                                              floor=int(r[7]), keep=int(r[8])) for r in rows],
+                    dtype=np.uint32)
     mism = np.nonzero(got != want)[0]
     assert mism.size == 0, [(rows[i], int(got[i]), int(want[i])) for i in mism[:5]]
 

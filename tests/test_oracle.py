@@ -217,6 +217,17 @@ def test_controller_monotone_in_reduce_cost(B, R_s, C_s, R_p, C_p):
     assert n2 >= n1 >= n3
 
 
+def test_controller_keeps_one_compute_workgroup_per_partition():
+    # R_s C_s dominates: the formula asks for ~B, the clamp keeps `keep` computing
+    assert oracle.controller_target(256, 1000, 10 ** 6, 10, 1, current=2) == 255
+    assert oracle.controller_target(256, 1000, 10 ** 6, 10, 1, current=2, keep=8) == 248
+    # the clamp does not apply once compute is done (the drain target is B)
+    assert oracle.controller_target(256, 1000, 5, 0, 5, current=2, keep=8) == 256
+    # and a balanced case is unaffected: 256 * 1/2 = 128
+    assert oracle.controller_target(256, 100, 100, 100, 100, current=2, keep=8) == 128
+    assert oracle.controller_update(256, 100, 0, 0, 0, 0, current=300, keep=8) == 248
+
+
 def test_controller_update_keeps_target_without_samples():
     assert oracle.controller_update(256, 100, 0, 0, 0, 0, current=9) == 9
     assert oracle.controller_update(256, 100, 5, 0, 500, 0, current=9) == 9
