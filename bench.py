@@ -186,7 +186,23 @@ def main():
 
     mk.set_partition("adaptive", 0)
     ms_fused, wall_fused = time_leg(fused, args.steps, args.warmup, flush, stream, torch)
-    st = mk.get_stats()
+    st = mk.get_stats(maps=True)
+    # phase windows of the last timed launch, from the device's constant clock
+    kernel_us = (st["kernel_ticks_end"] - st["kernel_ticks_start"]) / st["timer_hz"] * 1e6
+    compute_us = float(np.max(st["compute_end_us"])) if len(st["compute_end_us"]) else 0.0
+    reduce_us = (st["reduce_ticks_end"] - st["reduce_ticks_start"]) / st["timer_hz"] * 1e6
+    reduce_bytes = 4.0 * w.M * w.N * (w.peers + 2)
+    phases = {
+        "kernel_us": kernel_us,
+        "compute_window_us": compute_us,
+        "gemm_tflops_in_compute_window": w.flops / (compute_us * 1e-6) / 1e12 if compute_us else None,
+        "reduce_window_us": reduce_us,
+        "reduce_GBps_in_reduce_window": reduce_bytes / (reduce_us * 1e-6) / 1e9 if reduce_us > 0 else None,
+        "reduce_bytes": reduce_bytes,
+        "xcd_local": st["xcd_local"],
+        "n_reduce_initial": st["n_reduce_initial"],
+        "n_reduce_range": [st["n_reduce_min_seen"], st["n_reduce_max_seen"]],
+    }
     print(f"[bench] fused adaptive: {summary(ms_fused)} (n_reduce final {st['n_reduce_final']}, "
           f"range {st['n_reduce_min_seen']}-{st['n_reduce_max_seen']})", file=sys.stderr, flush=True)
 
@@ -259,7 +275,8 @@ def main():
     roof["traffic_note"] = traffic_note
     roof["algorithmic_bytes"] = w.algorithmic_bytes
     roof["algorithmic_flops"] = w.flops
-    roof["kernel"] = f"mk::fused_gemm_reduce_kernel<{w.tile_m}, {w.tile_n}>"
+    roof["kernel"] = (f"mk::fused_gemm_reduce_kernel<{w.tile_m}, {w.tile_n}, "
+                      f"{'true' if st['xcd_local'] else 'false'}>")
     roof["max_roofline_frac"] = max(t_mfma, t_hbm) / sec
 
     result = {
@@ -283,6 +300,7 @@ def main():
         "hbm_GBps_algorithmic": gbps,
         "wall_s_fused_leg": wall_fused,
         "n_reduce_final": st["n_reduce_final"],
+        "fused_phases": phases,
         **out_extra,
     }
     if not args.no_cpu and not args.fused_only:
