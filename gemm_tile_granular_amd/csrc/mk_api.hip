@@ -500,13 +500,13 @@ int mk_get_stats(mk_stats *out, uint32_t *maps, size_t maps_len) {
     out->n_reduce_min_seen = snap.ns_min < l.ns_init ? snap.ns_min : l.ns_init;
     out->n_reduce_max_seen = snap.ns_max > l.ns_init ? snap.ns_max : l.ns_init;
     out->role_switches = snap.role_switches;
-    out->compute_tasks = (uint32_t)(snap.role_compute & kCountMask);
-    out->reduce_tasks = (uint32_t)(snap.role_reduce & kCountMask);
-    out->chunks_released = snap.chunks_released;
+    out->compute_tasks = (uint32_t)(snap.role_compute.v & kCountMask);
+    out->reduce_tasks = (uint32_t)(snap.role_reduce.v & kCountMask);
+    out->chunks_released = snap.chunks_released.v;
     out->invariant_violations = snap.violations;
     out->ns_trace_len = snap.trace_len < (uint32_t)kTraceCap ? snap.trace_len : (uint32_t)kTraceCap;
-    out->sum_cycles_compute = snap.role_compute >> kCountBits;
-    out->sum_cycles_reduce = snap.role_reduce >> kCountBits;
+    out->sum_cycles_compute = snap.role_compute.v >> kCountBits;
+    out->sum_cycles_reduce = snap.role_reduce.v >> kCountBits;
     out->kernel_ticks_start = snap.t_start;
     out->kernel_ticks_end = snap.t_end;
     out->reduce_ticks_start = snap.r_start;

@@ -26,26 +26,32 @@ enum Err : uint32_t { kErrNone = 0, kErrTimeout = 1, kErrXcd = 2 };
 constexpr int kCountBits = 22;
 constexpr uint64_t kCountMask = (1ull << kCountBits) - 1;
 
+// A counter on a 256-byte line of its own.  Every workgroup hits the claim
+// counters, the role words and the target once per task; kept apart they do
+// not serialise behind each other's atomics.
+template <class T> struct alignas(256) Line {
+    T v;
+};
+
 struct alignas(256) Live {
-    uint32_t compute_claim[kMaxXcd];  // next compute claim per partition (init 0)
-    uint32_t reduce_claim[kMaxXcd];   // next reduce ticket per partition (init 0)
-    uint32_t exit_count;       // workgroups that left               (init 0)
-    uint32_t target_ns;        // controller target, 0 = unset       (init 0)
+    Line<uint32_t> compute_claim[kMaxXcd];  // next compute claim per partition (init 0)
+    Line<uint32_t> reduce_claim[kMaxXcd];   // next reduce ticket per partition (init 0)
+    Line<uint64_t> role_compute;   // (cycles << kCountBits) | tasks      (init 0)
+    Line<uint64_t> role_reduce;    //                                     (init 0)
+    Line<uint32_t> target_ns;      // controller target, 0 = unset        (init 0)
+    Line<uint32_t> chunks_released;//                                     (init 0)
+    uint64_t r_start;          // min over reduce tasks              (init ~0)
+    uint64_t r_end;            // max                                (init 0)
+    alignas(256) uint32_t exit_count;  // workgroups that left       (init 0)
     uint32_t role_switches;    //                                    (init 0)
-    uint32_t chunks_released;  //                                    (init 0)
     uint32_t violations;       //                                    (init 0)
     uint32_t error;            // Err                                (init 0)
     uint32_t ns_min;           //                                    (init ~0)
     uint32_t ns_max;           //                                    (init 0)
-    uint32_t trace_len;        //                                    (init 0)
+    uint32_t trace_len;        // written by workgroup 0 at exit     (init 0)
     uint32_t ns_final;         // written at exit                    (init 0)
-    uint32_t pad0[6];
-    uint64_t role_compute;     // (cycles << kCountBits) | tasks     (init 0)
-    uint64_t role_reduce;      //                                    (init 0)
     uint64_t t_start;          // min over workgroups                (init ~0)
     uint64_t t_end;            // max                                (init 0)
-    uint64_t r_start;          // min over reduce tasks              (init ~0)
-    uint64_t r_end;            // max                                (init 0)
 };
 
 // Workspace: one device allocation per device.

@@ -455,8 +455,7 @@ struct Gemm {
     }
 
     // Whole block at rows m0.., columns n0..: C = A[rows, :] . B[:, cols] in
-    // fp32.  `hook()` runs once the products are complete, before the block
-    // is stored.
+    // fp32.  `hook()` runs once the block's stores are issued (not drained).
     template <class Hook>
     static __device__ __forceinline__ void block(const Lane &ln, const uint16_t *A, const uint16_t *B,
                                                  float *C, int64_t M, int64_t N, int64_t K, int64_t m0,
@@ -486,7 +485,6 @@ struct Gemm {
         }
         // the ring is refilled by the next block only after every wave is done with it
         __syncthreads();
-        hook();
 
         // epilogue: 16-byte stores; rows >= M and columns >= N masked by an
         // out-of-range offset
@@ -510,6 +508,7 @@ struct Gemm {
                 }
             }
         }
+        hook();
     }
 };
 
@@ -745,6 +744,7 @@ struct Sched {
     uint32_t early_x, early_i, early_ns;
     bool early_flag;           // the readiness flags of the pending ticket's block
     uint32_t early_flag_value; // their common value (0 if they differ)
+    uint32_t trace_n;          // workgroup 0: target changes it has recorded
 };
 
 __device__ __forceinline__ bool timed_out(const FusedArgs &a, Live *L, uint64_t since) {
@@ -830,7 +830,7 @@ __device__ Decision next_task(const FusedArgs &a, const Parts &pt, const Blocks 
             for (uint32_t k = 0; k < parts; ++k) {
                 const uint32_t x = home + k < pt.nx ? home + k : home + k - pt.nx;
                 if (s.parts_done & (1u << x)) continue;
-                const uint32_t i = add_relaxed(&L->compute_claim[x], 1u);
+                const uint32_t i = add_relaxed(&L->compute_claim[x].v, 1u);
                 if (i < pt.size(x)) return {kRoleCompute, pt.tile(x, i), ns};
                 s.parts_done |= 1u << x;
             }
@@ -843,7 +843,7 @@ __device__ Decision next_task(const FusedArgs &a, const Parts &pt, const Blocks 
         // adaptive: a compute-role workgroup with no compute left reduces, as
         // every workgroup does once the controller's target reaches B
         s.pending_role = kRoleReduce;
-        s.pending_q = add_relaxed(&L->reduce_claim[a.local ? wg % pt.nx : 0u], 1u);
+        s.pending_q = add_relaxed(&L->reduce_claim[a.local ? wg % pt.nx : 0u].v, 1u);
         s.pending_ns = compute_role ? B : ns;
     }
 }
@@ -863,7 +863,7 @@ __device__ __forceinline__ void prefetch_claim(const FusedArgs &a, const Parts &
     if (d.role == kRoleReduce && !s.reduce_exhausted &&
                (!compute_role || (a.mode == kAdaptive && s.compute_exhausted))) {
         s.pending_role = kRoleReduce;
-        s.pending_q = add_relaxed(&L->reduce_claim[a.local ? wg % pt.nx : 0u], 1u);
+        s.pending_q = add_relaxed(&L->reduce_claim[a.local ? wg % pt.nx : 0u].v, 1u);
         s.pending_ns = compute_role ? (uint32_t)a.nwg : ns;
     }
 }
@@ -908,7 +908,7 @@ __device__ __forceinline__ Early early_issue(const FusedArgs &a, const Parts &pt
             e.kind = 1;
             e.x = x;
             e.ns = ns;
-            e.v0 = add_relaxed(&L->compute_claim[x], 1u);
+            e.v0 = add_relaxed(&L->compute_claim[x].v, 1u);
             return e;
         }
     }
@@ -929,20 +929,23 @@ __device__ __forceinline__ void early_finish(Sched &s, const Early &e) {
 }
 
 // Thread 0, after a task: one controller step from the two role words
-// (adaptive mode only); returns the target to use next.
-__device__ uint32_t controller_step(const FusedArgs &a, Live *L, uint64_t compute_word,
-                                    uint64_t reduce_word, uint32_t raw_target) {
+// (adaptive mode only); returns the target to use next.  Workgroup 0 records
+// the changes its own steps make in the trace, a sample of the target's path
+// that costs no shared counter.
+__device__ uint32_t controller_step(const FusedArgs &a, Live *L, uint32_t wg, Sched &s,
+                                    uint64_t compute_word, uint64_t reduce_word,
+                                    uint32_t raw_target) {
     const uint32_t cur = raw_target ? raw_target : (uint32_t)a.ns_init;
     const uint32_t n = controller_update(
         (uint32_t)a.nwg, a.T, (uint32_t)(compute_word & kCountMask),
         (uint32_t)(reduce_word & kCountMask), compute_word >> kCountBits,
         reduce_word >> kCountBits, cur, (uint32_t)a.ns_floor, (uint32_t)a.keep);
     if (n != cur || raw_target == 0) {
-        st_relaxed(&L->target_ns, n);
+        st_relaxed(&L->target_ns.v, n);
         min_relaxed(&L->ns_min, n);
         max_relaxed(&L->ns_max, n);
-        if (n != cur) {
-            const uint32_t i = add_relaxed(&L->trace_len, 1u);
+        if (wg == 0 && n != cur) {
+            const uint32_t i = s.trace_n++;
             if (i < (uint32_t)kTraceCap) {
                 a.ws.trace[2 * i] = (uint32_t)ticks_now();
                 a.ws.trace[2 * i + 1] = n;
@@ -957,38 +960,38 @@ __device__ uint32_t controller_step(const FusedArgs &a, Live *L, uint64_t comput
 __device__ void finish_launch(const FusedArgs &a, Live *L) {
     Live *S = a.ws.snap;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    const uint32_t raw = ld_relaxed(&L->target_ns);
-    for (int x = 0; x < kMaxXcd; ++x) S->compute_claim[x] = ld_relaxed(&L->compute_claim[x]);
-    for (int x = 0; x < kMaxXcd; ++x) S->reduce_claim[x] = ld_relaxed(&L->reduce_claim[x]);
+    const uint32_t raw = ld_relaxed(&L->target_ns.v);
+    for (int x = 0; x < kMaxXcd; ++x) S->compute_claim[x].v = ld_relaxed(&L->compute_claim[x].v);
+    for (int x = 0; x < kMaxXcd; ++x) S->reduce_claim[x].v = ld_relaxed(&L->reduce_claim[x].v);
     S->exit_count = ld_relaxed(&L->exit_count);
-    S->target_ns = raw;
+    S->target_ns.v = raw;
     S->role_switches = ld_relaxed(&L->role_switches);
-    S->chunks_released = ld_relaxed(&L->chunks_released);
+    S->chunks_released.v = ld_relaxed(&L->chunks_released.v);
     S->violations = ld_relaxed(&L->violations);
     S->error = ld_relaxed(&L->error);
     S->ns_min = ld_relaxed(&L->ns_min);
     S->ns_max = ld_relaxed(&L->ns_max);
     S->trace_len = ld_relaxed(&L->trace_len);
     S->ns_final = a.mode == kAdaptive ? (raw ? raw : (uint32_t)a.ns_init) : (uint32_t)a.ns_init;
-    S->role_compute = ld_relaxed(&L->role_compute);
-    S->role_reduce = ld_relaxed(&L->role_reduce);
+    S->role_compute.v = ld_relaxed(&L->role_compute.v);
+    S->role_reduce.v = ld_relaxed(&L->role_reduce.v);
     S->t_start = ld_relaxed(&L->t_start);
     S->t_end = ld_relaxed(&L->t_end);
     S->r_start = ld_relaxed(&L->r_start);
     S->r_end = ld_relaxed(&L->r_end);
 
-    for (int x = 0; x < kMaxXcd; ++x) st_relaxed(&L->compute_claim[x], 0u);
-    for (int x = 0; x < kMaxXcd; ++x) st_relaxed(&L->reduce_claim[x], 0u);
-    st_relaxed(&L->target_ns, 0u);
+    for (int x = 0; x < kMaxXcd; ++x) st_relaxed(&L->compute_claim[x].v, 0u);
+    for (int x = 0; x < kMaxXcd; ++x) st_relaxed(&L->reduce_claim[x].v, 0u);
+    st_relaxed(&L->target_ns.v, 0u);
     st_relaxed(&L->role_switches, 0u);
-    st_relaxed(&L->chunks_released, 0u);
+    st_relaxed(&L->chunks_released.v, 0u);
     st_relaxed(&L->violations, 0u);
     st_relaxed(&L->error, 0u);
     st_relaxed(&L->ns_min, 0xFFFFFFFFu);
     st_relaxed(&L->ns_max, 0u);
     st_relaxed(&L->trace_len, 0u);
-    st_relaxed(&L->role_compute, (uint64_t)0);
-    st_relaxed(&L->role_reduce, (uint64_t)0);
+    st_relaxed(&L->role_compute.v, (uint64_t)0);
+    st_relaxed(&L->role_reduce.v, (uint64_t)0);
     st_relaxed(&L->t_start, ~(uint64_t)0);
     st_relaxed(&L->t_end, (uint64_t)0);
     st_relaxed(&L->r_start, ~(uint64_t)0);
@@ -1014,26 +1017,26 @@ __device__ __forceinline__ CtlRead ctl_issue(const FusedArgs &a, Live *L, int ro
     CtlRead c;
     const uint64_t inc = (dt << kCountBits) | units;
     if (role == kRoleCompute) {
-        c.mine = add_relaxed(&L->role_compute, inc) + inc;
-        c.other = ld_relaxed(&L->role_reduce);
+        c.mine = add_relaxed(&L->role_compute.v, inc) + inc;
+        c.other = ld_relaxed(&L->role_reduce.v);
     } else {
-        c.mine = add_relaxed(&L->role_reduce, inc) + inc;
-        c.other = ld_relaxed(&L->role_compute);
+        c.mine = add_relaxed(&L->role_reduce.v, inc) + inc;
+        c.other = ld_relaxed(&L->role_compute.v);
         min_relaxed(&L->r_start, r0);
         max_relaxed(&L->r_end, r1);
     }
-    c.raw_target = a.mode == kAdaptive ? ld_relaxed(&L->target_ns) : 0u;
+    c.raw_target = a.mode == kAdaptive ? ld_relaxed(&L->target_ns.v) : 0u;
     return c;
 }
 
 // Thread 0: one controller step ("【学习】mKernel 分析" section 2.4) from the
 // words ctl_issue read; the role of the next task follows from its result.
-__device__ __forceinline__ void ctl_finish(const FusedArgs &a, Live *L, int role, const CtlRead &c,
-                                           Sched &s) {
+__device__ __forceinline__ void ctl_finish(const FusedArgs &a, Live *L, uint32_t wg, int role,
+                                           const CtlRead &c, Sched &s) {
     if (a.mode != kAdaptive) return;
     const uint64_t cw = role == kRoleCompute ? c.mine : c.other;
     const uint64_t rw = role == kRoleCompute ? c.other : c.mine;
-    s.target = controller_step(a, L, cw, rw, c.raw_target);
+    s.target = controller_step(a, L, wg, s, cw, rw, c.raw_target);
 }
 
 // Exactly-once and chunk counters of the tiles of a reduced block.  They are
@@ -1076,7 +1079,7 @@ __device__ __forceinline__ void cnt_finish(const FusedArgs &a, Live *L, const Cn
         if (k.old_c[i] + 1 == want) {
             // where a network send of the chunk would be posted
             st_relaxed(&a.ws.chunk_flag[c], a.epoch);
-            add_relaxed(&L->chunks_released, 1u);
+            add_relaxed(&L->chunks_released.v, 1u);
         } else if (k.old_c[i] + 1 > want) {
             add_relaxed(&L->violations, 1u);
         }
@@ -1156,6 +1159,7 @@ void fused_gemm_reduce_kernel(
         s.early_flag = false;
         s.early_flag_value = 0;
         s.decide_t0 = s.decide_t1 = 0;
+        s.trace_n = 0;
         min_relaxed(&L->t_start, ticks_now());
     }
 
@@ -1216,7 +1220,7 @@ void fused_gemm_reduce_kernel(
         }
         if (tid == 0) {
             cnt_finish(a, L, cnt);
-            ctl_finish(a, L, d.role, ctl, s);
+            ctl_finish(a, L, wg, d.role, ctl, s);
             early_finish(s, early);
         }
         // payload before flag ("【学习】mKernel 分析" section 2.5): every wave's
@@ -1255,6 +1259,7 @@ void fused_gemm_reduce_kernel(
         const CntRead k = cnt_issue(a, sh_pend_t0, sh_pend_n);
         cnt_finish(a, L, k);
         max_relaxed(&L->t_end, ticks_now());
+        if (wg == 0) st_relaxed(&L->trace_len, s.trace_n);
         const uint32_t old = add_acq_rel(&L->exit_count, 1u);
         if (old == (uint32_t)a.nwg - 1) finish_launch(a, L);
     }
@@ -1330,20 +1335,20 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
 // ---------------------------------------------------------------------------
 
 __device__ void live_init(Live *L) {
-    for (int x = 0; x < kMaxXcd; ++x) L->compute_claim[x] = 0;
-    for (int x = 0; x < kMaxXcd; ++x) L->reduce_claim[x] = 0;
+    for (int x = 0; x < kMaxXcd; ++x) L->compute_claim[x].v = 0;
+    for (int x = 0; x < kMaxXcd; ++x) L->reduce_claim[x].v = 0;
     L->exit_count = 0;
-    L->target_ns = 0;
+    L->target_ns.v = 0;
     L->role_switches = 0;
-    L->chunks_released = 0;
+    L->chunks_released.v = 0;
     L->violations = 0;
     L->error = 0;
     L->ns_min = 0xFFFFFFFFu;
     L->ns_max = 0;
     L->trace_len = 0;
     L->ns_final = 0;
-    L->role_compute = 0;
-    L->role_reduce = 0;
+    L->role_compute.v = 0;
+    L->role_reduce.v = 0;
     L->t_start = ~(uint64_t)0;
     L->t_end = 0;
     L->r_start = ~(uint64_t)0;

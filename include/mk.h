@@ -183,7 +183,8 @@ typedef struct mk_stats {
     uint32_t reduce_tasks;        /* reduce tasks finished (== T)                */
     uint32_t chunks_released;     /* chunks whose last tile was reduced (== Ch)  */
     uint32_t invariant_violations;/* flag/counter mismatches seen on the device  */
-    uint32_t ns_trace_len;        /* entries in the controller trace             */
+    uint32_t ns_trace_len;        /* entries in the controller trace (the target
+                                     changes made by workgroup 0's own steps)  */
     uint32_t tiles_per_task;      /* output tiles of one compute/reduce task     */
     uint64_t sum_cycles_compute;  /* shader-clock cycles over compute tasks      */
     uint64_t sum_cycles_reduce;   /* shader-clock cycles over reduce tasks       */
@@ -202,7 +203,8 @@ typedef struct mk_stats {
  *   compute_start[T] | compute_end[T] | reduce_start[T] | reduce_end[T] |
  *   compute_choice_ticks[T] | reduce_choice_ticks[T]
  * Owner words are (reduce target seen << 16) | workgroup.  Trace entries are
- * pairs (low 32 bits of the constant clock, new target).  The four timeline
+ * pairs (low 32 bits of the constant clock, new target), one for each step
+ * of workgroup 0 that changed the target: a sample of the target's path.  The four timeline
  * maps hold the low 32 bits of the constant clock at each task's start and
  * end (compare with kernel_ticks_start modulo 2^32); the last two, the ticks
  * the workgroup spent choosing the task (claim and readiness wait). */
