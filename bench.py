@@ -202,6 +202,8 @@ def main():
         "xcd_local": st["xcd_local"],
         "n_reduce_initial": st["n_reduce_initial"],
         "n_reduce_range": [st["n_reduce_min_seen"], st["n_reduce_max_seen"]],
+        "controller_cap": st["controller_cap"],
+        "help_tiles": int((st["compute_owner"] >> 31).sum()),
     }
     print(f"[bench] fused adaptive: {summary(ms_fused)} (n_reduce final {st['n_reduce_final']}, "
           f"range {st['n_reduce_min_seen']}-{st['n_reduce_max_seen']})", file=sys.stderr, flush=True)

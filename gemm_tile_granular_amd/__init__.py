@@ -75,6 +75,7 @@ class Stats(ctypes.Structure):
         ("timer_hz", ctypes.c_uint64),
         ("xcd_local", ctypes.c_uint32),
         ("keep_compute", ctypes.c_uint32),
+        ("controller_cap", ctypes.c_uint32),
     ]
 
 
@@ -85,6 +86,7 @@ SIGNATURES = {
     "mk_gemm_reduce_unfused": (_i32, [_vp, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp]),
     "mk_set_partition": (_i32, [_i32, _i32]),
     "mk_set_controller_floor": (_i32, [_i32]),
+    "mk_set_controller_cap": (_i32, [_i32]),
     "mk_set_num_workgroups": (_i32, [_i32]),
     "mk_set_timeout_us": (_i32, [ctypes.c_uint64]),
     "mk_set_fault_skip_publish": (_i32, [_i64]),
@@ -99,7 +101,7 @@ SIGNATURES = {
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m gemm_tile_granular_amd.build` "
+        raise ImportError(f"{LIB_PATH} is not built; run `python gemm_tile_granular_amd/build.py` "
                           "(or __graft_entry__.build()) first")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
@@ -173,6 +175,11 @@ def set_partition(mode, n_reduce: int = 0) -> None:
 
 def set_controller_floor(floor: int) -> None:
     _check(lib.mk_set_controller_floor(int(floor)))
+
+
+def set_controller_cap(cap: int) -> None:
+    """Most reduce workgroups the adaptive controller sets while compute remains (0: B/2)."""
+    _check(lib.mk_set_controller_cap(int(cap)))
 
 
 def set_num_workgroups(num_wg: int) -> None:
@@ -249,10 +256,10 @@ def get_stats(maps: bool = False, raise_on_error: bool = True) -> Dict:
 
 def controller_eval(rows: np.ndarray) -> np.ndarray:
     """Runs the device controller step on each row (B, T, compute_done,
-    reduce_done, sum_cycles_compute, sum_cycles_reduce, current, floor, keep)."""
+    reduce_done, sum_cycles_compute, sum_cycles_reduce, current, floor, keep, cap)."""
     torch = _torch()
     rows = np.ascontiguousarray(rows, dtype=np.uint64)
-    assert rows.ndim == 2 and rows.shape[1] == 9
+    assert rows.ndim == 2 and rows.shape[1] == 10
     n = rows.shape[0]
     dev_in = torch.from_numpy(rows.view(np.int64)).cuda()
     dev_out = torch.zeros(n, dtype=torch.int32, device=dev_in.device)

@@ -39,6 +39,7 @@ struct Settings {
     int mode = MK_PART_ADAPTIVE;
     int n_reduce = 0;
     int floor = 2;
+    int cap = 0;              // 0: half the workgroups
     int num_wg = 0;
     uint64_t timeout_us = 2000000;
     int64_t skip_publish = -1;
@@ -52,7 +53,7 @@ struct Launch {
     bool valid = false;
     uint32_t epoch = 0, calls = 0, nwg = 0, T = 0, Ch = 0, tpc = 0, tm = 0, tn = 0;
     uint32_t mode = 0, ns_init = 0;
-    uint32_t local = 0, keep = 1;
+    uint32_t local = 0, keep = 1, cap = 0;
 };
 
 struct DevState {
@@ -312,9 +313,17 @@ int run(bool fused, const void *A, const void *B, const float *peers, int num_pe
                        set.mode != MK_PART_STATIC_DETERMINISTIC &&
                        (set.mode == MK_PART_ADAPTIVE || (ns_init >= nxcd && ns_init <= nwg - nxcd));
     const int keep = local ? nxcd : 1;
+    // most reducers while compute remains: half the workgroups by default
+    // (about where the reduce role saturates HBM: a CU streams 40-57 GB/s)
+    int cap = set.cap ? set.cap : nwg / 2;
+    if (cap > nwg - keep) cap = nwg - keep;
+    if (cap < 1) cap = 1;
     if (set.mode == MK_PART_ADAPTIVE) {
-        if (ns_init == 0) ns_init = 2;
-        if (ns_init > nwg - keep) ns_init = nwg - keep;
+        // default start: the cap.  Reducers with nothing ready yet compute,
+        // so a high start costs no idle workgroups, and the reduce role is
+        // staffed the moment the first tiles are published.
+        if (ns_init == 0) ns_init = cap;
+        if (ns_init > cap) ns_init = cap;
         if (ns_init < 1) ns_init = 1;
     }
 
@@ -374,6 +383,7 @@ int run(bool fused, const void *A, const void *B, const float *peers, int num_pe
     a.nxcd = nxcd;
     a.local = local ? 1 : 0;
     a.keep = keep;
+    a.ns_cap = cap;
     a.timeout_ticks = set.timeout_us * (d.timer_hz / 1000000ull);
     a.skip_publish = set.skip_publish;
     a.ws = v;
@@ -395,6 +405,7 @@ int run(bool fused, const void *A, const void *B, const float *peers, int num_pe
     d.last.ns_init = (uint32_t)ns_init;
     d.last.local = local ? 1u : 0u;
     d.last.keep = (uint32_t)keep;
+    d.last.cap = (uint32_t)cap;
     return MK_OK;
 }
 
@@ -432,6 +443,13 @@ int mk_set_controller_floor(int floor) {
     std::lock_guard<std::mutex> lk(g_mu);
     if (floor < 1 || floor > kMaxWG) return fail(MK_ERR_INVALID_ARG, "floor must be in [1, 1024]");
     g_set.floor = floor;
+    return MK_OK;
+}
+
+int mk_set_controller_cap(int cap) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (cap < 0 || cap > kMaxWG) return fail(MK_ERR_INVALID_ARG, "cap must be in [0, 1024]");
+    g_set.cap = cap;
     return MK_OK;
 }
 
@@ -514,6 +532,7 @@ int mk_get_stats(mk_stats *out, uint32_t *maps, size_t maps_len) {
     out->timer_hz = d.timer_hz;
     out->xcd_local = l.local;
     out->keep_compute = l.keep;
+    out->controller_cap = l.cap;
 
     if (maps) {
         uint32_t *p = maps;

@@ -91,6 +91,7 @@ struct FusedArgs {
     int32_t nxcd;             // tile partitions (XCDs) for the claim order
     int32_t local;            // 1: every tile is computed and reduced on its partition's XCD
     int32_t keep;             // compute workgroups the controller keeps while compute remains
+    int32_t ns_cap;           // most reduce workgroups the controller sets while compute remains
     uint64_t timeout_ticks;   // bound on any wait, constant-clock ticks
     int64_t skip_publish;     // fault injection: tile whose flag is never set (-1 none)
     WsView ws;

@@ -95,9 +95,6 @@ template <class T> __device__ __forceinline__ void st_relaxed(T *p, T v) {
 template <class T> __device__ __forceinline__ T add_relaxed(T *p, T v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-template <class T> __device__ __forceinline__ T add_acq_rel(T *p, T v) {
-    return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-}
 template <class T> __device__ __forceinline__ void min_relaxed(T *p, T v) {
     __hip_atomic_fetch_min(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -119,11 +116,12 @@ template <class T> __device__ __forceinline__ void max_relaxed(T *p, T v) {
 // ---------------------------------------------------------------------------
 __device__ uint32_t controller_update(uint32_t B, uint32_t T, uint32_t compute_done,
                                       uint32_t reduce_done, uint64_t sum_p, uint64_t sum_s,
-                                      uint32_t current, uint32_t floor, uint32_t keep) {
+                                      uint32_t current, uint32_t floor, uint32_t keep,
+                                      uint32_t cap) {
     const uint32_t R_p = T - compute_done;
     const uint32_t R_s = T - reduce_done;
     if (R_p == 0) return B;
-    const uint32_t hi = B - keep;
+    const uint32_t hi = B - keep < cap ? B - keep : cap;
     const uint32_t lo = floor < hi ? floor : hi;
     uint64_t n;
     if (compute_done == 0 || reduce_done == 0) {
@@ -688,8 +686,10 @@ enum Role : int { kRoleCompute = 0, kRoleReduce = 1, kRoleExit = 2, kRoleNone = 
 struct Decision {
     int role;
     uint32_t tile;      // compute: block index; reduce: tile index
-    uint32_t ns_seen;   // reduce target the claim was made under (logged in owner maps)
+    uint32_t ns_seen;   // reduce target the claim was made under (logged in owner maps),
+                        // | kHelp for a compute task taken while a reduce ticket waits
 };
+constexpr uint32_t kHelp = 1u << 15;   // bit 31 of the owner word
 
 // Compute tasks are blocks of tpb adjacent tiles of one tile row (a ragged
 // last block holds fewer).  A reduce task takes the same block once every
@@ -775,12 +775,47 @@ __device__ bool wait_block(const FusedArgs &a, const Blocks &bk, Live *L, uint32
     return true;
 }
 
+// Thread 0: claim a compute block, from the workgroup's own partition first,
+// then (unless tiles stay on their XCD) the others.  False once every
+// partition it may claim from is exhausted.
+__device__ __forceinline__ bool claim_compute(const FusedArgs &a, const Parts &pt, Live *L,
+                                              uint32_t wg, Sched &s, uint32_t &block) {
+    if (s.compute_exhausted) return false;
+    const uint32_t home = wg % pt.nx;
+    const uint32_t parts = a.local ? 1u : pt.nx;
+    for (uint32_t k = 0; k < parts; ++k) {
+        const uint32_t x = home + k < pt.nx ? home + k : home + k - pt.nx;
+        if (s.parts_done & (1u << x)) continue;
+        const uint32_t i = add_relaxed(&L->compute_claim[x].v, 1u);
+        if (i < pt.size(x)) {
+            block = pt.tile(x, i);
+            return true;
+        }
+        s.parts_done |= 1u << x;
+    }
+    s.compute_exhausted = true;
+    return false;
+}
+
+// Every tile of block b carries this launch's epoch (one compute task stores
+// their flags together, so the first and the last decide).
+__device__ __forceinline__ bool block_ready(const FusedArgs &a, const Blocks &bk, uint32_t b) {
+    const uint32_t t0 = bk.first_tile(b), t1 = t0 + bk.count(b) - 1;
+    const uint32_t f0 = ld_relaxed(&a.ws.tile_flag[t0]);
+    const uint32_t f1 = ld_relaxed(&a.ws.tile_flag[t1]);
+    return f0 == a.epoch && f1 == a.epoch;
+}
+
 // Thread 0 only: the next task.  Roles follow the workgroup index against the
 // current target and are re-read here, at every task boundary ("【学习】mKernel
 // 分析" sections 2.4 and 4.1).  Claims are tickets from device-scope counters
 // in one common order, so compute and reduce walk the tiles in step.  A claim
 // taken ahead of time (prefetched during the previous task) is a commitment
 // and is honoured first, so a role change takes effect one task later.
+// Under the adaptive controller a workgroup whose reduce ticket is not ready
+// yet computes a block meanwhile and keeps the ticket: a block waiting for its
+// input helps the other role ("【学习】mKernel 分析" section 2.4, read in the
+// direction data flows here, from compute to reduce).
 __device__ Decision next_task(const FusedArgs &a, const Parts &pt, const Blocks &bk, Live *L, uint32_t wg,
                              Sched &s) {
     const uint32_t B = (uint32_t)a.nwg;
@@ -814,7 +849,17 @@ __device__ Decision next_task(const FusedArgs &a, const Parts &pt, const Blocks 
             const uint32_t home = wg % pt.nx;
             if (a.local ? q < pt.size(home) : q < bk.TB) {
                 const uint32_t b = a.local ? pt.tile(home, q) : pt.ticket(q);
-                if (!seen && !wait_block(a, bk, L, b)) return {kRoleExit, 0, ns_seen};
+                if (!seen) {
+                    uint32_t cb;
+                    if (a.mode == kAdaptive && !s.compute_exhausted && !block_ready(a, bk, b) &&
+                        claim_compute(a, pt, L, wg, s, cb)) {
+                        s.pending_role = kRoleReduce;
+                        s.pending_q = q;
+                        s.pending_ns = ns_seen;
+                        return {kRoleCompute, cb, s.target | kHelp};
+                    }
+                    if (!wait_block(a, bk, L, b)) return {kRoleExit, 0, ns_seen};
+                }
                 return {kRoleReduce, b, ns_seen};
             }
             s.reduce_exhausted = true;
@@ -823,18 +868,8 @@ __device__ Decision next_task(const FusedArgs &a, const Parts &pt, const Blocks 
         const uint32_t ns = s.target;
         const bool compute_role = wg >= ns;
         if (compute_role && !s.compute_exhausted) {
-            // own XCD's partition first, then (unless tiles stay on their
-            // XCD) the others
-            const uint32_t home = wg % pt.nx;
-            const uint32_t parts = a.local ? 1u : pt.nx;
-            for (uint32_t k = 0; k < parts; ++k) {
-                const uint32_t x = home + k < pt.nx ? home + k : home + k - pt.nx;
-                if (s.parts_done & (1u << x)) continue;
-                const uint32_t i = add_relaxed(&L->compute_claim[x].v, 1u);
-                if (i < pt.size(x)) return {kRoleCompute, pt.tile(x, i), ns};
-                s.parts_done |= 1u << x;
-            }
-            s.compute_exhausted = true;
+            uint32_t cb;
+            if (claim_compute(a, pt, L, wg, s, cb)) return {kRoleCompute, cb, ns};
             continue;
         }
         // static partition: compute workgroups leave once compute is all claimed
@@ -939,7 +974,7 @@ __device__ uint32_t controller_step(const FusedArgs &a, Live *L, uint32_t wg, Sc
     const uint32_t n = controller_update(
         (uint32_t)a.nwg, a.T, (uint32_t)(compute_word & kCountMask),
         (uint32_t)(reduce_word & kCountMask), compute_word >> kCountBits,
-        reduce_word >> kCountBits, cur, (uint32_t)a.ns_floor, (uint32_t)a.keep);
+        reduce_word >> kCountBits, cur, (uint32_t)a.ns_floor, (uint32_t)a.keep, (uint32_t)a.ns_cap);
     if (n != cur || raw_target == 0) {
         st_relaxed(&L->target_ns.v, n);
         min_relaxed(&L->ns_min, n);
@@ -1260,7 +1295,13 @@ void fused_gemm_reduce_kernel(
         cnt_finish(a, L, k);
         max_relaxed(&L->t_end, ticks_now());
         if (wg == 0) st_relaxed(&L->trace_len, s.trace_n);
-        const uint32_t old = add_acq_rel(&L->exit_count, 1u);
+        // Every write this workgroup made to the control block is a
+        // device-scope atomic, complete once the drain returns, so a relaxed
+        // count suffices for the last workgroup to read them all.  A release
+        // here would write back (and the acquire invalidate) the XCD's L2
+        // under the workgroups still reducing.
+        drain_vmem();
+        const uint32_t old = add_relaxed(&L->exit_count, 1u);
         if (old == (uint32_t)a.nwg - 1) finish_launch(a, L);
     }
 }
@@ -1379,9 +1420,9 @@ __global__ __launch_bounds__(64) void xcc_probe_kernel(uint32_t *out) {
 __global__ void controller_eval_kernel(const uint64_t *in, uint32_t *out, int n) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    const uint64_t *r = in + 9 * (int64_t)i;
+    const uint64_t *r = in + 10 * (int64_t)i;
     out[i] = controller_update((uint32_t)r[0], (uint32_t)r[1], (uint32_t)r[2], (uint32_t)r[3], r[4],
-                               r[5], (uint32_t)r[6], (uint32_t)r[7], (uint32_t)r[8]);
+                               r[5], (uint32_t)r[6], (uint32_t)r[7], (uint32_t)r[8], (uint32_t)r[9]);
 }
 
 // ---------------------------------------------------------------------------

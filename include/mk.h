@@ -60,7 +60,11 @@ typedef enum {
 
 typedef enum {
     /* On-GPU controller sets the reduce-workgroup count from measured
-     * per-task cycle costs ("【学习】mKernel 分析" section 2.4).            */
+     * per-task cycle costs ("【学习】mKernel 分析" section 2.4), bounded
+     * by mk_set_controller_floor and mk_set_controller_cap while compute
+     * remains.  A reduce-role workgroup whose next block is not published
+     * yet computes a block meanwhile (the same section: a block waiting
+     * for input helps the other role) and keeps its reduce ticket.       */
     MK_PART_ADAPTIVE = 0,
     /* Fixed count of reduce workgroups; tasks are claimed dynamically.     */
     MK_PART_STATIC = 1,
@@ -124,8 +128,10 @@ int mk_gemm_reduce_unfused(const void *A, const void *B, const float *peers, int
  * compute roles for subsequent mk_gemm_reduce_local launches (process-wide).
  *   mode       mk_part_mode.
  *   n_reduce   STATIC*: reduce-workgroup count, must lie in [1, B-1] at launch
- *              time (B = workgroups of the launch).  ADAPTIVE: initial count
- *              (0 selects 2, the low end of the page's 2-64 sweep).
+ *              time (B = workgroups of the launch).  ADAPTIVE: initial count,
+ *              at most the controller cap (0 selects the cap, B/2 by default;
+ *              reducers with no tile ready compute meanwhile, so a high start
+ *              leaves no workgroup idle).
  * Errors: MK_ERR_INVALID_ARG for an unknown mode or negative n_reduce.
  */
 int mk_set_partition(int mode, int n_reduce);
@@ -135,6 +141,17 @@ int mk_set_partition(int mode, int n_reduce);
  * may choose while compute remains (default 2; clamped to B-1 at run time).
  */
 int mk_set_controller_floor(int floor);
+
+/*
+ * mk_set_controller_cap -- largest reduce count the adaptive controller may
+ * choose while compute remains.  0 (default) = B/2: on MI355X the reduce
+ * role saturates HBM with about half the CUs (one CU streams 40-57 GB/s),
+ * and more reducers only lengthen every reduce task while taking compute
+ * units from the tiles they wait for.  Valid: 0..1024; at run time it is
+ * clamped to [1, B - keep_compute].  Also bounds the initial adaptive count.
+ * Errors: MK_ERR_INVALID_ARG outside 0..1024.
+ */
+int mk_set_controller_cap(int cap);
 
 /*
  * mk_set_num_workgroups -- persistent workgroups per launch (B).  0 (default)
@@ -195,6 +212,7 @@ typedef struct mk_stats {
     uint64_t timer_hz;            /* constant clock frequency                    */
     uint32_t xcd_local;           /* 1: every tile stayed on its partition's XCD */
     uint32_t keep_compute;        /* compute workgroups the controller kept      */
+    uint32_t controller_cap;      /* most reducers while compute remained        */
 } mk_stats;
 
 /* Words per map in the optional `maps` output of mk_get_stats, in order:
@@ -202,7 +220,9 @@ typedef struct mk_stats {
  *   compute_owner[T] | reduce_owner[T] | ns_trace[2 * MK_TRACE_CAP] |
  *   compute_start[T] | compute_end[T] | reduce_start[T] | reduce_end[T] |
  *   compute_choice_ticks[T] | reduce_choice_ticks[T]
- * Owner words are (reduce target seen << 16) | workgroup.  Trace entries are
+ * Owner words are (help << 31) | (reduce target seen << 16) | workgroup, where
+ * help marks a compute task taken by a workgroup waiting on a reduce ticket
+ * (adaptive mode only).  Trace entries are
  * pairs (low 32 bits of the constant clock, new target), one for each step
  * of workgroup 0 that changed the target: a sample of the target's path.  The four timeline
  * maps hold the low 32 bits of the constant clock at each task's start and
@@ -223,12 +243,13 @@ int mk_get_stats(mk_stats *out, uint32_t *maps, size_t maps_len);
 
 /*
  * mk_controller_eval -- evaluates the device's controller step on a table,
- * for parity tests against the host closed form.  `in` holds n rows of nine
+ * for parity tests against the host closed form.  `in` holds n rows of ten
  * uint64 (device memory): B, T, compute_done, reduce_done,
  * sum_cycles_compute, sum_cycles_reduce, current_target, floor, keep (compute
  * workgroups the clamp keeps while compute remains: 1, or one per XCD when
- * tiles stay on their XCD).  `out` (device, n uint32) receives the new target
- * for each row.  Limits: B in [2, 1024], T < 2^22, 1 <= keep < B.
+ * tiles stay on their XCD), cap (most reducers while compute remains).
+ * `out` (device, n uint32) receives the new target for each row.  Limits:
+ * B in [2, 1024], T < 2^22, 1 <= keep < B, cap >= 1.
  * Asynchronous on `stream`.
  */
 int mk_controller_eval(const uint64_t *in, uint32_t *out, int n, void *stream);

@@ -27,7 +27,11 @@ What it computes, and from which passage:
   protocol: per-tile readiness flags (section 2.2, Figure 2), per-chunk
   counters where the last tile of a 4-tile chunk releases it (section 2.3),
   roles chosen by workgroup index and re-checked at task boundaries
-  (sections 2.4 and 4.1).
+  (sections 2.4 and 4.1); under the adaptive controller a reduce-role
+  workgroup whose next tile is not ready yet may compute meanwhile (the
+  section 2.4 rule that a block waiting for its input helps the other role,
+  read in the direction this kernel's data flows), which its owner word
+  marks.
 
 Parity pins (tests/test_oracle.py) tie each function to something other than
 itself: hand-worked fixtures, closed forms (A = 0, no peers, B = I, all-ones,
@@ -173,7 +177,8 @@ COST_CAP = (1 << 26) - 1     # per-task cycle means saturate here (keeps the u64
 
 
 def controller_target(B: int, R_s: int, C_s: int, R_p: int, C_p: int,
-                      current: int, floor: int = 2, keep: int = 1) -> int:
+                      current: int, floor: int = 2, keep: int = 1,
+                      cap: Optional[int] = None) -> int:
     """Target reduce-workgroup count n_s*.
 
     Readings of the page's undefined symbols (applied here and on the GPU):
@@ -188,14 +193,17 @@ def controller_target(B: int, R_s: int, C_s: int, R_p: int, C_p: int,
     partition is worked only by its own XCD's workgroups -- otherwise a
     partition could be left without a producer) and at least `floor` reducers
     (2, the low end of the page's static sweep); with no compute left the
-    formula itself gives B.
+    formula itself gives B.  `cap` (None: none) is the most reducers while
+    compute remains: the count at which the reduce role already saturates the
+    memory system, past which more reducers only stretch every reduce task and
+    take compute units from the tiles the reducers wait for.
     A zero denominator carries no information: the current target stays.
     """
     if B < 2:
         raise ValueError("need at least two workgroups")
     if R_p == 0:
         return B
-    hi = B - keep
+    hi = _upper(B, keep, cap)
     lo = min(floor, hi)
     num = B * R_s * C_s
     den = R_p * C_p + R_s * C_s
@@ -208,6 +216,16 @@ def controller_target(B: int, R_s: int, C_s: int, R_p: int, C_p: int,
     return min(max(n, lo), hi)
 
 
+def _upper(B: int, keep: int, cap: Optional[int]) -> int:
+    """Upper clamp while compute remains: B - keep, and at most `cap`."""
+    hi = B - keep
+    if cap is not None:
+        if cap < 1:
+            raise ValueError("cap must be at least 1")
+        hi = min(hi, cap)
+    return hi
+
+
 def cycle_mean(total_cycles: int, tasks: int) -> int:
     """Cumulative mean cost per task since launch (integer, saturating)."""
     return min(total_cycles // tasks, COST_CAP)
@@ -215,7 +233,8 @@ def cycle_mean(total_cycles: int, tasks: int) -> int:
 
 def controller_update(B: int, T: int, compute_done: int, reduce_done: int,
                       sum_cycles_compute: int, sum_cycles_reduce: int,
-                      current: int, floor: int = 2, keep: int = 1) -> int:
+                      current: int, floor: int = 2, keep: int = 1,
+                      cap: Optional[int] = None) -> int:
     """One controller step from the progress counters.
 
     R_p counts compute tasks not yet finished (claimed-but-running tasks count
@@ -228,11 +247,11 @@ def controller_update(B: int, T: int, compute_done: int, reduce_done: int,
     if R_p == 0:
         return B
     if compute_done == 0 or reduce_done == 0:
-        hi = B - keep
+        hi = _upper(B, keep, cap)
         return min(max(current, min(floor, hi)), hi)
     C_p = cycle_mean(sum_cycles_compute, compute_done)
     C_s = cycle_mean(sum_cycles_reduce, reduce_done)
-    return controller_target(B, R_s, C_s, R_p, C_p, current, floor, keep)
+    return controller_target(B, R_s, C_s, R_p, C_p, current, floor, keep, cap)
 
 
 def controller_exact(B: int, R_s: int, C_s: int, R_p: int, C_p: int) -> Fraction:
@@ -289,6 +308,8 @@ def deterministic_owners(T: int, B: int, n_reduce: int, tiles_n: Optional[int] =
 
 
 OWNER_WG_MASK = 0xFFFF
+OWNER_NS_MASK = 0x7FFF        # bits 16..30: the reduce target the task was taken under
+OWNER_HELP = 1 << 31          # compute task taken by a workgroup waiting on a reduce ticket
 
 
 def expected_state(T: int, tiles_per_chunk: int, epoch: int, calls: int) -> Dict[str, np.ndarray]:
@@ -326,8 +347,8 @@ def check_state(maps: Dict[str, np.ndarray], T: int, tiles_per_chunk: int, epoch
                        f"({idx.size} mismatches)")
     co = np.asarray(maps["compute_owner"], dtype=np.int64)
     ro = np.asarray(maps["reduce_owner"], dtype=np.int64)
-    co_wg, co_ns = co & OWNER_WG_MASK, co >> 16
-    ro_wg, ro_ns = ro & OWNER_WG_MASK, ro >> 16
+    co_wg, co_ns, co_help = co & OWNER_WG_MASK, (co >> 16) & OWNER_NS_MASK, (co & OWNER_HELP) != 0
+    ro_wg, ro_ns, ro_help = ro & OWNER_WG_MASK, (ro >> 16) & OWNER_NS_MASK, (ro & OWNER_HELP) != 0
     if mode == "deterministic":
         dc, dr = deterministic_owners(T, B, n_reduce, tiles_n, tiles_per_task)
         if not np.array_equal(co_wg, dc):
@@ -348,9 +369,14 @@ def check_state(maps: Dict[str, np.ndarray], T: int, tiles_per_chunk: int, epoch
         bad.append("compute owner outside [0, B)")
     if np.any(ro_wg >= B):
         bad.append("reduce owner outside [0, B)")
-    # role at the time of the task: compute iff index >= target, reduce iff index < target
-    if np.any(co_wg < co_ns):
-        i = int(np.nonzero(co_wg < co_ns)[0][0])
+    # role at the time of the task: compute iff index >= target, reduce iff
+    # index < target; a compute task marked as help may come from either
+    if np.any(ro_help):
+        bad.append(f"tile {int(np.nonzero(ro_help)[0][0])}: reduce owner carries the help mark")
+    if mode != "adaptive" and np.any(co_help):
+        bad.append(f"tile {int(np.nonzero(co_help)[0][0])}: help task outside adaptive mode")
+    if np.any((co_wg < co_ns) & ~co_help):
+        i = int(np.nonzero((co_wg < co_ns) & ~co_help)[0][0])
         bad.append(f"tile {i} computed by workgroup {int(co_wg[i])} while the reduce "
                    f"target was {int(co_ns[i])}")
     if np.any(ro_wg >= ro_ns):

@@ -13,7 +13,12 @@ HEADER = os.path.join(ROOT, "include", "mk.h")
 
 @pytest.fixture(scope="module")
 def mk():
-    from gemm_tile_granular_amd import build
+    # build.py by path: importing the package first would load a stale library
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_mk_build", os.path.join(ROOT, "gemm_tile_granular_amd", "build.py"))
+    build = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(build)
     if build.is_stale():
         build.build()
     import gemm_tile_granular_amd as mk
@@ -64,7 +69,7 @@ def test_stats_struct_matches_header(mk):
     got = [(n, t) for n, t in mk.Stats._fields_]
     assert [n for n, _ in got] == [n for n, _ in fields]
     assert all(t == want[c] for (_, t), (_, c) in zip(got, fields))
-    assert ctypes.sizeof(mk.Stats) == 152
+    assert ctypes.sizeof(mk.Stats) == 160
 
 
 def test_abi_version_and_trace_cap(mk):
@@ -131,6 +136,9 @@ def test_setting_calls_validate(mk):
     assert lib.mk_set_fault_skip_publish(-1) == 0
     assert lib.mk_set_controller_floor(0) == -1
     assert lib.mk_set_controller_floor(2) == 0
+    assert lib.mk_set_controller_cap(-1) == -1
+    assert lib.mk_set_controller_cap(1025) == -1
+    assert lib.mk_set_controller_cap(0) == 0
     assert lib.mk_controller_eval(None, None, -1, None) == -1
     assert lib.mk_controller_eval(None, None, 0, None) == 0
 

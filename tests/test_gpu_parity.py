@@ -23,6 +23,7 @@ def mk():
     mk.set_timeout_us(2_000_000)
     mk.set_fault_skip_publish(-1)
     mk.set_controller_floor(2)
+    mk.set_controller_cap(0)
     yield mk
     mk.set_partition("adaptive", 0)
     mk.set_num_workgroups(0)
@@ -176,17 +177,19 @@ def test_controller_device_matches_host_closed_form(mk):
         cur = int(rng.integers(1, B + 1))
         fl = int(rng.integers(1, 70))
         kp = int(rng.choice([1, 8])) if B > 8 else 1
-        rows.append((B, T, cd, rd, sp, ss, cur, fl, kp))
+        cap = int(rng.choice([B, B // 2 or 1, int(rng.integers(1, B + 1))]))
+        rows.append((B, T, cd, rd, sp, ss, cur, fl, kp, cap))
     # the hand-worked table, expressed as progress counters with exact means
     with open(os.path.join(os.path.dirname(__file__), "golden", "controller_table.json")) as f:
         g = json.load(f)
     for B, R_s, C_s, R_p, C_p, _, _ in g["rows"]:
         T = max(R_s, R_p) + 5
-        rows.append((B, T, T - R_p, T - R_s, (T - R_p) * C_p, (T - R_s) * C_s, 7 if B > 7 else 1, 2, 1))
+        rows.append((B, T, T - R_p, T - R_s, (T - R_p) * C_p, (T - R_s) * C_s, 7 if B > 7 else 1, 2, 1, B))
     table = np.array(rows, dtype=np.uint64)
     got = mk.controller_eval(table)
     want = np.array([oracle.controller_update(*[int(x) for x in r[:6]], current=int(r[6]),
-                                              floor=int(r[7]), keep=int(r[8])) for r in rows],
+                                              floor=int(r[7]), keep=int(r[8]), cap=int(r[9]))
+                     for r in rows],
                     dtype=np.uint32)
     mism = np.nonzero(got != want)[0]
     assert mism.size == 0, [(rows[i], int(got[i]), int(want[i])) for i in mism[:5]]
@@ -226,8 +229,10 @@ FULL = ["tp_share", "reduce_heavy", "compute_heavy", "wide_many_peer"]
 def test_full_size_workload_sampled(mk, name):
     w = wl.workload(name)
     a, b, p = wl.make_inputs(w)
-    C, st = run_fused(mk, w, a, b, p, mode="adaptive", n_reduce=2)
-    check_protocol(st, w, "adaptive", 2)
+    # the launch configuration the benchmark times: the library's default
+    # initial target (the controller cap) and cap
+    C, st = run_fused(mk, w, a, b, p, mode="adaptive", n_reduce=0)
+    check_protocol(st, w, "adaptive", 0)
     tiles_m, tiles_n = oracle.tile_grid(w.M, w.N, w.tile_m, w.tile_n)
     rng = np.random.default_rng(7)
     check_sampled(C, a, b, p, rng, tiles=[(0, 0), (tiles_m - 1, tiles_n - 1),
@@ -240,7 +245,31 @@ def test_full_size_workload_sampled(mk, name):
         assert np.all(np.abs(C[:nz].astype(np.float64) - ps) <= w.peers * 2.0 ** -24 * absum + 1e-30)
     print(f"[gpu] {name}: n_reduce initial {st['n_reduce_initial']} final {st['n_reduce_final']} "
           f"range [{st['n_reduce_min_seen']}, {st['n_reduce_max_seen']}] "
-          f"switches {st['role_switches']}", flush=True)
+          f"switches {st['role_switches']} cap {st['controller_cap']} "
+          f"help tiles {int((st['compute_owner'] >> 31).sum())}", flush=True)
+
+
+def test_adaptive_reducers_help_compute_while_waiting(mk):
+    # 16 workgroups (8 per role at the start), 32 blocks of 128x256 with
+    # K = 4096: no block can be published before every reducer's first
+    # readiness check, so reducers take compute blocks (marked as help) and
+    # keep their tickets; the result and the protocol must not change.
+    mk.set_num_workgroups(16)
+    mk.set_controller_cap(8)
+    try:
+        w = wl.custom(1024, 1024, 4096, 3, 128, 128, 4, wid=611)
+        a, b, p = wl.make_inputs(w)
+        C, st = run_fused(mk, w, a, b, p, mode="adaptive", n_reduce=8)
+        check_full(C, a, b, p)
+        check_protocol(st, w, "adaptive", 8)
+        help_tiles = int((st["compute_owner"] >> 31).sum())
+        print(f"[gpu] help tiles {help_tiles} cap {st['controller_cap']} local {st['xcd_local']}",
+              flush=True)
+        assert st["controller_cap"] == 8
+        assert help_tiles >= 1
+    finally:
+        mk.set_num_workgroups(0)
+        mk.set_controller_cap(0)
 
 
 @pytest.mark.slow

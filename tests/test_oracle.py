@@ -228,6 +228,23 @@ def test_controller_keeps_one_compute_workgroup_per_partition():
     assert oracle.controller_update(256, 100, 0, 0, 0, 0, current=300, keep=8) == 248
 
 
+def test_controller_cap_bounds_reducers_while_compute_remains():
+    # hand-worked: 256 * (300*30) / (100*10 + 300*30) = 256 * 9000/10000 = 230.4 -> 230
+    assert oracle.controller_target(256, 300, 30, 100, 10, current=2) == 230
+    assert oracle.controller_target(256, 300, 30, 100, 10, current=2, cap=128) == 128
+    # the tighter of B - keep and the cap wins
+    assert oracle.controller_target(256, 300, 30, 100, 10, current=2, keep=200, cap=128) == 56
+    # a value under the cap is untouched; so is the drain target B
+    assert oracle.controller_target(256, 100, 10, 300, 30, current=2, cap=128) == 26
+    assert oracle.controller_target(256, 300, 30, 0, 10, current=2, cap=128) == 256
+    # a cap below the floor wins over the floor (liveness of compute first)
+    assert oracle.controller_target(256, 1, 1, 10 ** 6, 10 ** 6, current=2, floor=8, cap=4) == 4
+    # without samples the current target is clamped to the cap as well
+    assert oracle.controller_update(256, 100, 0, 0, 0, 0, current=200, cap=128) == 128
+    with pytest.raises(ValueError):
+        oracle.controller_target(256, 1, 1, 1, 1, current=2, cap=0)
+
+
 def test_controller_update_keeps_target_without_samples():
     assert oracle.controller_update(256, 100, 0, 0, 0, 0, current=9) == 9
     assert oracle.controller_update(256, 100, 5, 0, 500, 0, current=9) == 9
@@ -362,6 +379,23 @@ def test_check_state_role_log_in_adaptive_mode():
     maps["reduce_owner"][:] = 1 | (3 << 16)       # index 1 < target 3: reduce ok
     assert oracle.check_state(maps, T, 4, 1, 1, B, "adaptive", 2) == []
     maps["reduce_owner"][4] = 6 | (3 << 16)       # reduced while in the compute role
+    assert oracle.check_state(maps, T, 4, 1, 1, B, "adaptive", 2)
+
+
+def test_check_state_help_mark():
+    T, B = 8, 8
+    maps = _good_maps(T, 4, 1, 1, B, 2)
+    maps["compute_owner"][:] = 5 | (3 << 16)
+    maps["reduce_owner"][:] = 1 | (3 << 16)
+    # workgroup 1 (reduce role under target 3) computed tile 2 while its
+    # reduce ticket was not ready: legal only with the help mark, only in
+    # adaptive mode, and never on a reduce owner
+    maps["compute_owner"][2] = 1 | (3 << 16)
+    assert oracle.check_state(maps, T, 4, 1, 1, B, "adaptive", 2)
+    maps["compute_owner"][2] = oracle.OWNER_HELP | 1 | (3 << 16)
+    assert oracle.check_state(maps, T, 4, 1, 1, B, "adaptive", 2) == []
+    assert oracle.check_state(maps, T, 4, 1, 1, B, "static", 2)
+    maps["reduce_owner"][3] = oracle.OWNER_HELP | 1 | (3 << 16)
     assert oracle.check_state(maps, T, 4, 1, 1, B, "adaptive", 2)
 
 
