@@ -991,32 +991,62 @@ __device__ uint32_t controller_step(const FusedArgs &a, Live *L, uint32_t wg, Sc
 }
 
 // The last workgroup out: copy the control block to the snapshot and restore
-// the initial values for the next launch.
+// the initial values for the next launch.  Every field is loaded before the
+// first store, so the device-scope loads are in flight together; the snapshot
+// may alias nothing here, but the compiler cannot know that, and interleaved
+// load/store pairs serialised into one round trip per field (about 10 us).
 __device__ void finish_launch(const FusedArgs &a, Live *L) {
-    Live *S = a.ws.snap;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    uint32_t cc[kMaxXcd], rc[kMaxXcd];
+#pragma unroll
+    for (int x = 0; x < kMaxXcd; ++x) {
+        cc[x] = ld_relaxed(&L->compute_claim[x].v);
+        rc[x] = ld_relaxed(&L->reduce_claim[x].v);
+    }
     const uint32_t raw = ld_relaxed(&L->target_ns.v);
-    for (int x = 0; x < kMaxXcd; ++x) S->compute_claim[x].v = ld_relaxed(&L->compute_claim[x].v);
-    for (int x = 0; x < kMaxXcd; ++x) S->reduce_claim[x].v = ld_relaxed(&L->reduce_claim[x].v);
-    S->exit_count = ld_relaxed(&L->exit_count);
-    S->target_ns.v = raw;
-    S->role_switches = ld_relaxed(&L->role_switches);
-    S->chunks_released.v = ld_relaxed(&L->chunks_released.v);
-    S->violations = ld_relaxed(&L->violations);
-    S->error = ld_relaxed(&L->error);
-    S->ns_min = ld_relaxed(&L->ns_min);
-    S->ns_max = ld_relaxed(&L->ns_max);
-    S->trace_len = ld_relaxed(&L->trace_len);
-    S->ns_final = a.mode == kAdaptive ? (raw ? raw : (uint32_t)a.ns_init) : (uint32_t)a.ns_init;
-    S->role_compute.v = ld_relaxed(&L->role_compute.v);
-    S->role_reduce.v = ld_relaxed(&L->role_reduce.v);
-    S->t_start = ld_relaxed(&L->t_start);
-    S->t_end = ld_relaxed(&L->t_end);
-    S->r_start = ld_relaxed(&L->r_start);
-    S->r_end = ld_relaxed(&L->r_end);
+    const uint32_t exits = ld_relaxed(&L->exit_count);
+    const uint32_t switches = ld_relaxed(&L->role_switches);
+    const uint32_t released = ld_relaxed(&L->chunks_released.v);
+    const uint32_t violations = ld_relaxed(&L->violations);
+    const uint32_t error = ld_relaxed(&L->error);
+    const uint32_t ns_min = ld_relaxed(&L->ns_min);
+    const uint32_t ns_max = ld_relaxed(&L->ns_max);
+    const uint32_t trace_len = ld_relaxed(&L->trace_len);
+    const uint64_t role_c = ld_relaxed(&L->role_compute.v);
+    const uint64_t role_r = ld_relaxed(&L->role_reduce.v);
+    const uint64_t t_start = ld_relaxed(&L->t_start);
+    const uint64_t t_end = ld_relaxed(&L->t_end);
+    const uint64_t r_start = ld_relaxed(&L->r_start);
+    const uint64_t r_end = ld_relaxed(&L->r_end);
 
-    for (int x = 0; x < kMaxXcd; ++x) st_relaxed(&L->compute_claim[x].v, 0u);
-    for (int x = 0; x < kMaxXcd; ++x) st_relaxed(&L->reduce_claim[x].v, 0u);
+    Live *S = a.ws.snap;
+#pragma unroll
+    for (int x = 0; x < kMaxXcd; ++x) {
+        S->compute_claim[x].v = cc[x];
+        S->reduce_claim[x].v = rc[x];
+    }
+    S->exit_count = exits;
+    S->target_ns.v = raw;
+    S->role_switches = switches;
+    S->chunks_released.v = released;
+    S->violations = violations;
+    S->error = error;
+    S->ns_min = ns_min;
+    S->ns_max = ns_max;
+    S->trace_len = trace_len;
+    S->ns_final = a.mode == kAdaptive ? (raw ? raw : (uint32_t)a.ns_init) : (uint32_t)a.ns_init;
+    S->role_compute.v = role_c;
+    S->role_reduce.v = role_r;
+    S->t_start = t_start;
+    S->t_end = t_end;
+    S->r_start = r_start;
+    S->r_end = r_end;
+
+#pragma unroll
+    for (int x = 0; x < kMaxXcd; ++x) {
+        st_relaxed(&L->compute_claim[x].v, 0u);
+        st_relaxed(&L->reduce_claim[x].v, 0u);
+    }
     st_relaxed(&L->target_ns.v, 0u);
     st_relaxed(&L->role_switches, 0u);
     st_relaxed(&L->chunks_released.v, 0u);
