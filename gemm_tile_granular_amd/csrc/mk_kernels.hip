@@ -79,6 +79,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t scalar_rsrc(const void *p) {
 // (s_waitcnt vmcnt(0); expcnt and lgkmcnt left unconstrained).
 __device__ __forceinline__ void drain_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// A uniform value made opaque to the optimiser where it is taken: address
+// arithmetic on it is redone per task instead of being hoisted out of a
+// persistent loop, where its results would occupy registers across every task
+// of both roles (in the fused kernel that pushed VGPRs into scratch, and each
+// scratch reload inside the reduce pipeline drained all loads in flight).
+__device__ __forceinline__ int64_t opaque(int64_t v) {
+    asm volatile("" : "+s"(v));
+    return v;
+}
+
 // ---------------------------------------------------------------------------
 // clocks and atomics
 // ---------------------------------------------------------------------------
@@ -1254,6 +1264,7 @@ void fused_gemm_reduce_kernel(
         d.tile = __builtin_amdgcn_readfirstlane(sh_dec.tile);
         d.ns_seen = __builtin_amdgcn_readfirstlane(sh_dec.ns_seen);
         if (d.role == kRoleExit) break;
+        const int64_t Mp = opaque(a.M), Np = opaque(a.N), Kp = opaque(a.K);
         // tiles [t0, t0 + nt) of block d.tile
         const uint32_t t0 = bk.first_tile(d.tile);
         const uint32_t nt = bk.count(d.tile);
@@ -1273,14 +1284,14 @@ void fused_gemm_reduce_kernel(
             }
         };
         if (d.role == kRoleCompute) {
-            G::block(ln, a.A, a.B, a.C, a.M, a.N, a.K, (int64_t)ti * TM, (int64_t)tj * TN, lds,
+            G::block(ln, a.A, a.B, a.C, Mp, Np, Kp, (int64_t)ti * TM, (int64_t)tj * TN, lds,
                      [&] { work_done(kRoleCompute); });
         } else {
             // thread 0 saw the flag before the barrier; the partial is read
             // with device-coherent loads, after it
             if (a.P > 0)
                 reduce_tile<TM, TPB * TN, G::NT, H::kPartialLoad, H::kResultStore>(
-                    a.peers, a.C, a.M, a.N, a.P, (int64_t)ti * TM, (int64_t)tj * TN);
+                    a.peers, a.C, Mp, Np, a.P, (int64_t)ti * TM, (int64_t)tj * TN);
             work_done(kRoleReduce);
         }
         if (tid == 0) {
@@ -1356,7 +1367,8 @@ void gemm_kernel(GemmArgs a) {
                                 chunk_blocks((uint32_t)a.tpc, TPB), (uint32_t)a.group_m);
     for (uint32_t q = blockIdx.x; q < bk.TB; q += gridDim.x) {
         const uint32_t t0 = bk.first_tile(pt.ticket(q));
-        G::block(ln, a.A, a.B, a.C, a.M, a.N, a.K, (int64_t)(t0 / (uint32_t)a.tiles_n) * TM,
+        const int64_t Mp = opaque(a.M), Np = opaque(a.N), Kp = opaque(a.K);
+        G::block(ln, a.A, a.B, a.C, Mp, Np, Kp, (int64_t)(t0 / (uint32_t)a.tiles_n) * TM,
                  (int64_t)(t0 % (uint32_t)a.tiles_n) * TN, lds, [] {});
     }
 }
