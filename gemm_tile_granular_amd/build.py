@@ -13,10 +13,15 @@ LIB = os.path.join(HERE, "libmk.so")
 SOURCES = [os.path.join(CSRC, "mk_kernels.hip"), os.path.join(CSRC, "mk_api.hip")]
 HEADERS = [os.path.join(CSRC, "mk_internal.hpp"), os.path.join(ROOT, "include", "mk.h")]
 
-# Packed fp32 instructions are switched off for all device code.
+# Packed fp32 instructions are switched off for all device code.  LLVM's
+# atomic optimizer is off too: every atomic here is issued by one lane, and the
+# optimizer's wave-level rewrite reads each returned value back at once
+# (readfirstlane), which waits for every bookkeeping round trip in turn instead
+# of letting a task's atomics overlap one another and its stores.
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -478,6 +478,11 @@ struct Gemm {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[fm][fn][i] = 0.0f;
 
+        // Nothing of the caller's may still be in flight here: a returned
+        // value the compiler has not yet waited for would make it wait for
+        // every outstanding load (vmcnt(0)) inside the slab loop, draining
+        // the operand ring each slab.
+        drain_vmem();
         const int S = (int)((K + KB - 1) / KB);
         const int pre = S < NS ? S : NS;
         for (int s = 0; s < pre; ++s)
