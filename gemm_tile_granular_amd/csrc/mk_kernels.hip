@@ -707,10 +707,11 @@ struct Decision {
 constexpr uint32_t kHelp = 1u << 15;   // bit 31 of the owner word
 
 // Compute tasks are blocks of tpb adjacent tiles of one tile row (a ragged
-// last block holds fewer).  A reduce task takes the same block once every
-// tile of it is published: the tiles become ready together, and the wider
-// region streams from HBM in longer contiguous runs.
+// last block holds fewer): a wider block needs fewer operand bytes per flop.
+// A reduce task is one tile, the unit the pages reduce; the shorter task
+// lets every workgroup share the last of the reduce work.
 constexpr int kMaxTpb = 2;   // largest tiles-per-block of any tile configuration
+constexpr uint32_t kNoTile = 0xFFFFFFFFu;
 
 struct Blocks {
     uint32_t tpb;       // tiles per block
@@ -735,6 +736,21 @@ __device__ __forceinline__ Blocks make_blocks(uint32_t tpb, uint32_t tiles_m, ui
     return k;
 }
 
+// Reduce tickets follow the blocks' claim order tile by tile: ticket q is tile
+// q mod tpb of the (q / tpb)-th block (of the workgroup's partition when tiles
+// stay on their XCD, else of the global order).  A ticket past a ragged
+// block's last tile is empty (kNoTile).
+__device__ __forceinline__ uint32_t ticket_count(bool local, const Parts &pt, const Blocks &bk,
+                                                 uint32_t home) {
+    return (local ? pt.size(home) : bk.TB) * bk.tpb;
+}
+__device__ __forceinline__ uint32_t ticket_tile(bool local, const Parts &pt, const Blocks &bk,
+                                                uint32_t home, uint32_t q) {
+    const uint32_t qb = q / bk.tpb, j = q % bk.tpb;
+    const uint32_t b = local ? pt.tile(home, qb) : pt.ticket(qb);
+    return j < bk.count(b) ? bk.first_tile(b) + j : kNoTile;
+}
+
 // chunk size in blocks for the claim order (1 when blocks do not divide chunks)
 __device__ __forceinline__ uint32_t chunk_blocks(uint32_t tpc, uint32_t tpb) {
     return (tpc % tpb) == 0 ? tpc / tpb : 1u;
@@ -757,8 +773,8 @@ struct Sched {
     // taken at the end of the previous task, while its stores drained:
     bool early_claim;          // a compute claim on partition early_x returned early_i
     uint32_t early_x, early_i, early_ns;
-    bool early_flag;           // the readiness flags of the pending ticket's block
-    uint32_t early_flag_value; // their common value (0 if they differ)
+    bool early_flag;           // the readiness flag of the pending ticket's tile
+    uint32_t early_flag_value; // its value
     uint32_t trace_n;          // workgroup 0: target changes it has recorded
 };
 
@@ -781,14 +797,6 @@ __device__ bool wait_ready(const FusedArgs &a, Live *L, uint32_t t) {
     }
 }
 
-// Wait until every tile of block b is published (tiles after the first are
-// checked once the first is: one compute task stores their flags together).
-__device__ bool wait_block(const FusedArgs &a, const Blocks &bk, Live *L, uint32_t b) {
-    const uint32_t t0 = bk.first_tile(b), n = bk.count(b);
-    for (uint32_t k = 0; k < n; ++k)
-        if (!wait_ready(a, L, t0 + k)) return false;
-    return true;
-}
 
 // Thread 0: claim a compute block, from the workgroup's own partition first,
 // then (unless tiles stay on their XCD) the others.  False once every
@@ -812,13 +820,9 @@ __device__ __forceinline__ bool claim_compute(const FusedArgs &a, const Parts &p
     return false;
 }
 
-// Every tile of block b carries this launch's epoch (one compute task stores
-// their flags together, so the first and the last decide).
-__device__ __forceinline__ bool block_ready(const FusedArgs &a, const Blocks &bk, uint32_t b) {
-    const uint32_t t0 = bk.first_tile(b), t1 = t0 + bk.count(b) - 1;
-    const uint32_t f0 = ld_relaxed(&a.ws.tile_flag[t0]);
-    const uint32_t f1 = ld_relaxed(&a.ws.tile_flag[t1]);
-    return f0 == a.epoch && f1 == a.epoch;
+// Tile t carries this launch's epoch (one read, no wait).
+__device__ __forceinline__ bool tile_ready(const FusedArgs &a, uint32_t t) {
+    return ld_relaxed(&a.ws.tile_flag[t]) == a.epoch;
 }
 
 // Thread 0 only: the next task.  Roles follow the workgroup index against the
@@ -837,11 +841,11 @@ __device__ Decision next_task(const FusedArgs &a, const Parts &pt, const Blocks 
     if (a.mode == kDeterministic) {
         const uint32_t ns = (uint32_t)a.ns_init;
         if (wg < ns) {
-            const uint32_t b = wg + s.det_i * ns;
-            if (b >= bk.TB) return {kRoleExit, 0, ns};
-            if (!wait_block(a, bk, L, b)) return {kRoleExit, 0, ns};
+            const uint32_t t = wg + s.det_i * ns;
+            if (t >= a.T) return {kRoleExit, 0, ns};
+            if (!wait_ready(a, L, t)) return {kRoleExit, 0, ns};
             ++s.det_i;
-            return {kRoleReduce, b, ns};
+            return {kRoleReduce, t, ns};
         }
         const uint32_t b = (wg - ns) + s.det_i * (B - ns);
         if (b >= bk.TB) return {kRoleExit, 0, ns};
@@ -862,20 +866,21 @@ __device__ Decision next_task(const FusedArgs &a, const Parts &pt, const Blocks 
             const bool seen = s.early_flag && s.early_flag_value == a.epoch;
             s.early_flag = false;
             const uint32_t home = wg % pt.nx;
-            if (a.local ? q < pt.size(home) : q < bk.TB) {
-                const uint32_t b = a.local ? pt.tile(home, q) : pt.ticket(q);
+            if (q < ticket_count(a.local, pt, bk, home)) {
+                const uint32_t t = ticket_tile(a.local, pt, bk, home, q);
+                if (t == kNoTile) continue;     // empty ticket: take another
                 if (!seen) {
                     uint32_t cb;
-                    if (a.mode == kAdaptive && !s.compute_exhausted && !block_ready(a, bk, b) &&
+                    if (a.mode == kAdaptive && !s.compute_exhausted && !tile_ready(a, t) &&
                         claim_compute(a, pt, L, wg, s, cb)) {
                         s.pending_role = kRoleReduce;
                         s.pending_q = q;
                         s.pending_ns = ns_seen;
                         return {kRoleCompute, cb, s.target | kHelp};
                     }
-                    if (!wait_block(a, bk, L, b)) return {kRoleExit, 0, ns_seen};
+                    if (!wait_ready(a, L, t)) return {kRoleExit, 0, ns_seen};
                 }
-                return {kRoleReduce, b, ns_seen};
+                return {kRoleReduce, t, ns_seen};
             }
             s.reduce_exhausted = true;
             continue;
@@ -922,30 +927,29 @@ __device__ __forceinline__ void prefetch_claim(const FusedArgs &a, const Parts &
 // stores are issued (kept in registers meanwhile, not in the LDS-resident
 // scheduling state, so issuing them does not wait for their return).
 struct Early {
-    int kind;           // 0: none, 1: compute claim on partition x, 2: readiness flags
+    int kind;           // 0: none, 1: compute claim on partition x, 2: readiness flag
     uint32_t x, ns;
-    uint32_t v0, v1;
+    uint32_t v0;
 };
 
 // Thread 0: start the round trips the next boundary needs.  A compute
 // workgroup still in the compute role (under the target of its previous
-// controller step) claims its next block; a reducer holding a ticket reads
-// that block's readiness flags.
+// controller step) claims its next block; a workgroup holding a reduce
+// ticket reads that tile's readiness flag.
 __device__ __forceinline__ Early early_issue(const FusedArgs &a, const Parts &pt, const Blocks &bk,
                                              Live *L, uint32_t wg, const Sched &s) {
     Early e;
     e.kind = 0;
-    e.x = e.ns = e.v0 = e.v1 = 0;
+    e.x = e.ns = e.v0 = 0;
     if (a.mode == kDeterministic) return e;
     const uint32_t home = wg % pt.nx;
     if (s.pending_role == kRoleReduce) {
-        if (a.local ? s.pending_q < pt.size(home) : s.pending_q < bk.TB) {
-            // the block is ready when its first and last tiles are
-            const uint32_t b = a.local ? pt.tile(home, s.pending_q) : pt.ticket(s.pending_q);
-            const uint32_t t0 = bk.first_tile(b), t1 = t0 + bk.count(b) - 1;
-            e.kind = 2;
-            e.v0 = ld_relaxed(&a.ws.tile_flag[t0]);
-            e.v1 = ld_relaxed(&a.ws.tile_flag[t1]);
+        if (s.pending_q < ticket_count(a.local, pt, bk, home)) {
+            const uint32_t t = ticket_tile(a.local, pt, bk, home, s.pending_q);
+            if (t != kNoTile) {
+                e.kind = 2;
+                e.v0 = ld_relaxed(&a.ws.tile_flag[t]);
+            }
         }
         return e;
     }
@@ -974,7 +978,7 @@ __device__ __forceinline__ void early_finish(Sched &s, const Early &e) {
         s.early_i = e.v0;
     } else if (e.kind == 2) {
         s.early_flag = true;
-        s.early_flag_value = e.v0 == e.v1 ? e.v0 : 0u;
+        s.early_flag_value = e.v0;
     }
 }
 
@@ -1270,9 +1274,10 @@ void fused_gemm_reduce_kernel(
         d.ns_seen = __builtin_amdgcn_readfirstlane(sh_dec.ns_seen);
         if (d.role == kRoleExit) break;
         const int64_t Mp = opaque(a.M), Np = opaque(a.N), Kp = opaque(a.K);
-        // tiles [t0, t0 + nt) of block d.tile
-        const uint32_t t0 = bk.first_tile(d.tile);
-        const uint32_t nt = bk.count(d.tile);
+        // tiles [t0, t0 + nt): block d.tile (compute) or tile d.tile (reduce)
+        const bool computing = d.role == kRoleCompute;
+        const uint32_t t0 = computing ? bk.first_tile(d.tile) : d.tile;
+        const uint32_t nt = computing ? bk.count(d.tile) : 1u;
         const int ti = (int)(t0 / (uint32_t)a.tiles_n);
         const int tj = (int)(t0 % (uint32_t)a.tiles_n);
 
@@ -1295,7 +1300,7 @@ void fused_gemm_reduce_kernel(
             // thread 0 saw the flag before the barrier; the partial is read
             // with device-coherent loads, after it
             if (a.P > 0)
-                reduce_tile<TM, TPB * TN, G::NT, H::kPartialLoad, H::kResultStore>(
+                reduce_tile<TM, TN, G::NT, H::kPartialLoad, H::kResultStore>(
                     a.peers, a.C, Mp, Np, a.P, (int64_t)ti * TM, (int64_t)tj * TN);
             work_done(kRoleReduce);
         }

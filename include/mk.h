@@ -68,10 +68,10 @@ typedef enum {
     MK_PART_ADAPTIVE = 0,
     /* Fixed count of reduce workgroups; tasks are claimed dynamically.     */
     MK_PART_STATIC = 1,
-    /* Fixed count; workgroup w < n reduces tasks b = w (mod n), workgroup
-     * w >= n computes tasks b = w - n (mod B - n), each in increasing order
-     * (a task of either role is the block of mk_stats.tiles_per_task
-     * adjacent tiles of one tile row; tasks are numbered row by row).      */
+    /* Fixed count; workgroup w < n reduces tiles t = w (mod n), workgroup
+     * w >= n computes blocks b = w - n (mod B - n), each in increasing
+     * order (a block is mk_stats.tiles_per_task adjacent tiles of one tile
+     * row; blocks and tiles are numbered row by row).                     */
     MK_PART_STATIC_DETERMINISTIC = 2
 } mk_part_mode;
 
@@ -97,8 +97,8 @@ typedef enum {
  *              one of 64x64, 128x128, 256x128.  A compute task produces a
  *              block of adjacent tiles of one tile row (two for 128x128 and
  *              256x128, one for 64x64; see mk_stats.tiles_per_task) and
- *              publishes each tile's flag; a reduce task takes the same block
- *              once all its tiles are published.
+ *              publishes each tile's flag; a reduce task takes one tile once
+ *              it is published.
  *   tiles_per_chunk  tiles per chunk (1..64; 4 in the method's
  *              GEMM+AllReduce).  Chunk c holds tiles [c*tpc, (c+1)*tpc) in
  *              row-major tile order; the last chunk may be short.
@@ -196,13 +196,14 @@ typedef struct mk_stats {
     uint32_t n_reduce_min_seen;   /* over controller updates and the initial    */
     uint32_t n_reduce_max_seen;
     uint32_t role_switches;       /* workgroups changing role between tasks      */
-    uint32_t compute_tasks;       /* compute tasks finished (== T)               */
-    uint32_t reduce_tasks;        /* reduce tasks finished (== T)                */
+    uint32_t compute_tasks;       /* tiles computed (== T)                       */
+    uint32_t reduce_tasks;        /* tiles reduced (== T)                        */
     uint32_t chunks_released;     /* chunks whose last tile was reduced (== Ch)  */
     uint32_t invariant_violations;/* flag/counter mismatches seen on the device  */
     uint32_t ns_trace_len;        /* entries in the controller trace (the target
                                      changes made by workgroup 0's own steps)  */
-    uint32_t tiles_per_task;      /* output tiles of one compute/reduce task     */
+    uint32_t tiles_per_task;      /* output tiles of one compute task (a reduce
+                                     task is always one tile)                  */
     uint64_t sum_cycles_compute;  /* shader-clock cycles over compute tasks      */
     uint64_t sum_cycles_reduce;   /* shader-clock cycles over reduce tasks       */
     uint64_t kernel_ticks_start;  /* first workgroup start (constant clock)      */

@@ -299,12 +299,13 @@ def deterministic_owners(T: int, B: int, n_reduce: int, tiles_n: Optional[int] =
     """Owner maps of the deterministic static schedule.
 
     Workgroups [0, n_reduce) reduce and the rest compute (roles by workgroup
-    index).  A task of either role covers the tiles of one compute task;
-    each workgroup takes its tasks round-robin in increasing task order, and
-    every tile of a task has that task's owner.
+    index).  A compute task covers the tiles of one block (`tiles_per_task`
+    adjacent tiles of a tile row); a reduce task is one tile, the unit the
+    pages reduce.  Each workgroup takes its tasks round-robin in increasing
+    task order, and every tile of a compute task has that task's owner.
     """
     task = compute_task_of_tile(T, tiles_n, tiles_per_task)
-    return n_reduce + task % (B - n_reduce), task % n_reduce
+    return n_reduce + task % (B - n_reduce), np.arange(T, dtype=np.int64) % n_reduce
 
 
 OWNER_WG_MASK = 0xFFFF
@@ -358,13 +359,13 @@ def check_state(maps: Dict[str, np.ndarray], T: int, tiles_per_chunk: int, epoch
             i = int(np.nonzero(ro_wg != dr)[0][0])
             bad.append(f"reduce_owner[{i}] = {int(ro_wg[i])}, expected {int(dr[i])}")
     if tiles_per_task > 1 and T:
+        # reduce tasks are single tiles; a compute task's tiles share one owner
         task = compute_task_of_tile(T, tiles_n, tiles_per_task)
-        for name, own in (("compute", co), ("reduce", ro)):
-            first = np.zeros(int(task.max()) + 1, dtype=np.int64)
-            first[task[::-1]] = own[::-1]
-            if np.any(own != first[task]):
-                i = int(np.nonzero(own != first[task])[0][0])
-                bad.append(f"tile {i}: {name} owner differs from the rest of its task")
+        first = np.zeros(int(task.max()) + 1, dtype=np.int64)
+        first[task[::-1]] = co[::-1]
+        if np.any(co != first[task]):
+            i = int(np.nonzero(co != first[task])[0][0])
+            bad.append(f"tile {i}: compute owner differs from the rest of its task")
     if np.any(co_wg >= B):
         bad.append("compute owner outside [0, B)")
     if np.any(ro_wg >= B):

@@ -322,9 +322,8 @@ def test_deterministic_owners_with_blocks():
     # tasks (0..11, three per row) go round-robin to workgroups 2, 3, 4
     want = [2, 2, 3, 3, 4, 4, 2, 2, 3, 3, 4, 4, 2, 2, 3, 3, 4, 4, 2, 2, 3, 3, 4, 4]
     np.testing.assert_array_equal(co, want)
-    # reduce tasks are the same blocks, round-robin over workgroups 0, 1
-    np.testing.assert_array_equal(ro, [0, 0, 1, 1, 0, 0, 1, 1, 0, 0, 1, 1,
-                                       0, 0, 1, 1, 0, 0, 1, 1, 0, 0, 1, 1])
+    # reduce tasks are single tiles, round-robin over workgroups 0, 1
+    np.testing.assert_array_equal(ro, [0, 1] * 12)
 
 
 def test_check_state_rejects_split_task_owner():
@@ -339,9 +338,12 @@ def test_check_state_rejects_split_task_owner():
     split = {k: v.copy() for k, v in maps.items()}
     split["compute_owner"][5] = (ns << 16) | 7    # the other tile of its task stays with 4
     assert oracle.check_state(split, T, 4, 1, 1, B, "static", ns, tiles_n, 2)
+    # reduce tasks are single tiles: in a dynamic schedule any reducer may take
+    # tile 3 whatever took tile 2; the deterministic schedule fixes which
     split = {k: v.copy() for k, v in maps.items()}
-    split["reduce_owner"][3] = (ns << 16) | 0     # tile 2 of the same task stays with 1
-    assert oracle.check_state(split, T, 4, 1, 1, B, "static", ns, tiles_n, 2)
+    split["reduce_owner"][3] = (ns << 16) | (1 - int(ro[3]))
+    assert oracle.check_state(split, T, 4, 1, 1, B, "static", ns, tiles_n, 2) == []
+    assert oracle.check_state(split, T, 4, 1, 1, B, "deterministic", ns, tiles_n, 2)
 
 
 def _good_maps(T, tpc, epoch, calls, B, ns):
