@@ -54,6 +54,11 @@ SHAPES = [
     (1000, 1000, 1000, 7, 128, 128, 4),  # 64 tiles, 16 chunks
     (130, 520, 8, 1, 64, 64, 1),         # K = 8: a single partial slab
     (97, 1024, 328, 9, 64, 64, 5),       # odd peer count (not a multiple of 4)
+    # 9 tile rows (XCD-local partitions, one holding two rows) and 3 tile
+    # columns: the two-tile blocks of each row end in a one-tile block, whose
+    # second reduce ticket is empty
+    (1100, 264, 200, 3, 128, 128, 4),
+    (2100, 264, 136, 2, 256, 128, 4),
 ]
 
 
