@@ -178,7 +178,7 @@ def set_controller_floor(floor: int) -> None:
 
 
 def set_controller_cap(cap: int) -> None:
-    """Most reduce workgroups the adaptive controller sets while compute remains (0: B/2)."""
+    """Most reduce workgroups the adaptive controller sets while compute remains (0: 5B/8)."""
     _check(lib.mk_set_controller_cap(int(cap)))
 
 

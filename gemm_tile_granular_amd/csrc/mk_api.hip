@@ -39,7 +39,7 @@ struct Settings {
     int mode = MK_PART_ADAPTIVE;
     int n_reduce = 0;
     int floor = 2;
-    int cap = 0;              // 0: half the workgroups
+    int cap = 0;              // 0: five eighths of the workgroups
     int num_wg = 0;
     uint64_t timeout_us = 2000000;
     int64_t skip_publish = -1;
@@ -313,16 +313,17 @@ int run(bool fused, const void *A, const void *B, const float *peers, int num_pe
                        set.mode != MK_PART_STATIC_DETERMINISTIC &&
                        (set.mode == MK_PART_ADAPTIVE || (ns_init >= nxcd && ns_init <= nwg - nxcd));
     const int keep = local ? nxcd : 1;
-    // most reducers while compute remains: half the workgroups by default
-    // (about where the reduce role saturates HBM: a CU streams 40-57 GB/s)
-    int cap = set.cap ? set.cap : nwg / 2;
+    // most reducers while compute remains: five eighths of the workgroups by
+    // default (the reduce role saturates HBM with about half to five eighths
+    // of the CUs: one CU streams 40-57 GB/s)
+    int cap = set.cap ? set.cap : (5 * nwg) / 8;
     if (cap > nwg - keep) cap = nwg - keep;
     if (cap < 1) cap = 1;
     if (set.mode == MK_PART_ADAPTIVE) {
-        // default start: the cap.  Reducers with nothing ready yet compute,
-        // so a high start costs no idle workgroups, and the reduce role is
-        // staffed the moment the first tiles are published.
-        if (ns_init == 0) ns_init = cap;
+        // default start: half the workgroups.  Reducers with nothing ready
+        // yet compute, so a high start costs no idle workgroups, and the
+        // reduce role is staffed the moment the first tiles are published.
+        if (ns_init == 0) ns_init = nwg / 2;
         if (ns_init > cap) ns_init = cap;
         if (ns_init < 1) ns_init = 1;
     }

@@ -129,9 +129,9 @@ int mk_gemm_reduce_unfused(const void *A, const void *B, const float *peers, int
  *   mode       mk_part_mode.
  *   n_reduce   STATIC*: reduce-workgroup count, must lie in [1, B-1] at launch
  *              time (B = workgroups of the launch).  ADAPTIVE: initial count,
- *              at most the controller cap (0 selects the cap, B/2 by default;
- *              reducers with no tile ready compute meanwhile, so a high start
- *              leaves no workgroup idle).
+ *              at most the controller cap (0 selects B/2; reducers with no
+ *              tile ready compute meanwhile, so a high start leaves no
+ *              workgroup idle).
  * Errors: MK_ERR_INVALID_ARG for an unknown mode or negative n_reduce.
  */
 int mk_set_partition(int mode, int n_reduce);
@@ -144,10 +144,10 @@ int mk_set_controller_floor(int floor);
 
 /*
  * mk_set_controller_cap -- largest reduce count the adaptive controller may
- * choose while compute remains.  0 (default) = B/2: on MI355X the reduce
- * role saturates HBM with about half the CUs (one CU streams 40-57 GB/s),
- * and more reducers only lengthen every reduce task while taking compute
- * units from the tiles they wait for.  Valid: 0..1024; at run time it is
+ * choose while compute remains.  0 (default) = 5B/8: on MI355X the reduce
+ * role saturates HBM with about half to five eighths of the CUs (one CU
+ * streams 40-57 GB/s), and more reducers only lengthen every reduce task
+ * while taking compute units from the tiles they wait for.  Valid: 0..1024; at run time it is
  * clamped to [1, B - keep_compute].  Also bounds the initial adaptive count.
  * Errors: MK_ERR_INVALID_ARG outside 0..1024.
  */
