@@ -1,7 +1,9 @@
 """Builds libmk.so (HIP, gfx950) in place next to this file."""
 from __future__ import annotations
 
+import json
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -33,15 +35,46 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+RESOURCES = LIB[:-3] + ".resources.json"
+_REMARK = re.compile(r"remark:\s+(Function Name|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|"
+                     r"Occupancy \[waves/SIMD\]|SGPRs Spill|VGPRs Spill|LDS Size \[bytes/block\]):"
+                     r"\s+(\S+)")
+
+
+def _resources(stderr: str) -> dict:
+    """Per-kernel register, scratch and occupancy figures from the compiler's
+    resource-usage remarks (device pass only)."""
+    out, cur = {}, None
+    for line in stderr.splitlines():
+        m = _REMARK.search(line)
+        if not m:
+            continue
+        key, val = m.group(1), m.group(2)
+        if key == "Function Name":
+            cur = out.setdefault(val, {})
+        elif cur is not None:
+            cur[key.split(" [")[0]] = int(val)
+    return out
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source into libmk.so; always recompiles."""
+    """Compile every source into libmk.so; always recompiles.  The kernels'
+    register and scratch use goes to libmk.resources.json next to it."""
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           "-o", tmp, *SOURCES]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-Rpass-analysis=kernel-resource-usage",
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp, *SOURCES]
     if verbose:
         print(" ".join(cmd), flush=True)
-    subprocess.check_call(cmd)
+    res = subprocess.run(cmd, stderr=subprocess.PIPE, text=True)
+    # pass the compiler's own diagnostics through, without the remarks
+    for line in res.stderr.splitlines():
+        if "-Rpass-analysis=kernel-resource-usage" not in line:
+            print(line, file=sys.stderr)
+    if res.returncode != 0:
+        raise subprocess.CalledProcessError(res.returncode, cmd)
     os.replace(tmp, LIB)
+    with open(RESOURCES, "w") as f:
+        json.dump(_resources(res.stderr), f, indent=1, sort_keys=True)
     return LIB
 
 

@@ -155,3 +155,29 @@ def test_binding_rejects_wrong_tensor_types(mk):
     a = torch.zeros(4, 8, dtype=torch.float32)
     with pytest.raises(ValueError):
         mk.gemm_reduce_local(a, a, None, a, 64, 64)
+
+
+def test_kernels_fit_their_register_and_lds_budget(mk):
+    """The compiler's resource report of the last build: the 128x128 fused
+    kernel and every plain GEMM keep all state in registers, the 256x128 fused
+    kernel (two blocks per CU, 256 registers a lane) spills only a bounded
+    amount, and no kernel asks for more LDS than a CU has (160 KiB)."""
+    import json
+    lib = os.path.join(ROOT, "gemm_tile_granular_amd", "libmk.so")
+    path = os.path.join(ROOT, "gemm_tile_granular_amd", "libmk.resources.json")
+    if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(lib):
+        pytest.skip("library built without a resource report")
+    with open(path) as f:
+        res = json.load(f)
+    fused = {k: v for k, v in res.items() if "fused_gemm_reduce_kernel" in k}
+    gemm = {k: v for k, v in res.items() if "gemm_kernel" in k and k not in fused}
+    assert len(fused) == 6 and len(gemm) == 3, sorted(res)
+    for name, r in res.items():
+        assert r["LDS Size"] <= 160 * 1024, name
+    for name, r in gemm.items():
+        assert r["ScratchSize"] == 0, (name, r)
+    for name, r in fused.items():
+        if "ILi256ELi128E" in name:
+            assert r["Occupancy"] == 2 and r["ScratchSize"] <= 128, (name, r)
+        else:
+            assert r["ScratchSize"] == 0, (name, r)
