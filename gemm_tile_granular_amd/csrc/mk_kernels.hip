@@ -308,6 +308,7 @@ struct Gemm {
     static_assert(BM % (A_ROWS * NWAVES) == 0 && KB % (B_ROWS * NWAVES) == 0, "load split");
     static_assert(STAGE < 65536, "in-slab offsets must fit the LDS immediate");
     static_assert(NS >= 2 && NS <= 4, "ring depth");
+    static_assert(NS >= 3, "a fill needs a ring slot beside the two being read");
 
     // XOR swizzles of 16-byte chunks (conflict-free operand reads, see above)
     static __device__ __forceinline__ int swz_a(int row) {
@@ -325,18 +326,18 @@ struct Gemm {
         uint32_t b_frag[FN];        // LDS offset of this lane's first B piece per fn
     };
 
-    // row and column (in elements) of the piece load i of this lane carries
-    static __device__ __forceinline__ int a_row(int i) {
-        return ((int)(threadIdx.x >> 6) * A_INST + i) * A_ROWS + (int)(threadIdx.x & 63) / A_CHUNKS;
+    // row and column (in elements) of the piece load i of thread t carries
+    static __device__ __forceinline__ int a_row(int i, int t = threadIdx.x) {
+        return ((t >> 6) * A_INST + i) * A_ROWS + (t & 63) / A_CHUNKS;
     }
-    static __device__ __forceinline__ int a_col(int i) {
-        return (((int)(threadIdx.x & 63) % A_CHUNKS) ^ swz_a(a_row(i))) * 8;
+    static __device__ __forceinline__ int a_col(int i, int t = threadIdx.x) {
+        return (((t & 63) % A_CHUNKS) ^ swz_a(a_row(i, t))) * 8;
     }
-    static __device__ __forceinline__ int b_row(int i) {
-        return ((int)(threadIdx.x >> 6) * B_INST + i) * B_ROWS + (int)(threadIdx.x & 63) / B_CHUNKS;
+    static __device__ __forceinline__ int b_row(int i, int t = threadIdx.x) {
+        return ((t >> 6) * B_INST + i) * B_ROWS + (t & 63) / B_CHUNKS;
     }
-    static __device__ __forceinline__ int b_col(int i) {
-        return (((int)(threadIdx.x & 63) % B_CHUNKS) ^ swz_b(b_row(i))) * 8;
+    static __device__ __forceinline__ int b_col(int i, int t = threadIdx.x) {
+        return (((t & 63) % B_CHUNKS) ^ swz_b(b_row(i, t))) * 8;
     }
 
     static __device__ __forceinline__ void init_lane(Lane &ln, int64_t N, int64_t K) {
@@ -376,18 +377,45 @@ struct Gemm {
 #pragma unroll
             for (int i = 0; i < B_INST; ++i) dma16(db, ln.b_dma[i], sb + i * 1024);
         } else {
-            // edge block or last K slab: out-of-range pieces read as zeros
+            // edge block or last K slab: out-of-range pieces read as zeros.
+            // The extents left are compared in 32 bits with the piece
+            // coordinates, recomputed here from a thread index the compiler
+            // cannot hoist: kept live across the task loop they would take
+            // registers the GEMM needs.
+            int t = threadIdx.x;
+            asm volatile("" : "+v"(t));
+            const int mr = (int)(M - m0 < BM ? M - m0 : BM), nr = (int)(N - n0 < BN ? N - n0 : BN);
+            const int kr = (int)(K - k0 < KB ? K - k0 : KB);
 #pragma unroll
             for (int i = 0; i < A_INST; ++i) {
-                const bool ok = m0 + a_row(i) < M && k0 + a_col(i) < K;
+                const bool ok = a_row(i, t) < mr && a_col(i, t) < kr;
                 dma16(da, ok ? ln.a_dma[i] : kOOB, sa + i * 1024);
             }
 #pragma unroll
             for (int i = 0; i < B_INST; ++i) {
-                const bool ok = k0 + b_row(i) < K && n0 + b_col(i) < N;
+                const bool ok = b_row(i, t) < kr && b_col(i, t) < nr;
                 dma16(db, ok ? ln.b_dma[i] : kOOB, sb + i * 1024);
             }
         }
+    }
+
+    // Loads [j0, j1) (the A pieces, then the B pieces) of a K slab that lies
+    // wholly inside A and B; j0 and j1 are constants once the caller's k-step
+    // loop is unrolled, so the loads sit between that k-step's MFMAs.
+    static __device__ __forceinline__ void issue_part(const Lane &ln, uint32_t slot, const uint16_t *A,
+                                                      const uint16_t *B, int64_t N, int64_t K,
+                                                      int64_t m0, int64_t n0, int64_t k0, int j0,
+                                                      int j1) {
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const uint32_t s0 = __builtin_amdgcn_readfirstlane(slot);
+        const uint32_t sa = s0 + wave * A_INST * 1024, sb = s0 + LDS_A + wave * B_INST * 1024;
+#pragma unroll
+        for (int i = 0; i < A_INST; ++i)
+            if (i >= j0 && i < j1) dma16(make_desc(A + m0 * K + k0), ln.a_dma[i], sa + i * 1024);
+#pragma unroll
+        for (int i = 0; i < B_INST; ++i)
+            if (A_INST + i >= j0 && A_INST + i < j1)
+                dma16(make_desc(B + k0 * N + n0), ln.b_dma[i], sb + i * 1024);
     }
 
     // this lane's MFMA operands for one 16-deep k-step
@@ -431,16 +459,27 @@ struct Gemm {
 
     // One K slab s whose k-step-0 operands are in f0.  Each k-step multiplies
     // from registers while the next k-step's operands come out of LDS.  Before
-    // the last k-step (when slab s+1 exists) the workgroup waits for slab s+1
-    // to land, and slab s+NS starts streaming into the slot slab s leaves free
-    // (slab s+NS has about NS-1 slab times to arrive); the last k-step then
-    // overlaps the reads of slab s+1's first operands, which end in f0.
-    template <bool kNext>
+    // the last k-step (when slab s+1 exists, kNext) the workgroup waits for
+    // slab s+1 to land; after that barrier no wave reads slab s any more.  The
+    // last k-step overlaps the reads of slab s+1's first operands, which end
+    // in f0.
+    //
+    // Blocks wholly inside A and B with K a multiple of KB (kFast) keep NS-1
+    // slabs ahead: the loads of slab s+NS-1 go into the slot slab s-1 left
+    // free, a share of them in each k-step of slab s but the last (kFill,
+    // while that slab exists), between the MFMAs.  One CU moves about 64
+    // bytes a clock from L2 into LDS, so a slab's loads take most of a slab's
+    // MFMA time; issued in one burst they would hold every wave at the load
+    // issue while the matrix cores idle.  Other blocks (edges, ragged K) keep
+    // NS slabs ahead: slab s+NS goes into slab s's slot in one burst right
+    // after the barrier, with range checks.
+    template <bool kNext, bool kFill, bool kFast>
     static __device__ __forceinline__ void slab(const Lane &ln, int s, int S, KFrag &f0, KFrag &f1,
                                                 f32x16 (&acc)[FM][FN], const uint16_t *A,
                                                 const uint16_t *B, int64_t M, int64_t N, int64_t K,
                                                 int64_t m0, int64_t n0, bool a_full, bool b_full,
                                                 lchar *lds, uint32_t base) {
+        static_assert(!kFill || (kFast && kNext), "fills belong to the steady state of fast blocks");
         const lchar *st = lds + (s % NS) * STAGE;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
@@ -448,11 +487,19 @@ struct Gemm {
             KFrag &nxt = (kk & 1) ? f0 : f1;
             if (kk + 1 < KK) {
                 kfrags(nxt, ln, st, kk + 1);
+                if constexpr (kFill)
+                    issue_part(ln, base + ((s + NS - 1) % NS) * STAGE, A, B, N, K, m0, n0,
+                               (int64_t)(s + NS - 1) * KB, kk * L / (KK - 1), (kk + 1) * L / (KK - 1));
             } else if (kNext) {
-                const int later = (S - 2 - s) < (NS - 2) ? (S - 2 - s) : (NS - 2);
-                wait_slabs(later);     // this wave's part of slab s+1 has landed
-                __syncthreads();       // every wave's has; slab s is no longer read
-                if (s + NS < S)
+                if constexpr (kFill) {
+                    wait_vmcnt<(NS - 2) * L>();   // slab s+1 has landed, s+2 .. s+NS-1 may not
+                } else {
+                    // slabs issued past s+1: NS-2, fewer near the end of K
+                    const int later = (S - 2 - s) < (NS - 2) ? (S - 2 - s) : (NS - 2);
+                    wait_slabs(later);
+                }
+                __syncthreads();   // every wave's part of slab s+1 has landed; slab s is free
+                if (!kFast && s + NS < S)
                     issue(ln, base + (s % NS) * STAGE, A, B, M, N, K, m0, n0, (int64_t)(s + NS) * KB,
                           a_full, b_full);
                 kfrags(nxt, ln, lds + ((s + 1) % NS) * STAGE, 0);
@@ -460,6 +507,31 @@ struct Gemm {
             kmfma(acc, cur);
             if (kk + 1 < KK || kNext) Interleave<0, NMF, NDS>::run();
         }
+    }
+
+    // the K loop of one block (see slab())
+    template <bool kFast>
+    static __device__ __forceinline__ void kloop(const Lane &ln, f32x16 (&acc)[FM][FN], const uint16_t *A,
+                                                 const uint16_t *B, int64_t M, int64_t N, int64_t K,
+                                                 int64_t m0, int64_t n0, bool a_full, bool b_full,
+                                                 lchar *lds, uint32_t base) {
+        const int S = (int)((K + KB - 1) / KB);
+        const int ahead = NS - (int)kFast;   // slabs the prologue issues
+        const int pre = S < ahead ? S : ahead;
+        for (int s = 0; s < pre; ++s)
+            issue(ln, base + s * STAGE, A, B, M, N, K, m0, n0, (int64_t)s * KB, a_full, b_full);
+        if (S <= 0) return;
+        wait_slabs(pre - 1);
+        __syncthreads();
+        KFrag f0, f1;
+        kfrags(f0, ln, lds, 0);
+        int s = 0;
+        if constexpr (kFast)
+            for (; s + NS - 1 < S; ++s)
+                slab<true, true, true>(ln, s, S, f0, f1, acc, A, B, M, N, K, m0, n0, a_full, b_full, lds, base);
+        for (; s + 1 < S; ++s)
+            slab<true, false, kFast>(ln, s, S, f0, f1, acc, A, B, M, N, K, m0, n0, a_full, b_full, lds, base);
+        slab<false, false, kFast>(ln, S - 1, S, f0, f1, acc, A, B, M, N, K, m0, n0, a_full, b_full, lds, base);
     }
 
     // Whole block at rows m0.., columns n0..: C = A[rows, :] . B[:, cols] in
@@ -483,38 +555,36 @@ struct Gemm {
         // every outstanding load (vmcnt(0)) inside the slab loop, draining
         // the operand ring each slab.
         drain_vmem();
-        const int S = (int)((K + KB - 1) / KB);
-        const int pre = S < NS ? S : NS;
-        for (int s = 0; s < pre; ++s)
-            issue(ln, base + s * STAGE, A, B, M, N, K, m0, n0, (int64_t)s * KB, a_full, b_full);
-        if (S > 0) {
-            wait_slabs(pre - 1);
-            __syncthreads();
-            KFrag f0, f1;
-            kfrags(f0, ln, lds, 0);
-            for (int s = 0; s + 1 < S; ++s)
-                slab<true>(ln, s, S, f0, f1, acc, A, B, M, N, K, m0, n0, a_full, b_full, lds, base);
-            slab<false>(ln, S - 1, S, f0, f1, acc, A, B, M, N, K, m0, n0, a_full, b_full, lds, base);
-        }
+        if (__builtin_amdgcn_readfirstlane((int)(a_full && b_full && K % KB == 0)))
+            kloop<true>(ln, acc, A, B, M, N, K, m0, n0, a_full, b_full, lds, base);
+        else
+            kloop<false>(ln, acc, A, B, M, N, K, m0, n0, a_full, b_full, lds, base);
         // the ring is refilled by the next block only after every wave is done with it
         __syncthreads();
 
         // epilogue: 16-byte stores; rows >= M and columns >= N masked by an
-        // out-of-range offset
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        // out-of-range offset.  Offsets and the extents left are 32-bit (a
+        // block lies within the buffer's 32-bit range), from a thread index
+        // the compiler cannot hoist: kept live across the task loop, the
+        // per-lane columns would take registers the K loop needs.
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, wave = tid >> 6;
         const int wm = wave / WGN, wn = wave % WGN;
+        const int mr = (int)(M - m0 < BM ? M - m0 : BM), nr = (int)(N - n0 < BN ? N - n0 : BN);
+        const uint32_t pitch = (uint32_t)N;
         const auto rc = scalar_rsrc(C + m0 * N + n0);
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
             const int r = wm * WTM + fm * 32 + (lane & 31);
-            const bool row_ok = m0 + r < M;
+            const bool row_ok = r < mr;
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int cc = wn * WTN + fn * 32 + 8 * g + 4 * (lane >> 5);
-                    const bool ok = row_ok && n0 + cc < N;
-                    const uint32_t off = ok ? (uint32_t)((r * N + cc) * 4) : kOOB;
+                    const bool ok = row_ok && cc < nr;
+                    const uint32_t off = ok ? ((uint32_t)r * pitch + (uint32_t)cc) * 4u : kOOB;
                     f32x4 v{acc[fm][fn][4 * g + 0], acc[fm][fn][4 * g + 1], acc[fm][fn][4 * g + 2],
                             acc[fm][fn][4 * g + 3]};
                     __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, kStorePolicy);

@@ -158,10 +158,11 @@ def test_binding_rejects_wrong_tensor_types(mk):
 
 
 def test_kernels_fit_their_register_and_lds_budget(mk):
-    """The compiler's resource report of the last build: the 128x128 fused
-    kernel and every plain GEMM keep all state in registers, the 256x128 fused
-    kernel (two blocks per CU, 256 registers a lane) spills only a bounded
-    amount, and no kernel asks for more LDS than a CU has (160 KiB)."""
+    """The compiler's resource report of the last build: every kernel keeps
+    its state in registers (no scratch: a reload in a K loop would make the
+    compiler wait for every load in flight, the operand ring included), the
+    256x128 fused kernel keeps two 8-wave blocks per CU, and no kernel asks
+    for more LDS than a CU has (160 KiB)."""
     import json
     lib = os.path.join(ROOT, "gemm_tile_granular_amd", "libmk.so")
     path = os.path.join(ROOT, "gemm_tile_granular_amd", "libmk.resources.json")
@@ -174,10 +175,7 @@ def test_kernels_fit_their_register_and_lds_budget(mk):
     assert len(fused) == 6 and len(gemm) == 3, sorted(res)
     for name, r in res.items():
         assert r["LDS Size"] <= 160 * 1024, name
-    for name, r in gemm.items():
         assert r["ScratchSize"] == 0, (name, r)
     for name, r in fused.items():
         if "ILi256ELi128E" in name:
-            assert r["Occupancy"] == 2 and r["ScratchSize"] <= 128, (name, r)
-        else:
-            assert r["ScratchSize"] == 0, (name, r)
+            assert r["Occupancy"] == 2, (name, r)
