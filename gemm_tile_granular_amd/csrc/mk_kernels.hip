@@ -625,11 +625,14 @@ using GemmFor = Gemm<TM, TN * TileCfg<TM, TN>::TPB, TileCfg<TM, TN>::KB, TileCfg
 // before group g is summed, so two groups stay in flight.  Per-tile uniform buffer bases keep lane offsets in 32
 // bits; ragged tiles use out-of-range offsets.
 // ---------------------------------------------------------------------------
-// loads of one group per lane: about 64 KiB per workgroup, so two groups keep
-// about 128 KiB in flight (a CU's streaming rate does not grow beyond that)
-template <int PP, int NT>
+// Loads of one group per lane: KIB KiB per workgroup, and two groups are in
+// flight.  Sharing the fabric with the GEMM and the other reducers, a
+// reducer streams at a rate that follows its bytes in flight: the XCD-local
+// fused kernel takes 128 KiB groups (256 KiB in flight), the other 64 KiB
+// groups, as many as its registers hold without spilling.
+template <int PP, int NT, int KIB>
 struct ReducePlan {
-    static constexpr int kLoads = 4096 / NT;
+    static constexpr int kLoads = KIB * 64 / NT;   // float4 per lane
     static constexpr int U = (kLoads / (PP + 1)) >= 16 ? 16
                            : (kLoads / (PP + 1)) >= 8 ? 8
                            : (kLoads / (PP + 1)) >= 4 ? 4
@@ -652,12 +655,12 @@ struct ReduceGroup {
 };
 
 // Region of TM rows x BW columns at (m0, n0): the tiles of one compute block.
-template <int TM, int BW, int NT, int PP, int kLoadPol, int kStorePol>
+template <int TM, int BW, int NT, int PP, int kLoadPol, int kStorePol, int KIB>
 __device__ __forceinline__ void reduce_tile_pp(const float *__restrict__ peers, float *__restrict__ C,
                                                int64_t M, int64_t N, int P, int64_t m0, int64_t n0) {
     using RG = ReduceGeom<TM, BW, NT>;
     constexpr int PB = 8;                   // peer block when PP is the generic 0
-    constexpr int UP = ReducePlan<(PP > 0 ? PP : PB), NT>::U;
+    constexpr int UP = ReducePlan<(PP > 0 ? PP : PB), NT, KIB>::U;
     constexpr int U = UP < RG::PASSES ? UP : RG::PASSES;
     constexpr int G = RG::PASSES / U;
     static_assert(RG::PASSES % U == 0, "reduce layout");
@@ -750,15 +753,15 @@ __device__ __forceinline__ void reduce_tile_pp(const float *__restrict__ peers, 
 
 // Dispatch on the peer count: the R-1 of 2, 4, 8 and 16 ranks get straight-line
 // pipelined code; other counts take the blocked loop.
-template <int TM, int BW, int NT, int kLoadPol, int kStorePol>
+template <int TM, int BW, int NT, int kLoadPol, int kStorePol, int KIB>
 __device__ __forceinline__ void reduce_tile(const float *__restrict__ peers, float *__restrict__ C,
                                             int64_t M, int64_t N, int P, int64_t m0, int64_t n0) {
     switch (P) {
 #define MK_REDUCE_CASE(k) \
-    case k: reduce_tile_pp<TM, BW, NT, k, kLoadPol, kStorePol>(peers, C, M, N, P, m0, n0); break;
+    case k: reduce_tile_pp<TM, BW, NT, k, kLoadPol, kStorePol, KIB>(peers, C, M, N, P, m0, n0); break;
         MK_REDUCE_CASE(1) MK_REDUCE_CASE(3) MK_REDUCE_CASE(7) MK_REDUCE_CASE(15)
 #undef MK_REDUCE_CASE
-        default: reduce_tile_pp<TM, BW, NT, 0, kLoadPol, kStorePol>(peers, C, M, N, P, m0, n0); break;
+        default: reduce_tile_pp<TM, BW, NT, 0, kLoadPol, kStorePol, KIB>(peers, C, M, N, P, m0, n0); break;
     }
 }
 
@@ -1370,7 +1373,7 @@ void fused_gemm_reduce_kernel(
             // thread 0 saw the flag before the barrier; the partial is read
             // with device-coherent loads, after it
             if (a.P > 0)
-                reduce_tile<TM, TN, G::NT, H::kPartialLoad, H::kResultStore>(
+                reduce_tile<TM, TN, G::NT, H::kPartialLoad, H::kResultStore, LOCAL ? 128 : 64>(
                     a.peers, a.C, Mp, Np, a.P, (int64_t)ti * TM, (int64_t)tj * TN);
             work_done(kRoleReduce);
         }
