@@ -59,6 +59,13 @@ SHAPES = [
     # second reduce ticket is empty
     (1100, 264, 200, 3, 128, 128, 4),
     (2100, 264, 136, 2, 256, 128, 4),
+    # K a multiple of the K slab and long enough for the steady-state loop:
+    # interior blocks take the GEMM core's fast path (loads spread over the
+    # k-steps), the ragged last row and column of blocks the checked path,
+    # in the same launch
+    (1000, 1000, 1024, 3, 128, 128, 4),
+    (600, 520, 512, 2, 256, 128, 4),
+    (300, 328, 512, 2, 64, 64, 4),
 ]
 
 
@@ -74,7 +81,7 @@ def test_ragged_shapes_full_oracle(mk, shape, mode):
 
 
 def test_unfused_baseline_full_oracle(mk):
-    for shape in SHAPES[:3] + [(256, 256, 512, 1, 64, 64, 4)]:
+    for shape in SHAPES[:3] + SHAPES[-3:] + [(256, 256, 512, 1, 64, 64, 4)]:
         M, N, K, P, tm, tn, tpc = shape
         w = wl.custom(M, N, K, P, tm, tn, tpc, wid=500)
         a, b, p = wl.make_inputs(w)
