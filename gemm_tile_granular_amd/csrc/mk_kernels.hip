@@ -220,12 +220,12 @@ __device__ __forceinline__ Parts make_parts(uint32_t nx, uint32_t tiles_m, uint3
 // GEMM tile on MFMA
 //
 // A [M,K] and B [K,N] (both row-major bf16) reach LDS by direct buffer-to-LDS
-// loads (no register staging) into a ring of NS K-slabs of 64, so the loads
-// for slab s+NS-1 are in flight while slab s is multiplied.  The load
-// instruction is issued from inline assembly: the compiler cannot yet tell
-// which ring slot a direct-to-LDS load writes and would otherwise wait for
-// every outstanding load before any LDS read; the ring's waits are explicit
-// (wait_vmcnt) and each is followed by a workgroup barrier.
+// loads (no register staging) into a ring of NS K-slabs (KB deep), so later
+// slabs stream in while slab s is multiplied (see slab() for the schedule).
+// The load instruction is issued from inline assembly: the compiler cannot
+// yet tell which ring slot a direct-to-LDS load writes and would otherwise
+// wait for every outstanding load before any LDS read; the ring's waits are
+// explicit (wait_vmcnt) and each is followed by a workgroup barrier.
 //
 // LDS layout per slab, chosen for the 64-bank LDS of gfx950:
 //   A: row m = 128 bytes (64 k), 16-byte chunk c stored at c ^ ((m >> 1) & 7);
@@ -238,7 +238,8 @@ __device__ __forceinline__ Parts make_parts(uint32_t nx, uint32_t tiles_m, uint3
 //      rows kbase .. kbase+3 of column nbase + i.
 // The MFMA is fed (B, A), so lane l ends with row (l & 31) and columns
 // 8g + 4(l >> 5) + 0..3 of every 32x32 block: the tile leaves as 16-byte
-// stores.  All per-lane LDS and buffer offsets are computed once per kernel.
+// stores.  The per-lane LDS and buffer offsets of the K loop are computed once
+// per kernel; those of the edge checks and the epilogue, once per block.
 // ---------------------------------------------------------------------------
 
 typedef __attribute__((address_space(3))) char lchar;
