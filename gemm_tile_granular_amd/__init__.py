@@ -76,6 +76,7 @@ class Stats(ctypes.Structure):
         ("xcd_local", ctypes.c_uint32),
         ("keep_compute", ctypes.c_uint32),
         ("controller_cap", ctypes.c_uint32),
+        ("xcd_bands", ctypes.c_uint32),
     ]
 
 
@@ -87,6 +88,7 @@ SIGNATURES = {
     "mk_set_partition": (_i32, [_i32, _i32]),
     "mk_set_controller_floor": (_i32, [_i32]),
     "mk_set_controller_cap": (_i32, [_i32]),
+    "mk_set_xcd_bands": (_i32, [_i32]),
     "mk_set_num_workgroups": (_i32, [_i32]),
     "mk_set_timeout_us": (_i32, [ctypes.c_uint64]),
     "mk_set_fault_skip_publish": (_i32, [_i64]),
@@ -180,6 +182,11 @@ def set_controller_floor(floor: int) -> None:
 def set_controller_cap(cap: int) -> None:
     """Most reduce workgroups the adaptive controller sets while compute remains (0: 5B/8)."""
     _check(lib.mk_set_controller_cap(int(cap)))
+
+
+def set_xcd_bands(bands: int) -> None:
+    """Column bands of the XCD-local partitions (0: least operand traffic; 1, 2, 4, 8)."""
+    _check(lib.mk_set_xcd_bands(int(bands)))
 
 
 def set_num_workgroups(num_wg: int) -> None:

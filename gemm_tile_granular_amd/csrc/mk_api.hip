@@ -44,6 +44,7 @@ struct Settings {
     uint64_t timeout_us = 2000000;
     int64_t skip_publish = -1;
     int group_m = 8;
+    int xcd_bands = 0;        // 0: the most column bands the shape allows
 };
 Settings g_set;
 
@@ -53,7 +54,7 @@ struct Launch {
     bool valid = false;
     uint32_t epoch = 0, calls = 0, nwg = 0, T = 0, Ch = 0, tpc = 0, tm = 0, tn = 0;
     uint32_t mode = 0, ns_init = 0;
-    uint32_t local = 0, keep = 1, cap = 0;
+    uint32_t local = 0, keep = 1, cap = 0, bands = 1;
 };
 
 struct DevState {
@@ -117,6 +118,40 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 // on MI355X) when the grid spans whole XCDs, else a single partition.
 int xcd_partitions(int nwg, int num_cu) {
     return (num_cu % kMaxXcd == 0 && nwg >= 2 * kMaxXcd && nwg % kMaxXcd == 0) ? kMaxXcd : 1;
+}
+
+// Column bands of the XCD-local partitions: nxcd = px * py, px row groups
+// (each must hold a tile row) by py bands of whole chunks (each must hold a
+// chunk column of blocks; py = 1 is whole rows).  An XCD fetches the A rows
+// of its row group and the B columns of its band.  The default is the most
+// bands the shape allows: on all four benchmark shapes the fused kernel ran
+// fastest with eight bands (1-6% over whole rows), square shapes included,
+// where the operand traffic py*M + px*N of each split is the same or larger.
+// `want`, when that split is valid, overrides.  0: no valid split.
+int xcd_bands(int nxcd, int tiles_m, int tiles_n, int tile_m, int tile_n, int tpc, int want) {
+    const int tpb = tiles_per_block(tile_m, tile_n);
+    const int bn = (tiles_n + tpb - 1) / tpb;            // blocks per block row
+    const int cb = (tpc % tpb == 0) ? tpc / tpb : 1;      // blocks per chunk
+    int best = 0, forced = 0;
+    for (int py = 1; py <= nxcd; py *= 2) {
+        if (nxcd % py != 0 || tiles_m < nxcd / py) continue;
+        if (py > 1 && (bn % cb != 0 || bn / cb < py)) continue;
+        best = py;
+        if (py == want) forced = py;
+    }
+    return forced ? forced : best;
+}
+
+// The same for the persistent GEMM of the unfused baseline, whose blocks are
+// taken in one interleaved order (partition w mod 8 for workgroup w): a split
+// with py > 1 is used only when every partition is the same size.
+int gemm_xcd_bands(int nxcd, int tiles_m, int tiles_n, int tile_m, int tile_n, int tpc, int want) {
+    const int tpb = tiles_per_block(tile_m, tile_n);
+    const int bn = (tiles_n + tpb - 1) / tpb;
+    const int cb = (tpc % tpb == 0) ? tpc / tpb : 1;
+    int py = xcd_bands(nxcd, tiles_m, tiles_n, tile_m, tile_n, tpc, want);
+    while (py > 1 && (tiles_m % (nxcd / py) != 0 || (bn / cb) % py != 0)) py /= 2;
+    return py > 0 ? py : 1;
 }
 
 // All argument checks that do not need the GPU.
@@ -276,6 +311,9 @@ int run(bool fused, const void *A, const void *B, const float *peers, int num_pe
         g.tpc = tpc;
         g.group_m = set.group_m;
         g.nxcd = xcd_partitions(d.num_cu, d.num_cu);
+        g.xcd_cols = g.nxcd == kMaxXcd
+                         ? gemm_xcd_bands(g.nxcd, tiles_m, tiles_n, tile_m, tile_n, tpc, set.xcd_bands)
+                         : 1;
         hipError_t e = launch_gemm(tile_m, tile_n, g, d.num_cu, s);
         if (e != hipSuccess) return hip_fail(e, "GEMM launch");
         if (num_peers > 0) {
@@ -309,7 +347,9 @@ int run(bool fused, const void *A, const void *B, const float *peers, int num_pe
     // reducer and a compute workgroup (8 <= n_reduce <= B - 8).  Otherwise
     // tiles cross XCDs with write-through hand-off.
     const int nxcd = xcd_partitions(nwg, d.num_cu);
-    const bool local = d.xcd_ok && nxcd == kMaxXcd && tiles_m >= nxcd &&
+    const int bands = nxcd == kMaxXcd ? xcd_bands(nxcd, tiles_m, tiles_n, tile_m, tile_n, tpc, set.xcd_bands)
+                                      : 0;
+    const bool local = d.xcd_ok && nxcd == kMaxXcd && bands > 0 &&
                        set.mode != MK_PART_STATIC_DETERMINISTIC &&
                        (set.mode == MK_PART_ADAPTIVE || (ns_init >= nxcd && ns_init <= nwg - nxcd));
     const int keep = local ? nxcd : 1;
@@ -385,6 +425,7 @@ int run(bool fused, const void *A, const void *B, const float *peers, int num_pe
     a.local = local ? 1 : 0;
     a.keep = keep;
     a.ns_cap = cap;
+    a.xcd_cols = local ? bands : 1;
     a.timeout_ticks = set.timeout_us * (d.timer_hz / 1000000ull);
     a.skip_publish = set.skip_publish;
     a.ws = v;
@@ -407,6 +448,7 @@ int run(bool fused, const void *A, const void *B, const float *peers, int num_pe
     d.last.local = local ? 1u : 0u;
     d.last.keep = (uint32_t)keep;
     d.last.cap = (uint32_t)cap;
+    d.last.bands = local ? (uint32_t)bands : 1u;
     return MK_OK;
 }
 
@@ -451,6 +493,14 @@ int mk_set_controller_cap(int cap) {
     std::lock_guard<std::mutex> lk(g_mu);
     if (cap < 0 || cap > kMaxWG) return fail(MK_ERR_INVALID_ARG, "cap must be in [0, 1024]");
     g_set.cap = cap;
+    return MK_OK;
+}
+
+int mk_set_xcd_bands(int bands) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (bands != 0 && bands != 1 && bands != 2 && bands != 4 && bands != 8)
+        return fail(MK_ERR_INVALID_ARG, "bands must be 0, 1, 2, 4 or 8");
+    g_set.xcd_bands = bands;
     return MK_OK;
 }
 
@@ -534,6 +584,7 @@ int mk_get_stats(mk_stats *out, uint32_t *maps, size_t maps_len) {
     out->xcd_local = l.local;
     out->keep_compute = l.keep;
     out->controller_cap = l.cap;
+    out->xcd_bands = l.bands;
 
     if (maps) {
         uint32_t *p = maps;

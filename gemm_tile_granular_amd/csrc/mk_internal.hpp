@@ -90,6 +90,7 @@ struct FusedArgs {
     int32_t group_m;          // tile-row band height of the claim order
     int32_t nxcd;             // tile partitions (XCDs) for the claim order
     int32_t local;            // 1: every tile is computed and reduced on its partition's XCD
+    int32_t xcd_cols;         // local: column bands of the XCD partitions (1: whole tile rows)
     int32_t keep;             // compute workgroups the controller keeps while compute remains
     int32_t ns_cap;           // most reduce workgroups the controller sets while compute remains
     uint64_t timeout_ticks;   // bound on any wait, constant-clock ticks
@@ -105,6 +106,7 @@ struct GemmArgs {
     int32_t tiles_m, tiles_n;
     int32_t tpc, group_m;
     int32_t nxcd;
+    int32_t xcd_cols;         // column bands of the partitions (1: whole tile rows)
 };
 
 struct ReduceArgs {

@@ -173,29 +173,54 @@ __device__ __forceinline__ uint32_t tile_of_claim(uint32_t q, uint32_t tiles_m, 
 // XCD-aware tile partitions
 //
 // MI355X has 8 XCDs, each with its own L2, and dispatches workgroup w to XCD
-// w mod 8.  Tile rows are dealt to nx partitions (row r -> partition r mod nx,
-// so chunks stay whole); workgroups claim compute tiles from their own XCD's
-// partition first, in the banded order above, so the tiles one L2 serves at
-// once share A rows and B columns, and steal from the other partitions when
-// theirs is done.  Reduce tickets walk the partitions round-robin, which is
-// the order in which tiles complete when the partitions progress together.
+// w mod 8.  The blocks are cut into nx = px * py partitions: px row groups
+// (tile row r -> group r mod px) times py column bands (contiguous runs of
+// whole chunks).  Partition x is row group x / py, band x % py.  An XCD then
+// fetches only its row groups' A panels and its band's B panels: operand
+// traffic py*|A| + px*|B| against |A| + 8*|B| for whole rows (py = 1).
+// Workgroups claim compute blocks from their own XCD's partition first, in
+// the banded order above, so the blocks one L2 serves at once share A rows
+// and B columns, and (unless tiles stay on their XCD) steal from the other
+// partitions when theirs is done.  Without that restriction reduce tickets
+// walk the partitions round-robin, which is the order in which tiles
+// complete when the partitions progress together (whole rows only).
 // ---------------------------------------------------------------------------
 struct Parts {
-    uint32_t nx;        // partitions (1 or the XCD count)
-    uint32_t rows_min;  // tile rows in the smaller partitions
-    uint32_t rem;       // partitions [0, rem) hold one more tile row
-    uint32_t tiles_n, tiles_m, tpc, group_m;
+    uint32_t nx;          // partitions (1 or the XCD count)
+    uint32_t lpy;         // log2 of the column bands py (0: whole block rows)
+    uint32_t px;          // row groups, nx / py
+    uint32_t rows_min;    // block rows in the smaller row groups
+    uint32_t rem;         // row groups [0, rem) hold one more block row
+    uint32_t cch_min;     // chunk columns in the narrower bands (py > 1)
+    uint32_t crem;        // bands [0, crem) hold one more chunk column
+    uint32_t tiles_n, tpc, group_m;   // in blocks: per block row, per chunk
 
-    __device__ __forceinline__ uint32_t rows(uint32_t x) const { return rows_min + (x < rem ? 1u : 0u); }
-    __device__ __forceinline__ uint32_t size(uint32_t x) const { return rows(x) * tiles_n; }
-    // tile of the i-th claim of partition x
-    __device__ __forceinline__ uint32_t tile(uint32_t x, uint32_t i) const {
-        const uint32_t local = tile_of_claim(i, rows(x), tiles_n, tpc, group_m);
-        const uint32_t lr = local / tiles_n, col = local % tiles_n;
-        return (lr * nx + x) * tiles_n + col;
+    __device__ __forceinline__ uint32_t rows(uint32_t x) const {
+        return rows_min + ((x >> lpy) < rem ? 1u : 0u);
     }
-    // tile of global ticket q: partitions interleaved claim by claim
+    __device__ __forceinline__ uint32_t cols(uint32_t x) const {
+        if (lpy == 0) return tiles_n;
+        const uint32_t xc = x & ((1u << lpy) - 1u);
+        return (cch_min + (xc < crem ? 1u : 0u)) * tpc;
+    }
+    __device__ __forceinline__ uint32_t col0(uint32_t x) const {
+        if (lpy == 0) return 0;
+        const uint32_t xc = x & ((1u << lpy) - 1u);
+        return (xc * cch_min + (xc < crem ? xc : crem)) * tpc;
+    }
+    __device__ __forceinline__ uint32_t size(uint32_t x) const { return rows(x) * cols(x); }
+    // block of the i-th claim of partition x
+    __device__ __forceinline__ uint32_t tile(uint32_t x, uint32_t i) const {
+        const uint32_t c = cols(x);
+        const uint32_t local = tile_of_claim(i, rows(x), c, tpc, group_m);
+        const uint32_t lr = local / c, lc = local % c;
+        return (lr * px + (x >> lpy)) * tiles_n + col0(x) + lc;
+    }
+    // block of global ticket q: partitions interleaved claim by claim.  With
+    // column bands every partition is the same size (the host checks); with
+    // whole rows all but the last rem are.
     __device__ __forceinline__ uint32_t ticket(uint32_t q) const {
+        if (lpy != 0) return tile(q % nx, q / nx);
         const uint32_t base = nx * rows_min * tiles_n;
         if (q < base) return tile(q % nx, q / nx);
         const uint32_t q2 = q - base;
@@ -203,14 +228,20 @@ struct Parts {
     }
 };
 
-__device__ __forceinline__ Parts make_parts(uint32_t nx, uint32_t tiles_m, uint32_t tiles_n,
+// py (a power of two) must divide nx, and for py > 1 the chunk columns
+// (tiles_n / tpc, whole) must number at least py; the host checks both.
+__device__ __forceinline__ Parts make_parts(uint32_t nx, uint32_t py, uint32_t tiles_m, uint32_t tiles_n,
                                             uint32_t tpc, uint32_t group_m) {
     Parts p;
     p.nx = nx;
-    p.rows_min = tiles_m / nx;
-    p.rem = tiles_m % nx;
+    p.lpy = py > 1 ? 31u - (uint32_t)__builtin_clz(py) : 0u;
+    p.px = nx >> p.lpy;
+    p.rows_min = tiles_m / p.px;
+    p.rem = tiles_m % p.px;
+    const uint32_t cch = py > 1 ? tiles_n / tpc : 0;
+    p.cch_min = cch >> p.lpy;
+    p.crem = cch & (py - 1u);
     p.tiles_n = tiles_n;
-    p.tiles_m = tiles_m;
     p.tpc = tpc;
     p.group_m = group_m;
     return p;
@@ -1282,6 +1313,9 @@ void fused_gemm_reduce_kernel(
 
     const int tid = threadIdx.x;
     const uint32_t wg = blockIdx.x;
+    // the host launches this instance exactly when a.local is LOCAL: as a
+    // constant it removes the other mode's claim paths from the scheduler
+    a.local = LOCAL ? 1 : 0;
     Live *L = a.ws.live;
     typename G::Lane ln;
     G::init_lane(ln, a.N, a.K);
@@ -1289,8 +1323,13 @@ void fused_gemm_reduce_kernel(
     constexpr int TPB = TileCfg<TM, TN>::TPB;
     static_assert(TPB <= kMaxTpb, "tiles per block");
     const Blocks bk = make_blocks(TPB, (uint32_t)a.tiles_m, (uint32_t)a.tiles_n);
-    const Parts pt = make_parts((uint32_t)a.nxcd, (uint32_t)a.tiles_m, bk.bn, chunk_blocks(a.tpc, TPB),
-                                (uint32_t)a.group_m);
+    // the partitions serve thread 0's claims only: kept in LDS beside the
+    // scheduling state
+    __shared__ Parts sh_parts;
+    const Parts &pt = sh_parts;
+    if (tid == 0)
+        sh_parts = make_parts((uint32_t)a.nxcd, a.local ? (uint32_t)a.xcd_cols : 1u, (uint32_t)a.tiles_m,
+                              bk.bn, chunk_blocks(a.tpc, TPB), (uint32_t)a.group_m);
     Sched &s = sh_sched;
     if (LOCAL && tid == 0) {
         // tiles stay on their XCD only if this workgroup runs where its index
@@ -1447,7 +1486,7 @@ void gemm_kernel(GemmArgs a) {
     typename G::Lane ln;
     G::init_lane(ln, a.N, a.K);
     const Blocks bk = make_blocks(TPB, (uint32_t)a.tiles_m, (uint32_t)a.tiles_n);
-    const Parts pt = make_parts((uint32_t)a.nxcd, (uint32_t)a.tiles_m, bk.bn,
+    const Parts pt = make_parts((uint32_t)a.nxcd, (uint32_t)a.xcd_cols, (uint32_t)a.tiles_m, bk.bn,
                                 chunk_blocks((uint32_t)a.tpc, TPB), (uint32_t)a.group_m);
     for (uint32_t q = blockIdx.x; q < bk.TB; q += gridDim.x) {
         const uint32_t t0 = bk.first_tile(pt.ticket(q));

@@ -154,6 +154,24 @@ int mk_set_controller_floor(int floor);
 int mk_set_controller_cap(int cap);
 
 /*
+ * mk_set_xcd_bands -- column bands of the XCD-local tile partitions.  When
+ * every tile stays on its XCD (mk_stats.xcd_local), the blocks are cut into
+ * 8 partitions, one per XCD, as px row groups (tile row r in group r mod px)
+ * times py = bands column bands of whole chunks, px * py = 8.  An XCD then
+ * fetches only the A rows of its row group and the B columns of its band.
+ * This assignment of tiles to an 8-L2 GPU is this library's own; the pages
+ * fix none ("【学习】mKernel 分析" section 2.2 tiles the output, section 2.3
+ * groups tiles into chunks).
+ * 0 (default): the most bands the shape allows (eight on every benchmark
+ * shape, where it measured fastest); 1, 2, 4 or 8: that split, when the
+ * shape allows it (each row group needs a tile row and each band a chunk
+ * column of blocks), else the default.  Results do not depend on the split;
+ * mk_stats.xcd_bands reports the one used.
+ * Errors: MK_ERR_INVALID_ARG for any other value.
+ */
+int mk_set_xcd_bands(int bands);
+
+/*
  * mk_set_num_workgroups -- persistent workgroups per launch (B).  0 (default)
  * = every workgroup that can be resident: the compute-unit count (256 on
  * MI355X) times the workgroups one CU holds for the tile configuration (1 for
@@ -214,6 +232,7 @@ typedef struct mk_stats {
     uint32_t xcd_local;           /* 1: every tile stayed on its partition's XCD */
     uint32_t keep_compute;        /* compute workgroups the controller kept      */
     uint32_t controller_cap;      /* most reducers while compute remained        */
+    uint32_t xcd_bands;           /* column bands of the XCD partitions (1: rows) */
 } mk_stats;
 
 /* Words per map in the optional `maps` output of mk_get_stats, in order:

@@ -139,6 +139,10 @@ def test_setting_calls_validate(mk):
     assert lib.mk_set_controller_cap(-1) == -1
     assert lib.mk_set_controller_cap(1025) == -1
     assert lib.mk_set_controller_cap(0) == 0
+    for bad in (-1, 3, 5, 16):
+        assert lib.mk_set_xcd_bands(bad) == -1
+    for ok in (1, 2, 4, 8, 0):
+        assert lib.mk_set_xcd_bands(ok) == 0
     assert lib.mk_controller_eval(None, None, -1, None) == -1
     assert lib.mk_controller_eval(None, None, 0, None) == 0
 

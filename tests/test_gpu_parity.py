@@ -24,9 +24,11 @@ def mk():
     mk.set_fault_skip_publish(-1)
     mk.set_controller_floor(2)
     mk.set_controller_cap(0)
+    mk.set_xcd_bands(0)
     yield mk
     mk.set_partition("adaptive", 0)
     mk.set_num_workgroups(0)
+    mk.set_xcd_bands(0)
 
 
 def test_device_is_the_expected_one(mk):
@@ -319,3 +321,38 @@ def test_alternating_inputs_same_output_buffer(mk):
         st = mk.get_stats(maps=True)
         check_full(C.cpu().numpy(), a, b, p)
         check_protocol(st, w, mode, 64 if mode != "adaptive" else 2)
+
+
+# XCD-local partitions as row groups x column bands of whole chunks, forced to
+# each split the shape allows.  (M, N, K, P, bands, expected bands): 8 tile
+# rows by 8 chunk columns allow every split; 9 tile rows by 5 chunk columns
+# give ragged row groups and bands of unequal width (5 chunks over 4 bands),
+# and 8 bands fall back to the most the shape allows (4).
+BAND_CASES = [
+    (1024, 4096, 256, 2, 1, 1), (1024, 4096, 256, 2, 2, 2),
+    (1024, 4096, 256, 2, 4, 4), (1024, 4096, 256, 2, 8, 8),
+    (1100, 2560, 192, 3, 2, 2), (1100, 2560, 192, 3, 4, 4), (1100, 2560, 192, 3, 8, 4),
+]
+
+
+@pytest.mark.parametrize("case", BAND_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_xcd_column_bands_full_oracle(mk, case):
+    M, N, K, P, bands, used = case
+    w = wl.custom(M, N, K, P, 128, 128, 4, wid=700 + bands)
+    a, b, p = wl.make_inputs(w)
+    mk.set_xcd_bands(bands)
+    try:
+        C, st = run_fused(mk, w, a, b, p, mode="adaptive", n_reduce=0)
+        print(f"[gpu] bands forced {bands}: used {st['xcd_bands']} local {st['xcd_local']}", flush=True)
+        if st["xcd_local"]:
+            assert st["xcd_bands"] == used
+        check_full(C, a, b, p)
+        check_protocol(st, w, "adaptive", 0)
+        # the split moves work between XCDs, not the order of any sum
+        mk.set_xcd_bands(1)
+        C1, _ = run_fused(mk, w, a, b, p, mode="adaptive", n_reduce=0, maps=False)
+        assert np.array_equal(C, C1)
+        Cu = run_unfused(mk, w, a, b, p)
+        assert np.array_equal(C, Cu)
+    finally:
+        mk.set_xcd_bands(0)
