@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true", help="skip the static partition sweep")
     ap.add_argument("--fused-only", action="store_true",
                     help="only the fused leg (for profiler runs)")
+    ap.add_argument("--gemm-only", action="store_true",
+                    help="only the GEMM kernel of the unfused baseline, no peers (for counter "
+                         "runs on the MFMA core); prints its own JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of this size (counter calibration)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -144,6 +147,28 @@ def measured_traffic(workload):
     return float(wrec["hbm_bytes_per_launch"]), "rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated"
 
 
+def gemm_only(args, w, mk, wl, upload, np, torch):
+    """The unfused baseline's GEMM kernel alone (no peers): C = A.B, timed
+    with HIP events like the other legs."""
+    import dataclasses
+    a, b, _ = wl.make_inputs(dataclasses.replace(w, peers=0))
+    A, B, P, C = upload(a, b, np.zeros((0, w.M, w.N), np.float32), "cuda:0")
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def gemm():
+        mk.gemm_reduce_unfused(A, B, None, C, w.tile_m, w.tile_n, w.tiles_per_chunk)
+
+    ms, _ = time_leg(gemm, args.steps, args.warmup, None, stream, torch)
+    mean = statistics.fmean(ms)
+    print(json.dumps({"metric": "GEMM TFLOP/s (unfused baseline's GEMM kernel, no peers)",
+                      "value": w.flops / (mean * 1e-3) / 1e12, "unit": "TFLOP/s",
+                      "ms_per_step": mean, "steps": args.steps, "warmup": args.warmup,
+                      "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
+                                 "tile": [w.tile_m, w.tile_n]}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -159,6 +184,9 @@ def main():
     from gemm_tile_granular_amd.tensors import upload
 
     w = wl.workload(args.workload)
+    if args.gemm_only:
+        gemm_only(args, w, mk, wl, upload, np, torch)
+        return
     t_gen = time.perf_counter()
     a, b, p = wl.make_inputs(w)
     A, B, P, C = upload(a, b, p, "cuda:0")
