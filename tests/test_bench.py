@@ -1,0 +1,51 @@
+"""bench.py's host side without a GPU: the one-GPU rule, and the traffic
+record it reads (profiles/traffic.json) against the kernel sources."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_traffic_record_is_reported_only_for_its_kernel():
+    """bench.py reports the committed counters while the kernel sources hash
+    to the profiled version, and null once they changed."""
+    import bench
+    with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+        rec = json.load(f)
+    if rec["kernel_source_sha256_16"] != bench.kernel_source_hash():
+        for name in ("tp_share", "compute_heavy"):
+            got, note = bench.measured_traffic(name)
+            assert got is None and "changed" in note
+        return
+    for name in ("tp_share", "compute_heavy"):
+        got, note = bench.measured_traffic(name)
+        want = rec["workloads"][name]
+        assert got == pytest.approx(want["hbm_bytes_per_launch"]), note
+        # FETCH_SIZE and WRITE_SIZE (KiB per dispatch), scaled by the copy calibration
+        scaled = (want["fetch_size_kib"] * rec["calibration"]["FETCH_SIZE"]["factor"]
+                  + want["write_size_kib"] * rec["calibration"]["WRITE_SIZE"]["factor"]) * 1024
+        assert got == pytest.approx(scaled, rel=1e-9)
+        assert got >= want["algorithmic_bytes"]
+    assert bench.measured_traffic("tiny")[0] is None
+
+
+def test_algorithmic_work_of_the_named_workloads():
+    """flops 2MNK; bytes A and B once, every peer once, C written once."""
+    import workloads as wl
+    for name in ("tp_share", "reduce_heavy", "compute_heavy", "wide_many_peer"):
+        w = wl.workload(name)
+        assert w.flops == 2 * w.M * w.N * w.K
+        assert w.algorithmic_bytes == 2 * w.M * w.K + 2 * w.K * w.N + 4 * w.peers * w.M * w.N + 4 * w.M * w.N
