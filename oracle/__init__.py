@@ -17,6 +17,17 @@ What it computes, and from which passage:
   oracle is the definition itself, in float64, on the exact bfloat16 input
   values.  The reduction operator is addition (partial sums of a row-parallel
   product).
+* `gemm_reduce_scatter` / `rs_shard_bounds` -- one rank's share of
+  GEMM+ReduceScatter (GEMM + ReduceScatter row of the five-kernel table on the
+  MarkTechPost page: C = A @ B is computed and each output tile is reduced and
+  sent to the rank that owns it as soon as it exists; "【学习】mKernel 分析"
+  section 2.6, Table 3: tiles reach their rank by atomic add, in chunks of 2
+  to 32 tiles).  The pages fix no shard layout.  The reading used: R = P + 1
+  ranks, this rank is rank 0, and rank o owns tile rows [floor(o T_m / R),
+  floor((o+1) T_m / R)) of the T_m tile rows.  Rank 0's own rows receive the
+  other ranks' partials (the peers stand in for them); every other tile of
+  this rank's partial is added into its owner's output, which a buffer in
+  local memory stands in for.
 * `controller_update` / `controller_target` -- the adaptive partition rule of
   "【学习】mKernel 分析" section 2.4: the target number of communication
   (here: reduce) workgroups n_s* = B (R_s C_s) / (R_p C_p + R_s C_s), the value
@@ -117,6 +128,48 @@ def gemm_reduce_at(a_bits: np.ndarray, b_bits: np.ndarray, peers: np.ndarray,
     if peers is not None and peers.shape[0]:
         full += peers[:, rows, cols].astype(np.float64).sum(axis=0)
     return full, gemm
+
+
+def rs_shard_bounds(tiles_m: int, ranks: int) -> np.ndarray:
+    """Tile-row bounds of the R row shards: rank o owns tile rows
+    [bounds[o], bounds[o+1]), bounds[o] = floor(o * tiles_m / R).  Shards are
+    as even as whole tile rows allow; with fewer tile rows than ranks some
+    shards are empty."""
+    if tiles_m < 0 or ranks < 1:
+        raise ValueError("tiles_m >= 0 and ranks >= 1")
+    return np.array([(o * tiles_m) // ranks for o in range(ranks + 1)], dtype=np.int64)
+
+
+def gemm_reduce_scatter(a_bits: np.ndarray, b_bits: np.ndarray, peers: np.ndarray,
+                        remote_init: np.ndarray, tile_m: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Rank 0's share of GEMM+ReduceScatter with R = P + 1 ranks, float64.
+
+    Returns (C, remote), both [M,N]:
+    - C: on rank 0's rows, A.B + sum_p peers[p] (its reduced shard); on every
+      other row, A.B (this rank's partial, left where it was computed);
+    - remote: remote_init + A.B on the rows of ranks 1..R-1 (each tile added
+      once into its owner's output), remote_init on rank 0's rows.
+    """
+    a = np.asarray(a_bits)
+    b = np.asarray(b_bits)
+    if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError("A must be [M,K] and B must be [K,N]")
+    M, N = a.shape[0], b.shape[1]
+    P = 0 if peers is None else peers.shape[0]
+    if P and peers.shape[1:] != (M, N):
+        raise ValueError("peers must be [P,M,N]")
+    if remote_init.shape != (M, N):
+        raise ValueError("remote_init must be [M,N]")
+    tiles_m = -(-M // tile_m)
+    bounds = rs_shard_bounds(tiles_m, P + 1)
+    own_rows = slice(0, min(M, int(bounds[1]) * tile_m))
+    part = gemm_part(a, b)
+    C = part.copy()
+    if P:
+        C[own_rows] += peer_sum(peers[:, own_rows, :])
+    remote = remote_init.astype(np.float64).copy()
+    remote[own_rows.stop:] += part[own_rows.stop:]
+    return C, remote
 
 
 # ---------------------------------------------------------------------------
