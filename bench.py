@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--gemm-only", action="store_true",
                     help="only the GEMM kernel of the unfused baseline, no peers (for counter "
                          "runs on the MFMA core); prints its own JSON line")
+    ap.add_argument("--reduce-scatter", action="store_true",
+                    help="one rank's share of GEMM+ReduceScatter instead (fused and unfused legs); "
+                         "prints its own JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of this size (counter calibration)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -169,6 +172,42 @@ def gemm_only(args, w, mk, wl, upload, np, torch):
                                  "tile": [w.tile_m, w.tile_n]}}), flush=True)
 
 
+def reduce_scatter(args, w, mk, wl, upload, np, torch):
+    """Rank 0's share of GEMM+ReduceScatter on the workload's shapes: the
+    fused persistent launch and the two-launch baseline, timed with HIP
+    events like the other legs (caches flushed between steps)."""
+    a, b, p = wl.make_inputs(w)
+    A, B, P, C = upload(a, b, p, "cuda:0")
+    R = torch.from_numpy(wl.make_remote(w)).to("cuda:0")
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def flush():
+        scratch.fill_(1)
+
+    def fused():
+        mk.gemm_reduce_scatter_local(A, B, P, C, R, w.tile_m, w.tile_n, w.tiles_per_chunk)
+
+    def unfused():
+        mk.gemm_reduce_scatter_unfused(A, B, P, C, R, w.tile_m, w.tile_n, w.tiles_per_chunk)
+
+    mk.set_partition("adaptive", 0)
+    fl = None if args.no_flush else flush
+    ms_f, _ = time_leg(fused, args.steps, args.warmup, fl, stream, torch)
+    st = mk.get_stats(maps=False)
+    ms_u, _ = time_leg(unfused, args.steps, args.warmup, fl, stream, torch)
+    mf, mu = statistics.fmean(ms_f), statistics.fmean(ms_u)
+    print(json.dumps({"metric": "GEMM+ReduceScatter TFLOP/s (one rank's share, fused adaptive)",
+                      "value": w.flops / (mf * 1e-3) / 1e12, "unit": "TFLOP/s",
+                      "ms_per_step": mf, "unfused_ms_per_step": mu, "fused_over_unfused": mu / mf,
+                      "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic",
+                      "fused_ms": summary(ms_f), "unfused_ms": summary(ms_u),
+                      "status": st["status_name"],
+                      "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "ranks": w.peers + 1,
+                                 "tile": [w.tile_m, w.tile_n]}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -186,6 +225,9 @@ def main():
     w = wl.workload(args.workload)
     if args.gemm_only:
         gemm_only(args, w, mk, wl, upload, np, torch)
+        return
+    if args.reduce_scatter:
+        reduce_scatter(args, w, mk, wl, upload, np, torch)
         return
     t_gen = time.perf_counter()
     a, b, p = wl.make_inputs(w)

@@ -85,6 +85,10 @@ _vp, _i32, _i64, _u32p = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.P
 SIGNATURES = {
     "mk_gemm_reduce_local": (_i32, [_vp, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp]),
     "mk_gemm_reduce_unfused": (_i32, [_vp, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp]),
+    "mk_gemm_reduce_scatter_local": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32,
+                                             _vp]),
+    "mk_gemm_reduce_scatter_unfused": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32,
+                                               _vp]),
     "mk_set_partition": (_i32, [_i32, _i32]),
     "mk_set_controller_floor": (_i32, [_i32]),
     "mk_set_controller_cap": (_i32, [_i32]),
@@ -168,6 +172,36 @@ def gemm_reduce_unfused(A, B, peers, C, tile_m: int, tile_n: int, tiles_per_chun
                         stream=None) -> None:
     """Same result from two launches: GEMM, then reduce (mk_gemm_reduce_unfused)."""
     _call(lib.mk_gemm_reduce_unfused, A, B, peers, C, tile_m, tile_n, tiles_per_chunk, stream)
+
+
+def _call_rs(fn, A, B, peers, C, remote, tile_m, tile_n, tiles_per_chunk, stream):
+    M, N, K, P = _check_tensors(A, B, peers, C)
+    rp = None
+    if remote is not None:
+        torch = _torch()
+        if (remote.dtype != torch.float32 or not remote.is_cuda or not remote.is_contiguous()
+                or tuple(remote.shape) != (M, N)):
+            raise ValueError("remote must be a contiguous [M, N] float32 CUDA tensor")
+        rp = remote.data_ptr()
+    pp = peers.data_ptr() if (peers is not None and P > 0) else None
+    _check(fn(A.data_ptr(), B.data_ptr(), pp, P, C.data_ptr(), rp, M, N, K,
+              tile_m, tile_n, tiles_per_chunk, _stream_handle(stream)))
+
+
+def gemm_reduce_scatter_local(A, B, peers, C, remote, tile_m: int, tile_n: int, tiles_per_chunk: int = 4,
+                              stream=None) -> None:
+    """Rank 0's share of GEMM+ReduceScatter in one persistent launch
+    (mk_gemm_reduce_scatter_local): C = A.B + sum_p peers[p] on rank 0's tile
+    rows, A.B elsewhere; remote += A.B on the other ranks' rows."""
+    _call_rs(lib.mk_gemm_reduce_scatter_local, A, B, peers, C, remote, tile_m, tile_n, tiles_per_chunk,
+             stream)
+
+
+def gemm_reduce_scatter_unfused(A, B, peers, C, remote, tile_m: int, tile_n: int, tiles_per_chunk: int = 4,
+                                stream=None) -> None:
+    """Same result from two launches (mk_gemm_reduce_scatter_unfused)."""
+    _call_rs(lib.mk_gemm_reduce_scatter_unfused, A, B, peers, C, remote, tile_m, tile_n, tiles_per_chunk,
+             stream)
 
 
 def set_partition(mode, n_reduce: int = 0) -> None:

@@ -3,6 +3,7 @@
 // workspace (flags, counters, owner maps, control block), epochs, launches
 // and statistics.  Every check that can fail on the caller's arguments runs
 // before the first HIP call.
+#include <algorithm>
 #include <cstdarg>
 #include <mutex>
 #include <string>
@@ -281,10 +282,22 @@ int ensure_workspace(DevState &d, uint32_t T, uint32_t Ch, hipStream_t s) {
     return MK_OK;
 }
 
-int run(bool fused, const void *A, const void *B, const float *peers, int num_peers, float *C,
-        int64_t M, int64_t N, int64_t K, int tile_m, int tile_n, int tpc, void *stream) {
+// `rs`: one rank's share of GEMM+ReduceScatter (rank 0 of num_peers + 1):
+// tile rows [0, floor(tiles_m / R)) are reduced in place, the rest of this
+// rank's partial goes into `remote`.  Otherwise GEMM+AllReduce.
+int run(bool fused, bool rs, const void *A, const void *B, const float *peers, int num_peers, float *C,
+        float *remote, int64_t M, int64_t N, int64_t K, int tile_m, int tile_n, int tpc, void *stream) {
     int rc = check_args(A, B, peers, num_peers, C, M, N, K, tile_m, tile_n, tpc);
     if (rc) return rc;
+    if (!rs && remote) return fail(MK_ERR_INVALID_ARG, "remote is for reduce-scatter only");
+    if (rs && M > 0 && N > 0) {
+        const int64_t tm = (M + tile_m - 1) / tile_m;
+        const int64_t own = tm / (num_peers + 1);
+        if (own < tm && num_peers > 0 && !remote)
+            return fail(MK_ERR_INVALID_ARG, "remote is NULL while other ranks own tile rows");
+        if (remote && !aligned16(remote))
+            return fail(MK_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+    }
     if (M == 0 || N == 0) return MK_OK;
     const Settings set = g_set;
     DevState *dp = nullptr;
@@ -294,6 +307,7 @@ int run(bool fused, const void *A, const void *B, const float *peers, int num_pe
     hipStream_t s = (hipStream_t)stream;
 
     const int tiles_m = (int)((M + tile_m - 1) / tile_m);
+    const int own_tile_rows = rs ? tiles_m / (num_peers + 1) : tiles_m;
     const int tiles_n = (int)((N + tile_n - 1) / tile_n);
     const uint32_t T = (uint32_t)tiles_m * (uint32_t)tiles_n;
     const uint32_t Ch = (T + tpc - 1) / tpc;
@@ -320,8 +334,10 @@ int run(bool fused, const void *A, const void *B, const float *peers, int num_pe
             ReduceArgs r;
             r.peers = peers;
             r.C = C;
+            r.remote = own_tile_rows < tiles_m ? remote : nullptr;
             r.MN = M * N;
             r.count4 = M * N / 4;
+            r.own4 = std::min<int64_t>(M, (int64_t)own_tile_rows * tile_m) * N / 4;
             r.P = num_peers;
             e = launch_reduce(r, d.num_cu, s);
             if (e != hipSuccess) return hip_fail(e, "reduce launch");
@@ -426,6 +442,8 @@ int run(bool fused, const void *A, const void *B, const float *peers, int num_pe
     a.keep = keep;
     a.ns_cap = cap;
     a.xcd_cols = local ? bands : 1;
+    a.remote = own_tile_rows < tiles_m ? remote : nullptr;
+    a.own_tile_rows = own_tile_rows;
     a.timeout_ticks = set.timeout_us * (d.timer_hz / 1000000ull);
     a.skip_publish = set.skip_publish;
     a.ws = v;
@@ -460,14 +478,32 @@ int mk_gemm_reduce_local(const void *A, const void *B, const float *peers, int n
                          int64_t M, int64_t N, int64_t K, int tile_m, int tile_n,
                          int tiles_per_chunk, void *stream) {
     std::lock_guard<std::mutex> lk(g_mu);
-    return run(true, A, B, peers, num_peers, C, M, N, K, tile_m, tile_n, tiles_per_chunk, stream);
+    return run(true, false, A, B, peers, num_peers, C, nullptr, M, N, K, tile_m, tile_n, tiles_per_chunk,
+               stream);
 }
 
 int mk_gemm_reduce_unfused(const void *A, const void *B, const float *peers, int num_peers,
                            float *C, int64_t M, int64_t N, int64_t K, int tile_m, int tile_n,
                            int tiles_per_chunk, void *stream) {
     std::lock_guard<std::mutex> lk(g_mu);
-    return run(false, A, B, peers, num_peers, C, M, N, K, tile_m, tile_n, tiles_per_chunk, stream);
+    return run(false, false, A, B, peers, num_peers, C, nullptr, M, N, K, tile_m, tile_n, tiles_per_chunk,
+               stream);
+}
+
+int mk_gemm_reduce_scatter_local(const void *A, const void *B, const float *peers, int num_peers, float *C,
+                                 float *remote, int64_t M, int64_t N, int64_t K, int tile_m, int tile_n,
+                                 int tiles_per_chunk, void *stream) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    return run(true, true, A, B, peers, num_peers, C, remote, M, N, K, tile_m, tile_n, tiles_per_chunk,
+               stream);
+}
+
+int mk_gemm_reduce_scatter_unfused(const void *A, const void *B, const float *peers, int num_peers,
+                                   float *C, float *remote, int64_t M, int64_t N, int64_t K, int tile_m,
+                                   int tile_n, int tiles_per_chunk, void *stream) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    return run(false, true, A, B, peers, num_peers, C, remote, M, N, K, tile_m, tile_n, tiles_per_chunk,
+               stream);
 }
 
 int mk_set_partition(int mode, int n_reduce) {

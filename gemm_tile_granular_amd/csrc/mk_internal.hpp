@@ -91,6 +91,9 @@ struct FusedArgs {
     int32_t nxcd;             // tile partitions (XCDs) for the claim order
     int32_t local;            // 1: every tile is computed and reduced on its partition's XCD
     int32_t xcd_cols;         // local: column bands of the XCD partitions (1: whole tile rows)
+    float *remote;            // reduce-scatter: fp32 [M,N], the other ranks' outputs on their rows
+    int32_t own_tile_rows;    // tile rows [0, own) are reduced here; the rest go to `remote`
+                              // (reduce-scatter).  GEMM+AllReduce: every tile row
     int32_t keep;             // compute workgroups the controller keeps while compute remains
     int32_t ns_cap;           // most reduce workgroups the controller sets while compute remains
     uint64_t timeout_ticks;   // bound on any wait, constant-clock ticks
@@ -112,7 +115,9 @@ struct GemmArgs {
 struct ReduceArgs {
     const float *peers;
     float *C;
+    float *remote;            // reduce-scatter: receives C on elements [own4, count4)
     int64_t count4;           // M*N/4 float4 elements
+    int64_t own4;             // float4 elements reduced in place (count4 for GEMM+AllReduce)
     int64_t MN;
     int32_t P;
 };

@@ -797,6 +797,41 @@ __device__ __forceinline__ void reduce_tile(const float *__restrict__ peers, flo
     }
 }
 
+// Reduce-scatter: this rank's partial of a tile that another rank owns is
+// added into that rank's output (`remote` stands in for it), one fp32 atomic
+// add per element: the atomic add by which the pages deliver a finished tile
+// to its owner.  The tile goes in groups of four row passes, each group's
+// partial loads issued before its atomics; ragged tiles use out-of-range
+// offsets, which the atomics drop too.
+template <int TM, int BW, int NT, int kLoadPol>
+__device__ __forceinline__ void push_tile(const float *__restrict__ C, float *__restrict__ remote, int64_t M,
+                                          int64_t N, int64_t m0, int64_t n0) {
+    using RG = ReduceGeom<TM, BW, NT>;
+    constexpr int GP = RG::PASSES < 4 ? RG::PASSES : 4;
+    static_assert(RG::PASSES % GP == 0, "push layout");
+    const int tid = threadIdx.x;
+    const int cc = (tid % RG::C4) * 4;
+    const int r0 = tid / RG::C4;
+    const bool col_ok = n0 + cc < N;
+    const auto rc = scalar_rsrc(C + m0 * N + n0);
+    const auto rr = scalar_rsrc(remote + m0 * N + n0);
+    for (int g = 0; g < RG::PASSES; g += GP) {
+        f32x4 v[GP];
+        uint32_t off[GP];
+#pragma unroll
+        for (int r = 0; r < GP; ++r) {
+            const int row = (g + r) * RG::RP + r0;
+            off[r] = ((int)col_ok & (int)(m0 + row < M)) ? (uint32_t)((row * N + cc) * 4) : kOOB;
+            v[r] = __builtin_amdgcn_raw_buffer_load_b128(rc, off[r], 0, kLoadPol);
+        }
+#pragma unroll
+        for (int r = 0; r < GP; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v[r][e], rr, (int)(off[r] + 4 * e), 0, 0);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // the persistent fused kernel
 // ---------------------------------------------------------------------------
@@ -1296,7 +1331,10 @@ constexpr int fused_lds_bytes() {
     return G::LDS_BYTES > floor_bytes ? G::LDS_BYTES : floor_bytes;
 }
 
-template <int TM, int TN, bool LOCAL>
+// RS selects the reduce-scatter share: tile rows past own_tile_rows go to
+// their owners instead of being reduced here.  A separate instance keeps the
+// AllReduce kernels free of that path and of the registers it takes.
+template <int TM, int TN, bool LOCAL, bool RS>
 __global__ __launch_bounds__((GemmFor<TM, TN, kPolicyDefault>::NT),
                              (TileCfg<TM, TN>::WPC * GemmFor<TM, TN, kPolicyDefault>::NWAVES / 4))
 void fused_gemm_reduce_kernel(
@@ -1367,7 +1405,15 @@ void fused_gemm_reduce_kernel(
     // for the task after.  The counters of a reduced tile wait for the end
     // of the workgroup's next task (see CntRead).
     __shared__ uint32_t sh_pend_t0, sh_pend_n;   // reduced tiles whose counters are pending
-    if (tid == 0) sh_pend_n = 0;
+    __shared__ float *sh_remote;                 // reduce-scatter: the other ranks' outputs
+    __shared__ int32_t sh_own_tile_rows;         // tile rows reduced here
+    if (tid == 0) {
+        sh_pend_n = 0;
+        if (RS) {
+            sh_remote = a.remote;
+            sh_own_tile_rows = a.own_tile_rows;
+        }
+    }
     for (;;) {
         if (tid == 0) {
             s.decide_t0 = ticks_now();
@@ -1412,9 +1458,21 @@ void fused_gemm_reduce_kernel(
         } else {
             // thread 0 saw the flag before the barrier; the partial is read
             // with device-coherent loads, after it
-            if (a.P > 0)
-                reduce_tile<TM, TN, G::NT, H::kPartialLoad, H::kResultStore, LOCAL ? 128 : 64>(
-                    a.peers, a.C, Mp, Np, a.P, (int64_t)ti * TM, (int64_t)tj * TN);
+            if (a.P > 0) {
+                if constexpr (RS) {
+                    // read per task from LDS: kept live across the task loop,
+                    // these arguments would take registers the reduce needs
+                    if (ti < __builtin_amdgcn_readfirstlane(sh_own_tile_rows))
+                        reduce_tile<TM, TN, G::NT, H::kPartialLoad, H::kResultStore, 64>(
+                            a.peers, a.C, Mp, Np, a.P, (int64_t)ti * TM, (int64_t)tj * TN);
+                    else
+                        push_tile<TM, TN, G::NT, H::kPartialLoad>(a.C, sh_remote, Mp, Np, (int64_t)ti * TM,
+                                                                   (int64_t)tj * TN);
+                } else {
+                    reduce_tile<TM, TN, G::NT, H::kPartialLoad, H::kResultStore, LOCAL ? 128 : 64>(
+                        a.peers, a.C, Mp, Np, a.P, (int64_t)ti * TM, (int64_t)tj * TN);
+                }
+            }
             work_done(kRoleReduce);
         }
         if (tid == 0) {
@@ -1505,7 +1563,14 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
     f32x4 *C = (f32x4 *)a.C;
     const f32x4 *Pp = (const f32x4 *)a.peers;
     const int64_t MN4 = a.MN / 4;
-    for (; i + (U - 1) * stride < a.count4; i += U * stride) {
+    // reduce-scatter: elements past own4 belong to other ranks and receive
+    // this rank's partial (each by one thread, so a plain add)
+    if (a.remote)
+        for (int64_t j = a.own4 + i; j < a.count4; j += stride) {
+            f32x4 *R = (f32x4 *)a.remote;
+            __builtin_nontemporal_store(R[j] + C[j], R + j);
+        }
+    for (; i + (U - 1) * stride < a.own4; i += U * stride) {
         f32x4 acc[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) acc[u] = C[i + u * stride];
@@ -1529,7 +1594,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
 #pragma unroll
         for (int u = 0; u < U; ++u) __builtin_nontemporal_store(acc[u], C + i + u * stride);
     }
-    for (; i < a.count4; i += stride) {
+    for (; i < a.own4; i += stride) {
         f32x4 acc = C[i];
         for (int p = 0; p < a.P; ++p) acc += __builtin_nontemporal_load(Pp + (int64_t)p * MN4 + i);
         __builtin_nontemporal_store(acc, C + i);
@@ -1601,7 +1666,7 @@ template <int TM, int TN>
 static int fused_residency() {
     int blocks = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &blocks, reinterpret_cast<const void *>(&fused_gemm_reduce_kernel<TM, TN, true>),
+            &blocks, reinterpret_cast<const void *>(&fused_gemm_reduce_kernel<TM, TN, true, false>),
             GemmFor<TM, TN, kPolicyDefault>::NT, 0) != hipSuccess)
         return 0;
     return blocks < TileCfg<TM, TN>::WPC ? blocks : TileCfg<TM, TN>::WPC;
@@ -1625,14 +1690,22 @@ bool tile_supported(int tm, int tn) {
     return (tm == 64 && tn == 64) || (tm == 128 && tn == 128) || (tm == 256 && tn == 128);
 }
 
-template <int TM, int TN>
-static hipError_t launch_fused_t(const FusedArgs &a, hipStream_t s) {
+template <int TM, int TN, bool RS>
+static void launch_fused_rs(const FusedArgs &a, hipStream_t s) {
     if (a.local)
-        hipLaunchKernelGGL((fused_gemm_reduce_kernel<TM, TN, true>), dim3(a.nwg),
+        hipLaunchKernelGGL((fused_gemm_reduce_kernel<TM, TN, true, RS>), dim3(a.nwg),
                            dim3(GemmFor<TM, TN, kPolicyDefault>::NT), 0, s, a);
     else
-        hipLaunchKernelGGL((fused_gemm_reduce_kernel<TM, TN, false>), dim3(a.nwg),
+        hipLaunchKernelGGL((fused_gemm_reduce_kernel<TM, TN, false, RS>), dim3(a.nwg),
                            dim3(GemmFor<TM, TN, kPolicyDefault>::NT), 0, s, a);
+}
+
+template <int TM, int TN>
+static hipError_t launch_fused_t(const FusedArgs &a, hipStream_t s) {
+    if (a.remote)
+        launch_fused_rs<TM, TN, true>(a, s);
+    else
+        launch_fused_rs<TM, TN, false>(a, s);
     return hipGetLastError();
 }
 

@@ -124,6 +124,41 @@ int mk_gemm_reduce_unfused(const void *A, const void *B, const float *peers, int
                            int tile_m, int tile_n, int tiles_per_chunk, void *stream);
 
 /*
+ * mk_gemm_reduce_scatter_local -- one rank's share of GEMM+ReduceScatter in
+ * one persistent launch (GEMM + ReduceScatter row of the MarkTechPost page's
+ * five-kernel table; "【学习】mKernel 分析" section 2.6 and Table 3 for tiles
+ * reaching their owner by atomic add).  This rank is rank 0 of
+ * R = num_peers + 1; rank o owns tile rows [floor(o*T_m/R), floor((o+1)*T_m/R))
+ * of the T_m = ceil(M/tile_m) tile rows.  After the call:
+ *     C[i][j]      = (A.B)[i][j] + sum_p peers[p][i][j]   on rank 0's rows,
+ *                    (A.B)[i][j]                          on every other row;
+ *     remote[i][j] += (A.B)[i][j]                         on every row past
+ *                    rank 0's, each element once; rank 0's rows untouched.
+ * Only peers' rank-0 rows are read.
+ *
+ *   remote     fp32 [M, N], row-major, 16-byte aligned (device): stands in
+ *              for the other ranks' outputs.  Added into, not overwritten;
+ *              may be NULL only when rank 0 owns every tile row
+ *              (num_peers == 0, M == 0 or N == 0).  Must not overlap A, B,
+ *              peers or C.
+ *   Other arguments, layouts and errors as for mk_gemm_reduce_local; the
+ *   same partition settings and statistics apply.
+ */
+int mk_gemm_reduce_scatter_local(const void *A, const void *B, const float *peers, int num_peers,
+                                 float *C, float *remote, int64_t M, int64_t N, int64_t K,
+                                 int tile_m, int tile_n, int tiles_per_chunk, void *stream);
+
+/*
+ * mk_gemm_reduce_scatter_unfused -- the same result from two launches: the
+ * GEMM kernel writes the partial into C, then one elementwise kernel reduces
+ * rank 0's rows and adds the other rows into `remote` (plain adds: each
+ * element is written by one thread).  Arguments as above.
+ */
+int mk_gemm_reduce_scatter_unfused(const void *A, const void *B, const float *peers, int num_peers,
+                                   float *C, float *remote, int64_t M, int64_t N, int64_t K,
+                                   int tile_m, int tile_n, int tiles_per_chunk, void *stream);
+
+/*
  * mk_set_partition -- partition of the persistent workgroups into reduce and
  * compute roles for subsequent mk_gemm_reduce_local launches (process-wide).
  *   mode       mk_part_mode.

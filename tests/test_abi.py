@@ -109,6 +109,42 @@ def test_argument_errors_before_any_gpu_call(mk, kw, code):
                                          args["tn"], args["tpc"], None) == code
 
 
+R = 0x50000   # fake remote output
+
+
+def _call_rs(mk, fused=True, **kw):
+    args = dict(A=A, B=B, peers=P, num_peers=3, C=C, remote=R, M=256, N=256, K=512, tm=64, tn=64, tpc=4)
+    args.update(kw)
+    fn = mk.lib.mk_gemm_reduce_scatter_local if fused else mk.lib.mk_gemm_reduce_scatter_unfused
+    return fn(args["A"], args["B"], args["peers"], args["num_peers"], args["C"], args["remote"], args["M"],
+              args["N"], args["K"], args["tm"], args["tn"], args["tpc"], None)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), -1), (dict(tm=128, tn=64), -1), (dict(tpc=0), -1), (dict(N=260), -2),
+    (dict(C=0), -1), (dict(peers=0), -1), (dict(A=A + 8), -1),
+    (dict(remote=0), -1),                     # other ranks own tile rows: remote is needed
+    (dict(remote=R + 4), -1),                 # misaligned
+])
+def test_reduce_scatter_argument_errors(mk, fused, kw, code):
+    assert _call_rs(mk, fused, **kw) == code
+    assert mk.lib.mk_last_error().decode()
+
+
+def test_reduce_scatter_empty_output_is_a_no_op(mk):
+    assert _call_rs(mk, M=0, remote=0) == 0
+    assert _call_rs(mk, fused=False, N=0, remote=0) == 0
+
+
+@pytest.mark.skipif(_gpu_present(), reason="fake pointers must never reach a real GPU")
+def test_reduce_scatter_one_rank_needs_no_remote(mk):
+    # R = 1: rank 0 owns every row, so remote may be NULL; the call gets as
+    # far as looking for a device
+    assert _call_rs(mk, peers=0, num_peers=0, remote=0) == mk.MK_ERR_NO_DEVICE
+    assert _call_rs(mk) == mk.MK_ERR_NO_DEVICE
+
+
 def test_empty_output_is_a_no_op(mk):
     assert _call(mk, M=0) == 0
     assert _call(mk, N=0) == 0
@@ -176,7 +212,7 @@ def test_kernels_fit_their_register_and_lds_budget(mk):
         res = json.load(f)
     fused = {k: v for k, v in res.items() if "fused_gemm_reduce_kernel" in k}
     gemm = {k: v for k, v in res.items() if "gemm_kernel" in k and k not in fused}
-    assert len(fused) == 6 and len(gemm) == 3, sorted(res)
+    assert len(fused) == 12 and len(gemm) == 3, sorted(res)
     for name, r in res.items():
         assert r["LDS Size"] <= 160 * 1024, name
         assert r["ScratchSize"] == 0, (name, r)

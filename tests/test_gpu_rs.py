@@ -1,0 +1,153 @@
+"""GPU parity for one rank's share of GEMM+ReduceScatter: the fused and unfused
+entry points (through the C ABI) against oracle.gemm_reduce_scatter.
+
+C on this rank's tile rows and the other ranks' output (`remote`) on theirs:
+max|X - X_ref| <= 2e-3 max|X_ref|, with the GEMM part checked on its own
+(C - sum(peers) on the own rows, remote - remote_init elsewhere).  Rank 0's
+rows of `remote`: bit-exact, untouched.  Fused and unfused: bit-identical
+(the same GEMM core, the same order of additions).  Protocol state:
+bit-exact against its closed forms.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from gpu_util import REL_TOL, check_full, check_protocol
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mk():
+    import gemm_tile_granular_amd as mk
+    mk.set_num_workgroups(0)
+    mk.set_timeout_us(2_000_000)
+    mk.set_fault_skip_publish(-1)
+    mk.set_controller_floor(2)
+    mk.set_controller_cap(0)
+    mk.set_xcd_bands(0)
+    yield mk
+    mk.set_partition("adaptive", 0)
+
+
+def run_rs(mk, fused, w, a, b, p, r0, mode="adaptive", n_reduce=3):
+    import torch
+    from gemm_tile_granular_amd.tensors import upload
+    A, B, P, C = upload(a, b, p)
+    R = torch.from_numpy(np.ascontiguousarray(r0)).to(C.device)
+    print(f"[gpu] rs {'fused' if fused else 'unfused'} {w.M}x{w.N}x{w.K} P={w.peers} "
+          f"tile {w.tile_m}x{w.tile_n} tpc {w.tiles_per_chunk} mode {mode}", flush=True)
+    st = None
+    if fused:
+        mk.set_partition(mode, n_reduce)
+        mk.gemm_reduce_scatter_local(A, B, P, C, R, w.tile_m, w.tile_n, w.tiles_per_chunk)
+        st = mk.get_stats(maps=True)
+    else:
+        mk.gemm_reduce_scatter_unfused(A, B, P, C, R, w.tile_m, w.tile_n, w.tiles_per_chunk)
+    torch.cuda.synchronize()
+    return C.cpu().numpy(), R.cpu().numpy(), st
+
+
+def own_rows(w):
+    tiles_m = -(-w.M // w.tile_m)
+    return min(w.M, int(oracle.rs_shard_bounds(tiles_m, w.peers + 1)[1]) * w.tile_m)
+
+
+def check_rs_full(C, remote, a, b, p, r0, w):
+    M, N = C.shape
+    own = own_rows(w)
+    Cref, Rref = oracle.gemm_reduce_scatter(a, b, p, r0, w.tile_m)
+    # whole outputs against the oracle
+    for got, ref, name in ((C, Cref, "C"), (remote, Rref, "remote")):
+        err = float(np.max(np.abs(got.astype(np.float64) - ref)))
+        bound = REL_TOL * float(np.max(np.abs(ref)))
+        assert err <= bound, f"max|{name}-ref| = {err:.4e} > {bound:.4e}"
+    # the parts: own rows reduced, other rows this rank's partial
+    if own:
+        check_full(C[:own], a[:own], b, np.ascontiguousarray(p[:, :own]))
+    if own < M:
+        empty = np.zeros((0, M - own, N), np.float32)
+        check_full(C[own:], a[own:], b, empty)
+        part = oracle.gemm_part(a[own:], b)
+        gerr = float(np.max(np.abs((remote[own:].astype(np.float64) - r0[own:]) - part)))
+        gmax = float(np.max(np.abs(part)))
+        # remote = fl(r0 + partial): one more rounding of |r0 + partial|
+        slack = 2.0 ** -23 * float(np.max(np.abs(Rref[own:])))
+        assert gerr <= REL_TOL * gmax + slack, f"remote GEMM part {gerr:.4e}"
+    # rank 0's rows of the other ranks' output are never touched
+    assert np.array_equal(remote[:own], r0[:own])
+
+
+RS_SHAPES = [
+    # M, N, K, P, tile_m, tile_n, tpc -- R = P + 1 ranks; ragged M/N/K tails
+    (200, 136, 72, 3, 64, 64, 4),        # 4 tile rows, one per rank
+    (333, 264, 136, 2, 128, 128, 4),     # 3 tile rows, R = 3
+    (520, 392, 200, 5, 256, 128, 3),     # 3 tile rows, R = 6: rank 0 owns none
+    (1100, 264, 200, 1, 128, 128, 4),    # 9 tile rows, R = 2: own 4, ragged last row sent
+    (1000, 1000, 1024, 3, 128, 128, 4),  # fast K loop, 2 of 8 tile rows own
+    (600, 520, 512, 2, 256, 128, 4),
+    (300, 328, 512, 7, 64, 64, 4),       # 5 tile rows, R = 8: own none
+    (130, 520, 8, 1, 64, 64, 1),         # one K slab
+]
+
+
+@pytest.mark.parametrize("shape", RS_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("mode", ["adaptive", "deterministic"])
+def test_reduce_scatter_full_oracle(mk, shape, mode):
+    M, N, K, P, tm, tn, tpc = shape
+    w = wl.custom(M, N, K, P, tm, tn, tpc, wid=700 + M % 89)
+    a, b, p = wl.make_inputs(w)
+    r0 = wl.make_remote(w)
+    C, R, st = run_rs(mk, True, w, a, b, p, r0, mode=mode)
+    check_rs_full(C, R, a, b, p, r0, w)
+    check_protocol(st, w, mode, 3)
+    Cu, Ru, _ = run_rs(mk, False, w, a, b, p, r0)
+    assert np.array_equal(C, Cu)
+    assert np.array_equal(R, Ru)
+
+
+def test_reduce_scatter_one_rank_is_the_gemm(mk):
+    # R = 1: rank 0 owns every row; no remote buffer
+    import torch
+    from gemm_tile_granular_amd.tensors import upload
+    w = wl.custom(300, 200, 264, 0, 128, 128, 4, wid=790)
+    a, b, p = wl.make_inputs(w)
+    A, B, P, C = upload(a, b, p)
+    mk.set_partition("static", 4)
+    mk.gemm_reduce_scatter_local(A, B, None, C, None, 128, 128, 4)
+    torch.cuda.synchronize()
+    check_full(C.cpu().numpy(), a, b, p)
+
+
+def test_reduce_scatter_full_size_sampled(mk):
+    """The 4096x4096x1792, 8-rank tensor-parallel share at full size, in the
+    launch the bench times: sampled elements against the oracle one at a
+    time, the untouched rows bit-exact, and fused equal to unfused
+    everywhere."""
+    w = wl.workload("tp_share")
+    a, b, p = wl.make_inputs(w)
+    r0 = wl.make_remote(w)
+    C, R, st = run_rs(mk, True, w, a, b, p, r0, mode="adaptive")
+    check_protocol(st, w, "adaptive", 3)
+    own = own_rows(w)
+    rng = np.random.default_rng(11)
+    for lo, hi, reduced in ((0, own, True), (own, w.M, False)):
+        if lo == hi:
+            continue
+        rows = rng.integers(lo, hi, 2048)
+        cols = rng.integers(0, w.N, 2048)
+        ref, gemm = oracle.gemm_reduce_at(a, b, p, rows, cols)
+        scale = float(np.max(np.abs(ref if reduced else gemm)))
+        gotC = C[rows, cols].astype(np.float64)
+        if reduced:
+            err = float(np.max(np.abs(gotC - ref)))
+        else:
+            err = float(np.max(np.abs(gotC - gemm)))
+            gotR = R[rows, cols].astype(np.float64) - r0[rows, cols]
+            err = max(err, float(np.max(np.abs(gotR - gemm))) - 2.0 ** -22 * scale)
+        assert err <= REL_TOL * scale, (lo, hi, err, scale)
+    assert np.array_equal(R[:own], r0[:own])
+    Cu, Ru, _ = run_rs(mk, False, w, a, b, p, r0)
+    assert np.array_equal(C, Cu)
+    assert np.array_equal(R, Ru)

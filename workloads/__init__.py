@@ -180,3 +180,10 @@ def make_inputs(w: Workload, seed: int = DEFAULT_SEED, threads: Optional[int] = 
             for p in range(P):
                 fill(p)
     return a, b, peers
+
+
+def make_remote(w: Workload, seed: int = DEFAULT_SEED) -> np.ndarray:
+    """Draw the initial contents [M,N] float32 of the buffer that stands in
+    for the other ranks' outputs in GEMM+ReduceScatter (the peers'
+    distribution, a stream of its own after every peer's)."""
+    return _draw(_rng(seed, w.wid, 2 + w.peers), (w.M, w.N), w.dist_peer)
