@@ -21,13 +21,17 @@ What it computes, and from which passage:
   GEMM+ReduceScatter (GEMM + ReduceScatter row of the five-kernel table on the
   MarkTechPost page: C = A @ B is computed and each output tile is reduced and
   sent to the rank that owns it as soon as it exists; "【学习】mKernel 分析"
-  section 2.6, Table 3: tiles reach their rank by atomic add, in chunks of 2
-  to 32 tiles).  The pages fix no shard layout.  The reading used: R = P + 1
-  ranks, this rank is rank 0, and rank o owns tile rows [floor(o T_m / R),
-  floor((o+1) T_m / R)) of the T_m tile rows.  Rank 0's own rows receive the
-  other ranks' partials (the peers stand in for them); every other tile of
-  this rank's partial is added into its owner's output, which a buffer in
-  local memory stands in for.
+  section 2.6, Table 3: tiles reach their rank in chunks of 2 to 32 tiles).
+  The pages fix no shard layout.  The reading used: R = P + 1 ranks, this
+  rank is rank 0, and rank o owns tile rows [floor(o T_m / R),
+  floor((o+1) T_m / R)) of the T_m tile rows.  Each owner keeps an inbox with
+  one slot per other rank; a rank stores each finished tile it does not own
+  into its slot at the owner, and the owner sums its own partial and its
+  inbox.  Here rank 0's inbox is the peers (its own rows receive their sum),
+  and a buffer in local memory stands in for rank 0's slots at the other
+  owners: every tile of this rank's partial outside its rows is stored
+  there.  (The analysis page delivers tiles by atomic add into the owner's
+  output instead; the owner's reduced shard is the same sum either way.)
 * `controller_update` / `controller_target` -- the adaptive partition rule of
   "【学习】mKernel 分析" section 2.4: the target number of communication
   (here: reduce) workgroups n_s* = B (R_s C_s) / (R_p C_p + R_s C_s), the value
@@ -147,8 +151,9 @@ def gemm_reduce_scatter(a_bits: np.ndarray, b_bits: np.ndarray, peers: np.ndarra
     Returns (C, remote), both [M,N]:
     - C: on rank 0's rows, A.B + sum_p peers[p] (its reduced shard); on every
       other row, A.B (this rank's partial, left where it was computed);
-    - remote: remote_init + A.B on the rows of ranks 1..R-1 (each tile added
-      once into its owner's output), remote_init on rank 0's rows.
+    - remote: A.B on the rows of ranks 1..R-1 (this rank's inbox slot at each
+      owner receives its partial of that owner's tiles), remote_init on rank
+      0's rows (never written).
     """
     a = np.asarray(a_bits)
     b = np.asarray(b_bits)
@@ -168,7 +173,7 @@ def gemm_reduce_scatter(a_bits: np.ndarray, b_bits: np.ndarray, peers: np.ndarra
     if P:
         C[own_rows] += peer_sum(peers[:, own_rows, :])
     remote = remote_init.astype(np.float64).copy()
-    remote[own_rows.stop:] += part[own_rows.stop:]
+    remote[own_rows.stop:] = part[own_rows.stop:]
     return C, remote
 
 

@@ -2,8 +2,8 @@
 
 Rank 0 of R = P + 1 ranks: tile rows are cut into R shards (rank o owns tile
 rows [floor(o T_m / R), floor((o+1) T_m / R))); rank 0's rows get A.B plus the
-other ranks' partials (the peers), every other tile of A.B is added once into
-its owner's output (a stand-in buffer).  Pins: hand-worked shard bounds, an
+other ranks' partials (the peers, its inbox), every other tile of A.B is
+stored into this rank's inbox slot at its owner (a stand-in buffer).  Pins: hand-worked shard bounds, an
 integer hand example checked with exact integer arithmetic, closed forms (one
 rank, A = 0), the independent C brute force, the shard cover invariant, and
 planted mistakes that must each fail a pin.
@@ -55,7 +55,7 @@ def pin_rs_hand_example(fn):
     ab = [[sum(int(ai[i, k]) * int(bi[k, j]) for k in range(5)) for j in range(4)] for i in range(6)]
     wantC = [[ab[i][j] + (int(pi[0, i, j]) + int(pi[1, i, j]) if i < 2 else 0) for j in range(4)]
              for i in range(6)]
-    wantR = [[int(ri[i, j]) + (ab[i][j] if i >= 2 else 0) for j in range(4)] for i in range(6)]
+    wantR = [[ab[i][j] if i >= 2 else int(ri[i, j]) for j in range(4)] for i in range(6)]
     return np.array_equal(C, np.array(wantC)) and np.array_equal(R, np.array(wantR))
 
 
@@ -77,7 +77,9 @@ def pin_rs_zero_a(fn):
     C, R = fn(np.zeros((8, 6), np.uint16), b, peers, init, 2)
     want = np.zeros((8, 5))
     want[:2] = peers[:, :2].astype(np.float64).sum(0)
-    return np.allclose(C, want, rtol=0, atol=1e-12) and np.array_equal(R, init.astype(np.float64))
+    wantR = np.zeros((8, 5))
+    wantR[:2] = init[:2]
+    return np.allclose(C, want, rtol=0, atol=1e-12) and np.array_equal(R, wantR)
 
 
 def pin_rs_brute_force(fn):
@@ -92,7 +94,7 @@ def pin_rs_brute_force(fn):
         wantC = ab.copy()
         wantC[:own] = full[:own]
         wantR = init.astype(np.float64)
-        wantR[own:] += ab[own:]
+        wantR[own:] = ab[own:]
         if not (np.allclose(C, wantC, rtol=1e-12, atol=1e-12) and np.allclose(R, wantR, rtol=1e-12, atol=1e-12)):
             return False
     return True
@@ -106,7 +108,8 @@ def test_rs_oracle_meets_pin(pin):
     assert pin(oracle.gemm_reduce_scatter)
 
 
-def _rs_mutant(own_shard=0, init=True, remote_everywhere=False, peers_everywhere=False, ceil=False):
+def _rs_mutant(own_shard=0, init=True, remote_everywhere=False, peers_everywhere=False, ceil=False,
+               add=False):
     def fn(a, b, p, r0, tm):
         M = a.shape[0]
         P = p.shape[0]
@@ -128,14 +131,18 @@ def _rs_mutant(own_shard=0, init=True, remote_everywhere=False, peers_everywhere
         mask = np.ones(M, bool)
         if not remote_everywhere:
             mask[lo:hi] = False
-        Rm[mask] += ab[mask]
+        if add:
+            Rm[mask] += ab[mask]
+        else:
+            Rm[mask] = ab[mask]
         return C, Rm
     return fn
 
 
 RS_MUTANTS = {
     "owns_the_last_shard": lambda a, b, p, r0, tm: _rs_mutant(own_shard=max(0, p.shape[0]))(a, b, p, r0, tm),
-    "remote_drops_its_initial_value": _rs_mutant(init=False),
+    "own_rows_of_remote_cleared": _rs_mutant(init=False),
+    "partial_added_into_remote": _rs_mutant(add=True),
     "own_rows_also_sent": _rs_mutant(remote_everywhere=True),
     "peers_added_to_every_row": _rs_mutant(peers_everywhere=True),
     "shard_bounds_rounded_up": _rs_mutant(ceil=True),
