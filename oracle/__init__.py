@@ -30,8 +30,10 @@ What it computes, and from which passage:
   inbox.  Here rank 0's inbox is the peers (its own rows receive their sum),
   and a buffer in local memory stands in for rank 0's slots at the other
   owners: every tile of this rank's partial outside its rows is stored
-  there.  (The analysis page delivers tiles by atomic add into the owner's
-  output instead; the owner's reduced shard is the same sum either way.)
+  there.  A rank's output is its shard only; its partial of the other rows
+  is not kept.  (The analysis page delivers tiles by atomic add into the
+  owner's output instead; the owner's reduced shard is the same sum either
+  way.)
 * `controller_update` / `controller_target` -- the adaptive partition rule of
   "【学习】mKernel 分析" section 2.4: the target number of communication
   (here: reduce) workgroups n_s* = B (R_s C_s) / (R_p C_p + R_s C_s), the value
@@ -148,12 +150,12 @@ def gemm_reduce_scatter(a_bits: np.ndarray, b_bits: np.ndarray, peers: np.ndarra
                         remote_init: np.ndarray, tile_m: int) -> Tuple[np.ndarray, np.ndarray]:
     """Rank 0's share of GEMM+ReduceScatter with R = P + 1 ranks, float64.
 
-    Returns (C, remote), both [M,N]:
-    - C: on rank 0's rows, A.B + sum_p peers[p] (its reduced shard); on every
-      other row, A.B (this rank's partial, left where it was computed);
-    - remote: A.B on the rows of ranks 1..R-1 (this rank's inbox slot at each
-      owner receives its partial of that owner's tiles), remote_init on rank
-      0's rows (never written).
+    Returns (shard, remote):
+    - shard [own, N], own = min(M, floor(T_m / R) tile_m): rows [0, own) of
+      A.B + sum_p peers[p], rank 0's reduced shard;
+    - remote [M, N]: A.B on the rows of ranks 1..R-1 (this rank's inbox slot
+      at each owner receives its partial of that owner's tiles), remote_init
+      on rank 0's rows (never written).
     """
     a = np.asarray(a_bits)
     b = np.asarray(b_bits)
@@ -169,12 +171,12 @@ def gemm_reduce_scatter(a_bits: np.ndarray, b_bits: np.ndarray, peers: np.ndarra
     bounds = rs_shard_bounds(tiles_m, P + 1)
     own_rows = slice(0, min(M, int(bounds[1]) * tile_m))
     part = gemm_part(a, b)
-    C = part.copy()
+    shard = part[own_rows].copy()
     if P:
-        C[own_rows] += peer_sum(peers[:, own_rows, :])
+        shard += peer_sum(peers[:, own_rows, :])
     remote = remote_init.astype(np.float64).copy()
     remote[own_rows.stop:] = part[own_rows.stop:]
-    return C, remote
+    return shard, remote
 
 
 # ---------------------------------------------------------------------------
