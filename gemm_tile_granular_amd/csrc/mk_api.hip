@@ -283,8 +283,10 @@ int ensure_workspace(DevState &d, uint32_t T, uint32_t Ch, hipStream_t s) {
 }
 
 // `rs`: one rank's share of GEMM+ReduceScatter (rank 0 of num_peers + 1):
-// tile rows [0, floor(tiles_m / R)) are reduced in place, the rest of this
-// rank's partial goes into `remote`.  Otherwise GEMM+AllReduce.
+// tile rows [0, floor(tiles_m / R)) are computed into C and reduced there;
+// the GEMM stores every other tile row straight into `remote` (this rank's
+// inbox slots at the other owners) and leaves those rows of C untouched.
+// Otherwise GEMM+AllReduce.
 int run(bool fused, bool rs, const void *A, const void *B, const float *peers, int num_peers, float *C,
         float *remote, int64_t M, int64_t N, int64_t K, int tile_m, int tile_n, int tpc, void *stream) {
     int rc = check_args(A, B, peers, num_peers, C, M, N, K, tile_m, tile_n, tpc);
@@ -306,13 +308,14 @@ int run(bool fused, bool rs, const void *A, const void *B, const float *peers, i
     DevState &d = *dp;
     hipStream_t s = (hipStream_t)stream;
 
-    const int tiles_m = (int)((M + tile_m - 1) / tile_m);
-    const int own_tile_rows = rs ? tiles_m / (num_peers + 1) : tiles_m;
+    const int tiles_m_all = (int)((M + tile_m - 1) / tile_m);
+    const int own_tile_rows = rs ? tiles_m_all / (num_peers + 1) : tiles_m_all;
     const int tiles_n = (int)((N + tile_n - 1) / tile_n);
-    const uint32_t T = (uint32_t)tiles_m * (uint32_t)tiles_n;
-    const uint32_t Ch = (T + tpc - 1) / tpc;
 
-    if (!fused) {
+    // A rank that owns no tile row has nothing to reduce: the GEMM alone
+    // stores every tile into the other owners' inboxes.
+    if (!fused || own_tile_rows == 0) {
+        const int tiles_m = tiles_m_all;
         GemmArgs g;
         g.A = (const uint16_t *)A;
         g.B = (const uint16_t *)B;
@@ -324,17 +327,18 @@ int run(bool fused, bool rs, const void *A, const void *B, const float *peers, i
         g.tiles_n = tiles_n;
         g.tpc = tpc;
         g.group_m = set.group_m;
+        g.own_tile_rows = own_tile_rows;
+        g.remote = own_tile_rows < tiles_m ? remote : nullptr;
         g.nxcd = xcd_partitions(d.num_cu, d.num_cu);
         g.xcd_cols = g.nxcd == kMaxXcd
                          ? gemm_xcd_bands(g.nxcd, tiles_m, tiles_n, tile_m, tile_n, tpc, set.xcd_bands)
                          : 1;
         hipError_t e = launch_gemm(tile_m, tile_n, g, d.num_cu, s);
         if (e != hipSuccess) return hip_fail(e, "GEMM launch");
-        if (num_peers > 0) {
+        if (num_peers > 0 && own_tile_rows > 0) {
             ReduceArgs r;
             r.peers = peers;
             r.C = C;
-            r.remote = own_tile_rows < tiles_m ? remote : nullptr;
             r.MN = M * N;
             r.count4 = M * N / 4;
             r.own4 = std::min<int64_t>(M, (int64_t)own_tile_rows * tile_m) * N / 4;
@@ -344,6 +348,14 @@ int run(bool fused, bool rs, const void *A, const void *B, const float *peers, i
         }
         return MK_OK;
     }
+
+    // The fused protocol (flags, chunks, reduce tasks, controller) covers the
+    // rows this rank reduces: all of them for GEMM+AllReduce, its shard for
+    // reduce-scatter, whose other rows are plain GEMM blocks.
+    const int tiles_m = own_tile_rows;
+    const int64_t Mf = std::min<int64_t>(M, (int64_t)tiles_m * tile_m);
+    const uint32_t T = (uint32_t)tiles_m * (uint32_t)tiles_n;
+    const uint32_t Ch = (T + tpc - 1) / tpc;
 
     // every workgroup of the persistent grid must be resident at once
     const int per_cu = workgroups_per_cu(tile_m, tile_n);
@@ -420,7 +432,7 @@ int run(bool fused, bool rs, const void *A, const void *B, const float *peers, i
     a.B = (const uint16_t *)B;
     a.peers = peers;
     a.C = C;
-    a.M = M;
+    a.M = Mf;
     a.N = N;
     a.K = K;
     a.P = num_peers;
@@ -442,8 +454,10 @@ int run(bool fused, bool rs, const void *A, const void *B, const float *peers, i
     a.keep = keep;
     a.ns_cap = cap;
     a.xcd_cols = local ? bands : 1;
-    a.remote = own_tile_rows < tiles_m ? remote : nullptr;
-    a.own_tile_rows = own_tile_rows;
+    a.remote = own_tile_rows < tiles_m_all ? remote : nullptr;
+    a.M_all = M;
+    a.tiles_m_all = tiles_m_all;
+    a.peer_mn = M * N;
     a.timeout_ticks = set.timeout_us * (d.timer_hz / 1000000ull);
     a.skip_publish = set.skip_publish;
     a.ws = v;

@@ -36,6 +36,7 @@ template <class T> struct alignas(256) Line {
 struct alignas(256) Live {
     Line<uint32_t> compute_claim[kMaxXcd];  // next compute claim per partition (init 0)
     Line<uint32_t> reduce_claim[kMaxXcd];   // next reduce ticket per partition (init 0)
+    Line<uint32_t> extra_claim;    // next reduce-scatter GEMM block outside the shard (init 0)
     Line<uint64_t> role_compute;   // (cycles << kCountBits) | tasks      (init 0)
     Line<uint64_t> role_reduce;    //                                     (init 0)
     Line<uint32_t> target_ns;      // controller target, 0 = unset        (init 0)
@@ -91,9 +92,15 @@ struct FusedArgs {
     int32_t nxcd;             // tile partitions (XCDs) for the claim order
     int32_t local;            // 1: every tile is computed and reduced on its partition's XCD
     int32_t xcd_cols;         // local: column bands of the XCD partitions (1: whole tile rows)
-    float *remote;            // reduce-scatter: fp32 [M,N], the other ranks' outputs on their rows
-    int32_t own_tile_rows;    // tile rows [0, own) are reduced here; the rest go to `remote`
-                              // (reduce-scatter).  GEMM+AllReduce: every tile row
+    // reduce-scatter: M and tiles_m above are this rank's shard, the
+    // protocol's whole extent; tile rows [tiles_m, tiles_m_all) of the
+    // [M_all, N] product are plain GEMM blocks stored into `remote` (this
+    // rank's inbox slots at the other owners).  GEMM+AllReduce: remote is
+    // NULL and M_all == M.
+    float *remote;
+    int64_t M_all;
+    int32_t tiles_m_all;
+    int64_t peer_mn;          // elements between consecutive peers ([P, M_all, N])
     int32_t keep;             // compute workgroups the controller keeps while compute remains
     int32_t ns_cap;           // most reduce workgroups the controller sets while compute remains
     uint64_t timeout_ticks;   // bound on any wait, constant-clock ticks
@@ -110,14 +117,15 @@ struct GemmArgs {
     int32_t tpc, group_m;
     int32_t nxcd;
     int32_t xcd_cols;         // column bands of the partitions (1: whole tile rows)
+    int32_t own_tile_rows;    // tile rows [0, own) go to C, the rest to `remote` (reduce-scatter)
+    float *remote;            // reduce-scatter: this rank's inbox slots at the other owners
 };
 
 struct ReduceArgs {
     const float *peers;
     float *C;
-    float *remote;            // reduce-scatter: receives C on elements [own4, count4)
     int64_t count4;           // M*N/4 float4 elements
-    int64_t own4;             // float4 elements reduced in place (count4 for GEMM+AllReduce)
+    int64_t own4;             // float4 elements reduced (the first own4; count4 for GEMM+AllReduce)
     int64_t MN;
     int32_t P;
 };

@@ -687,9 +687,11 @@ struct ReduceGroup {
 };
 
 // Region of TM rows x BW columns at (m0, n0): the tiles of one compute block.
+// Rows past M are masked; peer p's partial starts p*MN elements into peers.
 template <int TM, int BW, int NT, int PP, int kLoadPol, int kStorePol, int KIB>
 __device__ __forceinline__ void reduce_tile_pp(const float *__restrict__ peers, float *__restrict__ C,
-                                               int64_t M, int64_t N, int P, int64_t m0, int64_t n0) {
+                                               int64_t M, int64_t N, int64_t MN, int P, int64_t m0,
+                                               int64_t n0) {
     using RG = ReduceGeom<TM, BW, NT>;
     constexpr int PB = 8;                   // peer block when PP is the generic 0
     constexpr int UP = ReducePlan<(PP > 0 ? PP : PB), NT, KIB>::U;
@@ -698,7 +700,6 @@ __device__ __forceinline__ void reduce_tile_pp(const float *__restrict__ peers, 
     static_assert(RG::PASSES % U == 0, "reduce layout");
     const int tid = threadIdx.x;
     const int64_t base = m0 * N + n0;
-    const int64_t MN = M * N;
     const int cc = (tid % RG::C4) * 4;
     const int r0 = tid / RG::C4;
     const bool col_ok = n0 + cc < N;
@@ -787,48 +788,13 @@ __device__ __forceinline__ void reduce_tile_pp(const float *__restrict__ peers, 
 // pipelined code; other counts take the blocked loop.
 template <int TM, int BW, int NT, int kLoadPol, int kStorePol, int KIB>
 __device__ __forceinline__ void reduce_tile(const float *__restrict__ peers, float *__restrict__ C,
-                                            int64_t M, int64_t N, int P, int64_t m0, int64_t n0) {
+                                            int64_t M, int64_t N, int64_t MN, int P, int64_t m0, int64_t n0) {
     switch (P) {
 #define MK_REDUCE_CASE(k) \
-    case k: reduce_tile_pp<TM, BW, NT, k, kLoadPol, kStorePol, KIB>(peers, C, M, N, P, m0, n0); break;
+    case k: reduce_tile_pp<TM, BW, NT, k, kLoadPol, kStorePol, KIB>(peers, C, M, N, MN, P, m0, n0); break;
         MK_REDUCE_CASE(1) MK_REDUCE_CASE(3) MK_REDUCE_CASE(7) MK_REDUCE_CASE(15)
 #undef MK_REDUCE_CASE
-        default: reduce_tile_pp<TM, BW, NT, 0, kLoadPol, kStorePol, KIB>(peers, C, M, N, P, m0, n0); break;
-    }
-}
-
-// Reduce-scatter: this rank's partial of a tile that another rank owns is
-// added into that rank's output (`remote` stands in for it), one fp32 atomic
-// add per element: the atomic add by which the pages deliver a finished tile
-// to its owner.  The tile goes in groups of four row passes, each group's
-// partial loads issued before its atomics; ragged tiles use out-of-range
-// offsets, which the atomics drop too.
-template <int TM, int BW, int NT, int kLoadPol>
-__device__ __forceinline__ void push_tile(const float *__restrict__ C, float *__restrict__ remote, int64_t M,
-                                          int64_t N, int64_t m0, int64_t n0) {
-    using RG = ReduceGeom<TM, BW, NT>;
-    constexpr int GP = RG::PASSES < 4 ? RG::PASSES : 4;
-    static_assert(RG::PASSES % GP == 0, "push layout");
-    const int tid = threadIdx.x;
-    const int cc = (tid % RG::C4) * 4;
-    const int r0 = tid / RG::C4;
-    const bool col_ok = n0 + cc < N;
-    const auto rc = scalar_rsrc(C + m0 * N + n0);
-    const auto rr = scalar_rsrc(remote + m0 * N + n0);
-    for (int g = 0; g < RG::PASSES; g += GP) {
-        f32x4 v[GP];
-        uint32_t off[GP];
-#pragma unroll
-        for (int r = 0; r < GP; ++r) {
-            const int row = (g + r) * RG::RP + r0;
-            off[r] = ((int)col_ok & (int)(m0 + row < M)) ? (uint32_t)((row * N + cc) * 4) : kOOB;
-            v[r] = __builtin_amdgcn_raw_buffer_load_b128(rc, off[r], 0, kLoadPol);
-        }
-#pragma unroll
-        for (int r = 0; r < GP; ++r)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v[r][e], rr, (int)(off[r] + 4 * e), 0, 0);
+        default: reduce_tile_pp<TM, BW, NT, 0, kLoadPol, kStorePol, KIB>(peers, C, M, N, MN, P, m0, n0); break;
     }
 }
 
@@ -1206,6 +1172,7 @@ __device__ void finish_launch(const FusedArgs &a, Live *L) {
         st_relaxed(&L->compute_claim[x].v, 0u);
         st_relaxed(&L->reduce_claim[x].v, 0u);
     }
+    st_relaxed(&L->extra_claim.v, 0u);
     st_relaxed(&L->target_ns.v, 0u);
     st_relaxed(&L->role_switches, 0u);
     st_relaxed(&L->chunks_released.v, 0u);
@@ -1331,9 +1298,11 @@ constexpr int fused_lds_bytes() {
     return G::LDS_BYTES > floor_bytes ? G::LDS_BYTES : floor_bytes;
 }
 
-// RS selects the reduce-scatter share: tile rows past own_tile_rows go to
-// their owners instead of being reduced here.  A separate instance keeps the
-// AllReduce kernels free of that path and of the registers it takes.
+// RS selects the reduce-scatter share: the protocol covers this rank's shard
+// (M, tiles_m), and once a workgroup has no task left in it, it computes the
+// other ranks' tile rows as plain GEMM blocks into their inbox slots.  A
+// separate instance keeps the AllReduce kernels free of that path and of the
+// registers it takes.
 template <int TM, int TN, bool LOCAL, bool RS>
 __global__ __launch_bounds__((GemmFor<TM, TN, kPolicyDefault>::NT),
                              (TileCfg<TM, TN>::WPC * GemmFor<TM, TN, kPolicyDefault>::NWAVES / 4))
@@ -1405,15 +1374,30 @@ void fused_gemm_reduce_kernel(
     // for the task after.  The counters of a reduced tile wait for the end
     // of the workgroup's next task (see CntRead).
     __shared__ uint32_t sh_pend_t0, sh_pend_n;   // reduced tiles whose counters are pending
-    __shared__ float *sh_remote;                 // reduce-scatter: the other ranks' outputs
-    __shared__ int32_t sh_own_tile_rows;         // tile rows reduced here
-    if (tid == 0) {
-        sh_pend_n = 0;
-        if (RS) {
-            sh_remote = a.remote;
-            sh_own_tile_rows = a.own_tile_rows;
-        }
-    }
+    if (tid == 0) sh_pend_n = 0;
+    // reduce-scatter: the other ranks' tile rows, plain GEMM blocks claimed
+    // one at a time, row by row, each stored straight into this rank's inbox
+    // slot at its owner
+    const uint32_t extra_row0 = (uint32_t)a.tiles_m;
+    const uint32_t n_extra = RS ? ((uint32_t)a.tiles_m_all - extra_row0) * bk.bn : 0u;
+    __shared__ uint32_t sh_extra;
+    auto extra_block = [&]() -> bool {
+        if (tid == 0) sh_extra = add_relaxed(&L->extra_claim.v, 1u);
+        __syncthreads();
+        const uint32_t q = __builtin_amdgcn_readfirstlane(sh_extra);
+        // sh_extra is rewritten only after every thread has read it
+        __syncthreads();
+        if (q >= n_extra) return false;
+        const int64_t Mp = opaque(a.M_all), Np = opaque(a.N), Kp = opaque(a.K);
+        G::block(ln, a.A, a.B, a.remote, Mp, Np, Kp, (int64_t)(extra_row0 + q / bk.bn) * TM,
+                 (int64_t)(q % bk.bn) * (TPB * TN), lds, [] {});
+        return true;
+    };
+    // A workgroup that starts in the reduce role has no shard tile to reduce
+    // before one block's compute time: it computes one block outside the
+    // shard first
+    if constexpr (RS)
+        if (a.mode != kDeterministic && wg < (uint32_t)a.ns_init) extra_block();
     for (;;) {
         if (tid == 0) {
             s.decide_t0 = ticks_now();
@@ -1459,19 +1443,13 @@ void fused_gemm_reduce_kernel(
             // thread 0 saw the flag before the barrier; the partial is read
             // with device-coherent loads, after it
             if (a.P > 0) {
-                if constexpr (RS) {
-                    // read per task from LDS: kept live across the task loop,
-                    // these arguments would take registers the reduce needs
-                    if (ti < __builtin_amdgcn_readfirstlane(sh_own_tile_rows))
-                        reduce_tile<TM, TN, G::NT, H::kPartialLoad, H::kResultStore, 64>(
-                            a.peers, a.C, Mp, Np, a.P, (int64_t)ti * TM, (int64_t)tj * TN);
-                    else
-                        push_tile<TM, TN, G::NT, H::kPartialLoad>(a.C, sh_remote, Mp, Np, (int64_t)ti * TM,
-                                                                   (int64_t)tj * TN);
-                } else {
+                // the peers are [P, M_all, N]: the shard's rows come first
+                if constexpr (RS)
+                    reduce_tile<TM, TN, G::NT, H::kPartialLoad, H::kResultStore, 64>(
+                        a.peers, a.C, Mp, Np, a.peer_mn, a.P, (int64_t)ti * TM, (int64_t)tj * TN);
+                else
                     reduce_tile<TM, TN, G::NT, H::kPartialLoad, H::kResultStore, LOCAL ? 128 : 64>(
-                        a.peers, a.C, Mp, Np, a.P, (int64_t)ti * TM, (int64_t)tj * TN);
-                }
+                        a.peers, a.C, Mp, Np, Mp * Np, a.P, (int64_t)ti * TM, (int64_t)tj * TN);
             }
             work_done(kRoleReduce);
         }
@@ -1515,6 +1493,12 @@ void fused_gemm_reduce_kernel(
         // counters of the last reduced tile; nothing else is in flight
         const CntRead k = cnt_issue(a, sh_pend_t0, sh_pend_n);
         cnt_finish(a, L, k);
+    }
+    // then whatever is left outside the shard
+    if constexpr (RS)
+        while (extra_block()) {
+        }
+    if (tid == 0) {
         max_relaxed(&L->t_end, ticks_now());
         if (wg == 0) st_relaxed(&L->trace_len, s.trace_n);
         // Every write this workgroup made to the control block is a
@@ -1549,8 +1533,11 @@ void gemm_kernel(GemmArgs a) {
     for (uint32_t q = blockIdx.x; q < bk.TB; q += gridDim.x) {
         const uint32_t t0 = bk.first_tile(pt.ticket(q));
         const int64_t Mp = opaque(a.M), Np = opaque(a.N), Kp = opaque(a.K);
-        G::block(ln, a.A, a.B, a.C, Mp, Np, Kp, (int64_t)(t0 / (uint32_t)a.tiles_n) * TM,
-                 (int64_t)(t0 % (uint32_t)a.tiles_n) * TN, lds, [] {});
+        const uint32_t ti = t0 / (uint32_t)a.tiles_n;
+        // reduce-scatter: other ranks' tile rows go straight to their inboxes
+        float *dst = ti < (uint32_t)a.own_tile_rows ? a.C : a.remote;
+        G::block(ln, a.A, a.B, dst, Mp, Np, Kp, (int64_t)ti * TM, (int64_t)(t0 % (uint32_t)a.tiles_n) * TN,
+                 lds, [] {});
     }
 }
 
@@ -1563,13 +1550,6 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
     f32x4 *C = (f32x4 *)a.C;
     const f32x4 *Pp = (const f32x4 *)a.peers;
     const int64_t MN4 = a.MN / 4;
-    // reduce-scatter: elements past own4 belong to other ranks and receive
-    // this rank's partial (each by one thread, so a plain add)
-    if (a.remote)
-        for (int64_t j = a.own4 + i; j < a.count4; j += stride) {
-            f32x4 *R = (f32x4 *)a.remote;
-            __builtin_nontemporal_store(R[j] + C[j], R + j);
-        }
     for (; i + (U - 1) * stride < a.own4; i += U * stride) {
         f32x4 acc[U];
 #pragma unroll
@@ -1608,6 +1588,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
 __device__ void live_init(Live *L) {
     for (int x = 0; x < kMaxXcd; ++x) L->compute_claim[x].v = 0;
     for (int x = 0; x < kMaxXcd; ++x) L->reduce_claim[x].v = 0;
+    L->extra_claim.v = 0;
     L->exit_count = 0;
     L->target_ns.v = 0;
     L->role_switches = 0;

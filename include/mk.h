@@ -127,18 +127,22 @@ int mk_gemm_reduce_unfused(const void *A, const void *B, const float *peers, int
  * mk_gemm_reduce_scatter_local -- one rank's share of GEMM+ReduceScatter in
  * one persistent launch (GEMM + ReduceScatter row of the MarkTechPost page's
  * five-kernel table; "【学习】mKernel 分析" section 2.6 and Table 3 for tiles
- * reaching their owner by atomic add).  This rank is rank 0 of
+ * reaching their owner as they finish).  This rank is rank 0 of
  * R = num_peers + 1; rank o owns tile rows [floor(o*T_m/R), floor((o+1)*T_m/R))
- * of the T_m = ceil(M/tile_m) tile rows.  After the call:
- *     C[i][j]      = (A.B)[i][j] + sum_p peers[p][i][j]   on rank 0's rows,
- *                    (A.B)[i][j]                          on every other row;
- *     remote[i][j] += (A.B)[i][j]                         on every row past
- *                    rank 0's, each element once; rank 0's rows untouched.
- * Only peers' rank-0 rows are read.
+ * of the T_m = ceil(M/tile_m) tile rows.  Each owner has an inbox with one
+ * slot per other rank: a tile that rank 0 does not own is stored, as the
+ * GEMM finishes it, into rank 0's slot at its owner, and rank 0 sums its own
+ * tiles and its inbox (peers).  After the call, with own = min(M,
+ * floor(T_m/R)*tile_m):
+ *     C[i][j]      = (A.B)[i][j] + sum_p peers[p][i][j]   for i < own;
+ *     remote[i][j] = (A.B)[i][j]                          for i >= own;
+ * rows i >= own of C and rows i < own of remote are left untouched.  Only
+ * peers' rows i < own are read.
  *
  *   remote     fp32 [M, N], row-major, 16-byte aligned (device): stands in
- *              for the other ranks' outputs.  Added into, not overwritten;
- *              may be NULL only when rank 0 owns every tile row
+ *              for rank 0's inbox slots at the other owners (row i of it in
+ *              the slot of row i's owner).  Overwritten on the other ranks'
+ *              rows; may be NULL only when rank 0 owns every tile row
  *              (num_peers == 0, M == 0 or N == 0).  Must not overlap A, B,
  *              peers or C.
  *   Other arguments, layouts and errors as for mk_gemm_reduce_local; the
@@ -150,9 +154,8 @@ int mk_gemm_reduce_scatter_local(const void *A, const void *B, const float *peer
 
 /*
  * mk_gemm_reduce_scatter_unfused -- the same result from two launches: the
- * GEMM kernel writes the partial into C, then one elementwise kernel reduces
- * rank 0's rows and adds the other rows into `remote` (plain adds: each
- * element is written by one thread).  Arguments as above.
+ * GEMM kernel writes rank 0's rows into C and the other rows into `remote`,
+ * then one elementwise kernel reduces rank 0's rows.  Arguments as above.
  */
 int mk_gemm_reduce_scatter_unfused(const void *A, const void *B, const float *peers, int num_peers,
                                    float *C, float *remote, int64_t M, int64_t N, int64_t K,
