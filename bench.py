@@ -348,7 +348,7 @@ def main():
     roof["algorithmic_bytes"] = w.algorithmic_bytes
     roof["algorithmic_flops"] = w.flops
     roof["kernel"] = (f"mk::fused_gemm_reduce_kernel<{w.tile_m}, {w.tile_n}, "
-                      f"{'true' if st['xcd_local'] else 'false'}>")
+                      f"{'true' if st['xcd_local'] else 'false'}, false>")
     roof["max_roofline_frac"] = max(t_mfma, t_hbm) / sec
 
     result = {
