@@ -1393,11 +1393,13 @@ void fused_gemm_reduce_kernel(
                  (int64_t)(q % bk.bn) * (TPB * TN), lds, [] {});
         return true;
     };
-    // A workgroup that starts in the reduce role has no shard tile to reduce
-    // before one block's compute time: it computes one block outside the
-    // shard first
+    // Before one block's compute time no shard tile is ready to reduce, and
+    // the shard's blocks keep only its first compute workgroups busy (claims
+    // go out in workgroup order): every other workgroup, reducers included,
+    // computes one block outside the shard first
     if constexpr (RS)
-        if (a.mode != kDeterministic && wg < (uint32_t)a.ns_init) extra_block();
+        if (a.mode != kDeterministic && (wg < (uint32_t)a.ns_init || wg >= (uint32_t)a.ns_init + bk.TB))
+            extra_block();
     for (;;) {
         if (tid == 0) {
             s.decide_t0 = ticks_now();
