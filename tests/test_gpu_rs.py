@@ -131,12 +131,13 @@ def test_reduce_scatter_one_rank_is_the_gemm(mk):
     check_full(C.cpu().numpy(), a, b, p)
 
 
-def test_reduce_scatter_full_size_sampled(mk):
-    """The 4096x4096x1792, 8-rank tensor-parallel share at full size, in the
-    launch the bench times: sampled elements against the oracle one at a
-    time, the untouched rows bit-exact, and fused equal to unfused
-    everywhere."""
-    w = wl.workload("tp_share")
+@pytest.mark.parametrize("name", ["tp_share", "compute_heavy"])
+def test_reduce_scatter_full_size_sampled(mk, name):
+    """The 4096x4096x1792 (128x128 tiles) and 16384x8192x8192 (256x128 tiles)
+    8-rank shares at full size, in the launch the bench times: sampled
+    elements against the oracle one at a time, the untouched rows
+    bit-exact, and fused equal to unfused everywhere."""
+    w = wl.workload(name)
     a, b, p = wl.make_inputs(w)
     r0 = wl.make_remote(w)
     C, R, st = run_rs(mk, True, w, a, b, p, r0, mode="adaptive")
