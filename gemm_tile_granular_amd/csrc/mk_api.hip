@@ -156,6 +156,13 @@ int gemm_xcd_bands(int nxcd, int tiles_m, int tiles_n, int tile_m, int tile_n, i
 }
 
 // All argument checks that do not need the GPU.
+// Byte ranges [p, p + pb) and [q, q + qb) share a byte (NULL or empty: never).
+bool overlaps(const void *p, int64_t pb, const void *q, int64_t qb) {
+    if (!p || !q || pb <= 0 || qb <= 0) return false;
+    const uint64_t a = (uint64_t)(uintptr_t)p, b = (uint64_t)(uintptr_t)q;
+    return a < b + (uint64_t)qb && b < a + (uint64_t)pb;
+}
+
 int check_args(const void *A, const void *B, const float *peers, int num_peers, const float *C,
                int64_t M, int64_t N, int64_t K, int tile_m, int tile_n, int tpc) {
     if (M < 0 || N < 0 || K < 0) return fail(MK_ERR_INVALID_ARG, "negative dimension");
@@ -184,6 +191,10 @@ int check_args(const void *A, const void *B, const float *peers, int num_peers, 
     if (num_peers == 0 && peers) return fail(MK_ERR_INVALID_ARG, "peers must be NULL when num_peers == 0");
     if (!aligned16(C) || (A && !aligned16(A)) || (B && !aligned16(B)) || (peers && !aligned16(peers)))
         return fail(MK_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+    const int64_t cb = M * N * 4;
+    if (overlaps(C, cb, A, M * K * 2) || overlaps(C, cb, B, K * N * 2) ||
+        overlaps(C, cb, peers, (int64_t)num_peers * M * N * 4))
+        return fail(MK_ERR_INVALID_ARG, "C overlaps A, B or peers");
     return MK_OK;
 }
 
@@ -299,6 +310,10 @@ int run(bool fused, bool rs, const void *A, const void *B, const float *peers, i
             return fail(MK_ERR_INVALID_ARG, "remote is NULL while other ranks own tile rows");
         if (remote && !aligned16(remote))
             return fail(MK_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+        const int64_t rb = M * N * 4;
+        if (overlaps(remote, rb, A, M * K * 2) || overlaps(remote, rb, B, K * N * 2) ||
+            overlaps(remote, rb, peers, (int64_t)num_peers * M * N * 4) || overlaps(remote, rb, C, rb))
+            return fail(MK_ERR_INVALID_ARG, "remote overlaps A, B, peers or C");
     }
     if (M == 0 || N == 0) return MK_OK;
     const Settings set = g_set;

@@ -104,8 +104,9 @@ typedef enum {
  *              row-major tile order; the last chunk may be short.
  *   stream     hipStream_t or NULL.
  *
- * Uses the partition set by mk_set_partition.  Errors: MK_ERR_INVALID_ARG,
- * MK_ERR_SHAPE (nothing launched), MK_ERR_NO_DEVICE, MK_ERR_HIP.  Kernel-side
+ * Uses the partition set by mk_set_partition.  Errors: MK_ERR_INVALID_ARG
+ * (also when C's bytes overlap A's, B's or the peers'), MK_ERR_SHAPE
+ * (nothing launched), MK_ERR_NO_DEVICE, MK_ERR_HIP.  Kernel-side
  * timeouts and protocol violations are reported by mk_get_stats.
  */
 int mk_gemm_reduce_local(const void *A, const void *B, const float *peers, int num_peers,
@@ -144,7 +145,7 @@ int mk_gemm_reduce_unfused(const void *A, const void *B, const float *peers, int
  *              the slot of row i's owner).  Overwritten on the other ranks'
  *              rows; may be NULL only when rank 0 owns every tile row
  *              (num_peers == 0, M == 0 or N == 0).  Must not overlap A, B,
- *              peers or C.
+ *              peers or C (MK_ERR_INVALID_ARG).
  *   Other arguments, layouts and errors as for mk_gemm_reduce_local; the
  *   same partition settings and statistics apply.
  */

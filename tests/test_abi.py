@@ -78,7 +78,7 @@ def test_abi_version_and_trace_cap(mk):
 
 
 # fake, never dereferenced addresses (16-byte aligned unless stated)
-A, B, P, C = 0x10000, 0x20000, 0x30000, 0x40000
+A, B, P, C = 0x1000000, 0x2000000, 0x3000000, 0x4000000
 
 
 def _call(mk, **kw):
@@ -97,6 +97,7 @@ def _call(mk, **kw):
     (dict(C=0), -1), (dict(A=0), -1), (dict(B=0), -1), (dict(peers=0), -1),
     (dict(num_peers=0), -1),                 # peers given but num_peers == 0
     (dict(A=A + 8), -1), (dict(C=C + 4), -1), (dict(peers=P + 2), -1),
+    (dict(C=A + 4096), -1), (dict(C=B), -1), (dict(C=P + 65536), -1),   # C overlaps an input
 ])
 def test_argument_errors_before_any_gpu_call(mk, kw, code):
     assert _call(mk, **kw) == code
@@ -109,7 +110,7 @@ def test_argument_errors_before_any_gpu_call(mk, kw, code):
                                          args["tn"], args["tpc"], None) == code
 
 
-R = 0x50000   # fake remote output
+R = 0x5000000   # fake remote output
 
 
 def _call_rs(mk, fused=True, **kw):
@@ -126,6 +127,8 @@ def _call_rs(mk, fused=True, **kw):
     (dict(C=0), -1), (dict(peers=0), -1), (dict(A=A + 8), -1),
     (dict(remote=0), -1),                     # other ranks own tile rows: remote is needed
     (dict(remote=R + 4), -1),                 # misaligned
+    (dict(remote=C + 1024), -1),              # overlaps C
+    (dict(remote=P + 4096), -1),              # overlaps the peers
 ])
 def test_reduce_scatter_argument_errors(mk, fused, kw, code):
     assert _call_rs(mk, fused, **kw) == code
