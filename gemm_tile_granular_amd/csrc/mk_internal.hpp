@@ -36,7 +36,8 @@ template <class T> struct alignas(256) Line {
 struct alignas(256) Live {
     Line<uint32_t> compute_claim[kMaxXcd];  // next compute claim per partition (init 0)
     Line<uint32_t> reduce_claim[kMaxXcd];   // next reduce ticket per partition (init 0)
-    Line<uint32_t> extra_claim;    // next reduce-scatter GEMM block outside the shard (init 0)
+    Line<uint32_t> extra_claim[kMaxXcd];  // reduce-scatter: next block outside the shard, per
+                                          // column band of the outside rows (init 0)
     Line<uint64_t> role_compute;   // (cycles << kCountBits) | tasks      (init 0)
     Line<uint64_t> role_reduce;    //                                     (init 0)
     Line<uint32_t> target_ns;      // controller target, 0 = unset        (init 0)

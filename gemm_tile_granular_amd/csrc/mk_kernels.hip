@@ -1172,7 +1172,8 @@ __device__ void finish_launch(const FusedArgs &a, Live *L) {
         st_relaxed(&L->compute_claim[x].v, 0u);
         st_relaxed(&L->reduce_claim[x].v, 0u);
     }
-    st_relaxed(&L->extra_claim.v, 0u);
+#pragma unroll
+    for (int x = 0; x < kMaxXcd; ++x) st_relaxed(&L->extra_claim[x].v, 0u);
     st_relaxed(&L->target_ns.v, 0u);
     st_relaxed(&L->role_switches, 0u);
     st_relaxed(&L->chunks_released.v, 0u);
@@ -1375,19 +1376,36 @@ void fused_gemm_reduce_kernel(
     // of the workgroup's next task (see CntRead).
     __shared__ uint32_t sh_pend_t0, sh_pend_n;   // reduced tiles whose counters are pending
     if (tid == 0) sh_pend_n = 0;
-    // reduce-scatter: the other ranks' tile rows, plain GEMM blocks claimed
-    // one at a time, row by row, each stored straight into this rank's inbox
-    // slot at its owner
+    // reduce-scatter: the other ranks' tile rows, plain GEMM blocks each
+    // stored straight into this rank's inbox slot at its owner.  Partition x
+    // of the nx column bands of those rows has its own queue, taken row by
+    // row, so an XCD keeps its band of B in its L2; a workgroup takes its own
+    // XCD's band first and the others' once it is empty.
     const uint32_t extra_row0 = (uint32_t)a.tiles_m;
-    const uint32_t n_extra = RS ? ((uint32_t)a.tiles_m_all - extra_row0) * bk.bn : 0u;
-    __shared__ uint32_t sh_extra;
+    __shared__ uint32_t sh_extra, sh_extra_done;
+    if (tid == 0) sh_extra_done = 0;
     auto extra_block = [&]() -> bool {
-        if (tid == 0) sh_extra = add_relaxed(&L->extra_claim.v, 1u);
+        if (tid == 0) {
+            const uint32_t nx = a.nxcd > 1 ? (uint32_t)a.nxcd : 1u;
+            const uint32_t rows = (uint32_t)a.tiles_m_all - extra_row0;
+            uint32_t blk = kNoTile;
+            for (uint32_t k = 0; k < nx && blk == kNoTile; ++k) {
+                const uint32_t x = (wg + k) % nx;
+                if (sh_extra_done & (1u << x)) continue;
+                const uint32_t c0 = bk.bn * x / nx, width = bk.bn * (x + 1) / nx - c0;
+                const uint32_t i = add_relaxed(&L->extra_claim[x].v, 1u);
+                if (i < rows * width)
+                    blk = (i / width) * bk.bn + c0 + i % width;
+                else
+                    sh_extra_done |= 1u << x;
+            }
+            sh_extra = blk;
+        }
         __syncthreads();
         const uint32_t q = __builtin_amdgcn_readfirstlane(sh_extra);
         // sh_extra is rewritten only after every thread has read it
         __syncthreads();
-        if (q >= n_extra) return false;
+        if (q == kNoTile) return false;
         const int64_t Mp = opaque(a.M_all), Np = opaque(a.N), Kp = opaque(a.K);
         G::block(ln, a.A, a.B, a.remote, Mp, Np, Kp, (int64_t)(extra_row0 + q / bk.bn) * TM,
                  (int64_t)(q % bk.bn) * (TPB * TN), lds, [] {});
@@ -1590,7 +1608,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
 __device__ void live_init(Live *L) {
     for (int x = 0; x < kMaxXcd; ++x) L->compute_claim[x].v = 0;
     for (int x = 0; x < kMaxXcd; ++x) L->reduce_claim[x].v = 0;
-    L->extra_claim.v = 0;
+    for (int x = 0; x < kMaxXcd; ++x) L->extra_claim[x].v = 0;
     L->exit_count = 0;
     L->target_ns.v = 0;
     L->role_switches = 0;
