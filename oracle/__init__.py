@@ -339,6 +339,24 @@ def chunk_sizes(T: int, tiles_per_chunk: int) -> np.ndarray:
     return sizes
 
 
+def tiles_per_task(tile_m: int, tile_n: int) -> int:
+    """Output tiles one compute task covers, from the tile shape alone.
+
+    The pages make the tile the unit of compute, flags and reduce
+    ("【学习】mKernel 分析" sections 2.2-2.3) and leave open how many tiles one
+    workgroup computes at once.  The reading taken: two adjacent tiles of one
+    tile row for the 128x128 and 256x128 tiles (two tiles share their A rows,
+    halving the operand bytes per flop), one for 64x64 tiles.  The protocol
+    checker builds its expectations from this value, never from what the
+    device reports.
+    """
+    if (tile_m, tile_n) == (64, 64):
+        return 1
+    if (tile_m, tile_n) in ((128, 128), (256, 128)):
+        return 2
+    raise ValueError(f"no task size for {tile_m}x{tile_n} tiles")
+
+
 def compute_task_of_tile(T: int, tiles_n: Optional[int], tiles_per_task: int) -> np.ndarray:
     """Index of the compute task that produces each tile.
 

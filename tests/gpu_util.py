@@ -87,9 +87,13 @@ def check_sampled(C, a, b, p, rng, n_samples=4096, tiles=(), tile=(128, 128)):
 
 
 def check_protocol(st, w, mode, n_reduce):
+    # the task size comes from the tile shape (the oracle's reading), and the
+    # device's own report must agree with it
+    tpt = oracle.tiles_per_task(w.tile_m, w.tile_n)
+    assert st["tiles_per_task"] == tpt, (st["tiles_per_task"], tpt)
     bad = oracle.check_state(st, w.tiles, w.tiles_per_chunk, st["epoch"], st["calls_since_reset"],
                              st["num_wg"], mode, n_reduce, tiles_n=-(-w.N // w.tile_n),
-                             tiles_per_task=st["tiles_per_task"])
+                             tiles_per_task=tpt)
     assert not bad, bad
     assert st["status"] == 0, st["status_name"]
     assert st["compute_tasks"] == w.tiles and st["reduce_tasks"] == w.tiles

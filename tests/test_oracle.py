@@ -179,6 +179,62 @@ def test_planted_result_mistake_fails_a_pin(name):
 
 
 # ---------------------------------------------------------------------------
+# peer_sum's row blocking: the blocked loop must cover every row exactly once
+# ---------------------------------------------------------------------------
+
+def _peer_sum_reference(peers):
+    """The peer sum from the C brute force with A = 0 (a path with no row
+    blocking at all): C = 0.B + sum_p peers[p]."""
+    P, M, N = peers.shape
+    return oracle.gemm_reduce_brute(np.zeros((M, 1), np.uint16), np.zeros((1, N), np.uint16), peers)
+
+
+def pin_peer_sum_blocked(fn):
+    rng = np.random.default_rng(11)
+    for (P, M, N, rb) in [(3, 10, 4, 3), (2, 7, 5, 7), (4, 9, 3, 2), (1, 5, 6, 1), (5, 8, 2, 4)]:
+        peers = rng.standard_normal((P, M, N)).astype(np.float32)
+        got = fn(peers, rb)
+        want = _peer_sum_reference(peers)
+        if got.shape != want.shape or not np.allclose(got, want, rtol=1e-12, atol=1e-12):
+            return False
+    return True
+
+
+def test_peer_sum_blocked_path_meets_brute_force():
+    # row blocks smaller than M (several blocks, a ragged last one, one-row
+    # blocks) against the unblocked brute force
+    assert pin_peer_sum_blocked(lambda p, rb: oracle.peer_sum(p, row_block=rb))
+
+
+def _peer_sum_mutant(drop_last=False, short_block=False, skip_first_peer=False):
+    def fn(peers, row_block):
+        P, M, N = peers.shape
+        out = np.zeros((M, N), dtype=np.float64)
+        stop = M - row_block if drop_last else M
+        for r0 in range(0, max(stop, 0), row_block):
+            r1 = min(M, r0 + row_block - (1 if short_block else 0))
+            for p in range(1 if skip_first_peer else 0, P):
+                out[r0:r1] += peers[p, r0:r1].astype(np.float64)
+        return out
+    return fn
+
+
+@pytest.mark.parametrize("kw", [{"drop_last": True}, {"short_block": True},
+                                {"skip_first_peer": True}], ids=lambda k: next(iter(k)))
+def test_planted_peer_sum_mistake_fails_the_pin(kw):
+    assert not pin_peer_sum_blocked(_peer_sum_mutant(**kw))
+
+
+def test_tiles_per_task_reading():
+    # two 128-wide tiles per task for the 128x128 and 256x128 tiles, one 64x64
+    assert oracle.tiles_per_task(64, 64) == 1
+    assert oracle.tiles_per_task(128, 128) == 2
+    assert oracle.tiles_per_task(256, 128) == 2
+    with pytest.raises(ValueError):
+        oracle.tiles_per_task(32, 32)
+
+
+# ---------------------------------------------------------------------------
 # controller
 # ---------------------------------------------------------------------------
 
