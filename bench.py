@@ -5,18 +5,30 @@ local partial C_r = A.B on MFMA plus the tile-granular reduction of every
 output tile with the R-1 peer partials, inputs resident in HBM.  Prints one
 JSON line.
 
-Legs (all on the same seeded inputs, same stream):
-  fused (adaptive partition)  -> value, roofline
+The headline (`value`, `roofline`, `cpu_baseline`) is the largest workload,
+compute_heavy (16384x8192x8192, 7 peers, 256x128 tiles).  The same line
+carries every workload of the suite under `per_config`, each with the same
+legs, plus geometric means over the four full-size workloads.
+
+Legs per workload (all on the same seeded inputs, same stream):
+  fused (adaptive partition)          -> ms, TFLOP/s, roofline fraction
   unfused: GEMM kernel then reduce kernel -> fused_vs_unfused
-  static partitions 2..64 reduce workgroups -> adaptive_vs_best_static
-  CPU oracle on a bounded sample of the same workload -> cpu_baseline
+  the pages' plain controller rule (start 2, no cap, no help)
+  static partitions 2..64 reduce workgroups (and 96..224 beyond the pages'
+    range) -> adaptive_vs_best_static_2_64, adaptive_vs_best_static_any
+  chunk release lag of the last fused launch (per-chunk stamps)
+Every leg ends with mk_get_stats, whose status is sticky over all the leg's
+launches: a timeout or protocol violation in any launch fails the bench.
 Before each timed launch a 512 MiB scratch buffer is rewritten (outside the
 timed events) so the 256 MB Infinity Cache and the L2s start cold.
+The CPU oracle runs on a bounded sample of the headline workload
+(cpu_baseline).
 """
 from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import statistics
 import sys
@@ -30,19 +42,32 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CU x 4096 flop/clk x 2.4 GHz, dense
 STATIC_SWEEP = (2, 4, 8, 16, 32, 64)          # the pages' sweep range
 STATIC_SWEEP_EXT = (96, 128, 160, 192, 224)   # beyond it, for MI355X's reduce role
+HEADLINE = "compute_heavy"                    # the largest workload
+SUITE = ("tiny", "tp_share", "reduce_heavy", "compute_heavy", "wide_many_peer")
+FULL_SIZE = ("tp_share", "reduce_heavy", "compute_heavy", "wide_many_peer")
 
 
-def parse():
+class BenchError(SystemExit):
+    """A leg whose launches reported an error: the bench prints no line."""
+
+    def __init__(self, msg: str):
+        print(f"[bench] FAILED: {msg}", file=sys.stderr, flush=True)
+        super().__init__(3)
+
+
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="tp_share")
+    ap.add_argument("--workload", default="all",
+                    help="'all' (default: the headline workload plus every other one under "
+                         "per_config) or one workload name")
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-sweep", action="store_true", help="skip the static partition sweep")
     ap.add_argument("--fused-only", action="store_true",
-                    help="only the fused leg (for profiler runs)")
+                    help="only the fused leg of one workload (for profiler runs)")
     ap.add_argument("--gemm-only", action="store_true",
                     help="only the GEMM kernel of the unfused baseline, no peers (for counter "
                          "runs on the MFMA core); prints its own JSON line")
@@ -52,11 +77,11 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of this size (counter calibration)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 def time_leg(fn, steps, warmup, flush, stream, torch):
-    """Per-launch durations (ms) from HIP events on the launch stream."""
+    """Per-launch durations (ms) from HIP events recorded on the launch stream."""
     for _ in range(warmup):
         if flush is not None:
             flush()
@@ -80,6 +105,16 @@ def time_leg(fn, steps, warmup, flush, stream, torch):
 def summary(ms):
     return {"mean": statistics.fmean(ms), "median": statistics.median(ms), "min": min(ms),
             "max": max(ms)}
+
+
+def check_leg(mk, leg: str, maps: bool = False):
+    """Stats after a leg.  mk_get_stats reports an error raised by ANY launch
+    since the previous call (sticky), so one call per leg covers every timed
+    and warm-up launch of it.  A non-OK status ends the bench (exit 3)."""
+    st = mk.get_stats(maps=maps, raise_on_error=False)
+    if st["rc"] != 0 or st["status"] != 0:
+        raise BenchError(f"{leg}: {st['status_name']} (sticky error bits {st['sticky_errors']:#x})")
+    return st
 
 
 def cpu_baseline(w, a, b, p, seconds):
@@ -131,23 +166,246 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def _traffic_record():
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            return json.load(f)
+    except (OSError, ValueError):
+        return None
+
+
 def measured_traffic(workload):
     """HBM bytes per launch of the fused kernel from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE passes (profiles/traffic.json), scaled by the
     plain-copy calibration stored with them.  None when the kernel sources
     changed since the counters were taken, or the workload was not profiled."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    try:
-        with open(path) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+    rec = _traffic_record()
+    if rec is None:
         return None, "no profiles/traffic.json"
     if rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None, "kernel changed since the counters were taken"
     wrec = rec.get("workloads", {}).get(workload)
-    if wrec is None:
+    if wrec is None or "hbm_bytes_per_launch" not in wrec:
         return None, f"{workload} not profiled"
     return float(wrec["hbm_bytes_per_launch"]), "rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated"
+
+
+def counter_figures(workload):
+    """Counter-derived figures of the fused kernel from the committed
+    rocprofv3 passes, when they match the current kernel sources:
+      - GEMM TFLOP/s: MFMA work counted by SQ_INSTS_VALU_MFMA_MOPS_BF16
+        (512 flops per count) over the kernel-trace average duration;
+      - HBM GB/s over the launch: copy-calibrated FETCH_SIZE + WRITE_SIZE
+        over the same duration (the reduce role moves nearly all of it)."""
+    rec = _traffic_record()
+    if rec is None or rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    wrec = rec.get("workloads", {}).get(workload)
+    if not wrec or "kernel_trace_avg_us" not in wrec:
+        return None
+    sec = wrec["kernel_trace_avg_us"] * 1e-6
+    out = {"kernel_trace_avg_us": wrec["kernel_trace_avg_us"], "source": "profiles/traffic.json"}
+    if "mfma_mops_bf16" in wrec:
+        flops = wrec["mfma_mops_bf16"] * 512.0
+        out["gemm_tflops_counters"] = flops / sec / 1e12
+        out["mfma_flops_per_launch_counters"] = flops
+    if "hbm_bytes_per_launch" in wrec:
+        out["hbm_GBps_counters"] = wrec["hbm_bytes_per_launch"] / sec / 1e9
+    return out
+
+
+def roofline(w, ms):
+    """Roofline of one fused launch from its algorithmic work (2MNK flops;
+    A, B, every peer once, C once) and its mean duration."""
+    sec = ms / 1e3
+    tflops = w.flops / sec / 1e12
+    gbps = w.algorithmic_bytes / sec / 1e9
+    t_mfma = w.flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    t_hbm = w.algorithmic_bytes / (HBM_PEAK_GBPS * 1e9)
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": gbps / HBM_PEAK_GBPS}
+    else:
+        roof = {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS}
+    traffic, note = measured_traffic(w.name)
+    roof["traffic"] = traffic
+    roof["traffic_unit"] = "bytes/launch"
+    roof["traffic_note"] = note
+    roof["algorithmic_bytes"] = w.algorithmic_bytes
+    roof["algorithmic_flops"] = w.flops
+    roof["max_roofline_frac"] = max(t_mfma, t_hbm) / sec
+    return roof, tflops, gbps
+
+
+def release_lags(st, w, np):
+    """Per-chunk lag from the end of the chunk's last reduced tile to the
+    chunk's release stamp (us), from the maps of the last launch."""
+    rel = st["chunk_release"].astype(np.uint32)
+    rend = st["reduce_end"].astype(np.uint32)
+    tpc = w.tiles_per_chunk
+    lags = []
+    for c in range(len(rel)):
+        tiles = rend[c * tpc:min(w.tiles, (c + 1) * tpc)]
+        d = (rel[c] - tiles).astype(np.uint32).view(np.int32).astype(np.int64)
+        lags.append(int(d.min()))
+    us = np.array(lags, dtype=np.float64) / float(st["timer_hz"]) * 1e6
+    return {"median_us": float(np.median(us)), "max_us": float(us.max()), "min_us": float(us.min()),
+            "chunks": int(len(us))}
+
+
+def phases_of(st, w, np):
+    kernel_us = (st["kernel_ticks_end"] - st["kernel_ticks_start"]) / st["timer_hz"] * 1e6
+    compute_us = float(np.max(st["compute_end_us"])) if len(st["compute_end_us"]) else 0.0
+    reduce_us = (st["reduce_ticks_end"] - st["reduce_ticks_start"]) / st["timer_hz"] * 1e6
+    reduce_bytes = 4.0 * w.M * w.N * (w.peers + 2)
+    return {
+        "kernel_us": kernel_us,
+        "compute_window_us": compute_us,
+        "gemm_tflops_in_compute_window": w.flops / (compute_us * 1e-6) / 1e12 if compute_us else None,
+        "reduce_window_us": reduce_us,
+        "reduce_GBps_in_reduce_window": reduce_bytes / (reduce_us * 1e-6) / 1e9 if reduce_us > 0 else None,
+        "reduce_bytes": reduce_bytes,
+        "xcd_local": st["xcd_local"],
+        "xcd_bands": st["xcd_bands"],
+        "n_reduce_initial": st["n_reduce_initial"],
+        "n_reduce_final": st["n_reduce_final"],
+        "n_reduce_range": [st["n_reduce_min_seen"], st["n_reduce_max_seen"]],
+        "controller_cap": st["controller_cap"],
+        "help_tiles": int((st["compute_owner"] >> 31).sum()),
+    }
+
+
+def set_adaptive_defaults(mk):
+    mk.set_partition("adaptive", 0)
+    mk.set_adaptive_help(True)
+    mk.set_controller_cap(0)
+
+
+def measure(args, w, mk, wl, upload, np, torch, keep_host=False):
+    """Every leg of one workload.  Returns (record, host inputs or None)."""
+    t_gen = time.perf_counter()
+    a, b, p = wl.make_inputs(w)
+    A, B, P, C = upload(a, b, p, "cuda:0")
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    print(f"[bench] {w.name}: {w.M}x{w.N}x{w.K}, {w.peers} peers, tile {w.tile_m}x{w.tile_n}; "
+          f"inputs ready in {t_gen:.1f} s", file=sys.stderr, flush=True)
+    host = (a, b, p) if keep_host else None
+    if not keep_host:
+        del a, b, p
+
+    stream = torch.cuda.current_stream()
+    flush = None
+    if not args.no_flush:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+        counter = [0]
+
+        def flush():
+            counter[0] = (counter[0] + 1) & 0xFF
+            scratch.fill_(counter[0])
+
+    def fused():
+        mk.gemm_reduce_local(A, B, P, C, w.tile_m, w.tile_n, w.tiles_per_chunk)
+
+    def unfused():
+        mk.gemm_reduce_unfused(A, B, P, C, w.tile_m, w.tile_n, w.tiles_per_chunk)
+
+    # the tiny workload runs its fixed partition (2 static reducers); the
+    # others the adaptive controller
+    static_only = w.mode != "adaptive"
+    set_adaptive_defaults(mk)
+    if static_only:
+        mk.set_partition(w.mode, w.n_reduce)
+    ms_fused, wall = time_leg(fused, args.steps, args.warmup, flush, stream, torch)
+    st = check_leg(mk, f"{w.name} fused", maps=True)
+    rec = {"partition": w.mode if static_only else "adaptive", "fused_ms": summary(ms_fused),
+           "wall_s_fused_leg": wall}
+    ms = statistics.fmean(ms_fused)
+    roof, tflops, gbps = roofline(w, ms)
+    roof["kernel"] = (f"mk::fused_gemm_reduce_kernel<{w.tile_m}, {w.tile_n}, "
+                      f"{'true' if st['xcd_local'] else 'false'}, false>")
+    rec.update({"ms": ms, "tflops": tflops, "hbm_GBps_algorithmic": gbps, "roofline": roof,
+                "phases": phases_of(st, w, np), "chunk_release_lag": release_lags(st, w, np)})
+    cf = counter_figures(w.name)
+    if cf:
+        rec["counters"] = cf
+    print(f"[bench] {w.name} fused: {summary(ms_fused)}", file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        print(f"[bench] copy calibration: {args.copy_calibration} MiB x3", file=sys.stderr, flush=True)
+
+    if args.fused_only:
+        return rec, host
+
+    # consistency of the timed fused result with the two-kernel path at
+    # sampled positions (the oracle comparison lives in the test suite)
+    C_fused = C.clone()
+    unfused()
+    torch.cuda.synchronize()
+    g = torch.Generator(device="cpu").manual_seed(0)
+    idx = torch.randint(0, w.M * w.N, (1 << 16,), generator=g).to(C.device)
+    fv, uv = C_fused.view(-1)[idx].double(), C.view(-1)[idx].double()
+    diff = float((fv - uv).abs().max())
+    scale = float(uv.abs().max())
+    rec["fused_matches_unfused"] = {"max_abs_diff": diff, "scale": scale, "ok": diff <= 2e-3 * scale}
+    del C_fused
+    if not rec["fused_matches_unfused"]["ok"]:
+        raise BenchError(f"{w.name}: fused and unfused results differ ({diff} > 2e-3 * {scale})")
+    ms_unf, _ = time_leg(unfused, args.steps, args.warmup, flush, stream, torch)
+    rec["unfused_ms"] = summary(ms_unf)
+    rec["fused_vs_unfused"] = statistics.fmean(ms_unf) / ms
+    print(f"[bench] {w.name} unfused: {summary(ms_unf)}", file=sys.stderr, flush=True)
+
+    if static_only or args.no_sweep:
+        set_adaptive_defaults(mk)
+        return rec, host
+
+    # the pages' rule as printed: start at the sweep floor, no cap below
+    # B - keep, reducers that wait instead of helping
+    mk.set_partition("adaptive", 2)
+    mk.set_adaptive_help(False)
+    mk.set_controller_cap(1024)
+    ms_plain, _ = time_leg(fused, args.steps, args.warmup, flush, stream, torch)
+    stp = check_leg(mk, f"{w.name} plain rule")
+    set_adaptive_defaults(mk)
+    rec["plain_rule_ms"] = summary(ms_plain)
+    rec["plain_rule_n_reduce_final"] = stp["n_reduce_final"]
+    rec["labelled_variants_gain"] = statistics.fmean(ms_plain) / ms
+    print(f"[bench] {w.name} plain rule: {summary(ms_plain)}", file=sys.stderr, flush=True)
+
+    sweep, ext = {}, {}
+    for table, counts in ((sweep, STATIC_SWEEP), (ext, STATIC_SWEEP_EXT)):
+        for n in counts:
+            mk.set_partition("static", n)
+            ms_n, _ = time_leg(fused, max(3, args.steps // 2), 1, flush, stream, torch)
+            check_leg(mk, f"{w.name} static {n}")
+            table[n] = statistics.fmean(ms_n)
+            print(f"[bench] {w.name} static {n}: {table[n]:.4f} ms", file=sys.stderr, flush=True)
+    set_adaptive_defaults(mk)
+    best_n = min(sweep, key=sweep.get)
+    best_all = min({**sweep, **ext}.items(), key=lambda kv: kv[1])
+    rec["static_sweep_ms"] = {str(k): v for k, v in sweep.items()}
+    rec["static_sweep_ext_ms"] = {str(k): v for k, v in ext.items()}
+    rec["best_static_2_64"] = {"n_reduce": best_n, "ms": sweep[best_n]}
+    rec["adaptive_vs_best_static_2_64"] = sweep[best_n] / ms
+    rec["best_static_any"] = {"n_reduce": best_all[0], "ms": best_all[1]}
+    rec["adaptive_vs_best_static_any"] = best_all[1] / ms
+    rec["plain_rule_vs_best_static_2_64"] = sweep[best_n] / statistics.fmean(ms_plain)
+    return rec, host
+
+
+def geomean(xs):
+    xs = [x for x in xs if x]
+    return math.exp(sum(math.log(x) for x in xs) / len(xs)) if xs else None
 
 
 def gemm_only(args, w, mk, wl, upload, np, torch):
@@ -192,10 +450,10 @@ def reduce_scatter(args, w, mk, wl, upload, np, torch):
     def unfused():
         mk.gemm_reduce_scatter_unfused(A, B, P, C, R, w.tile_m, w.tile_n, w.tiles_per_chunk)
 
-    mk.set_partition("adaptive", 0)
+    set_adaptive_defaults(mk)
     fl = None if args.no_flush else flush
     ms_f, _ = time_leg(fused, args.steps, args.warmup, fl, stream, torch)
-    st = mk.get_stats(maps=False)
+    st = check_leg(mk, f"{w.name} reduce-scatter fused")
     ms_u, _ = time_leg(unfused, args.steps, args.warmup, fl, stream, torch)
     mf, mu = statistics.fmean(ms_f), statistics.fmean(ms_u)
     print(json.dumps({"metric": "GEMM+ReduceScatter TFLOP/s (one rank's share, fused adaptive)",
@@ -208,8 +466,8 @@ def reduce_scatter(args, w, mk, wl, upload, np, torch):
                                  "tile": [w.tile_m, w.tile_n]}}), flush=True)
 
 
-def main():
-    args = parse()
+def main(argv=None):
+    args = parse(argv)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
               "multi-GPU GEMM+AllReduce is not part of it.", file=sys.stderr)
@@ -222,161 +480,69 @@ def main():
     import workloads as wl
     from gemm_tile_granular_amd.tensors import upload
 
-    w = wl.workload(args.workload)
+    head_name = HEADLINE if args.workload == "all" else args.workload
+    w_head = wl.workload(head_name)
     if args.gemm_only:
-        gemm_only(args, w, mk, wl, upload, np, torch)
+        gemm_only(args, w_head, mk, wl, upload, np, torch)
         return
     if args.reduce_scatter:
-        reduce_scatter(args, w, mk, wl, upload, np, torch)
+        reduce_scatter(args, w_head, mk, wl, upload, np, torch)
         return
-    t_gen = time.perf_counter()
-    a, b, p = wl.make_inputs(w)
-    A, B, P, C = upload(a, b, p, "cuda:0")
-    torch.cuda.synchronize()
-    t_gen = time.perf_counter() - t_gen
-    print(f"[bench] {w.name}: {w.M}x{w.N}x{w.K}, {w.peers} peers, tile {w.tile_m}x{w.tile_n}; "
-          f"inputs ready in {t_gen:.1f} s", file=sys.stderr, flush=True)
 
-    stream = torch.cuda.current_stream()
-    scratch = None
-    flush = None
-    if not args.no_flush:
-        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
-        counter = [0]
+    names = [head_name] if (args.workload != "all" or args.fused_only) else \
+        [head_name] + [n for n in SUITE if n != head_name]
+    per = {}
+    cpu = None
+    for name in names:
+        w = wl.workload(name)
+        want_cpu = name == head_name and not args.no_cpu and not args.fused_only
+        rec, host = measure(args, w, mk, wl, upload, np, torch, keep_host=want_cpu)
+        per[name] = rec
+        if want_cpu:
+            cpu = cpu_baseline(w, *host, args.cpu_seconds)
+            print(f"[bench] cpu oracle: {cpu['value']:.3f} TFLOP/s", file=sys.stderr, flush=True)
+        del host
+        torch.cuda.empty_cache()
 
-        def flush():
-            counter[0] = (counter[0] + 1) & 0xFF
-            scratch.fill_(counter[0])
-
-    def fused():
-        mk.gemm_reduce_local(A, B, P, C, w.tile_m, w.tile_n, w.tiles_per_chunk)
-
-    def unfused():
-        mk.gemm_reduce_unfused(A, B, P, C, w.tile_m, w.tile_n, w.tiles_per_chunk)
-
-    mk.set_partition("adaptive", 0)
-    ms_fused, wall_fused = time_leg(fused, args.steps, args.warmup, flush, stream, torch)
-    st = mk.get_stats(maps=True)
-    # phase windows of the last timed launch, from the device's constant clock
-    kernel_us = (st["kernel_ticks_end"] - st["kernel_ticks_start"]) / st["timer_hz"] * 1e6
-    compute_us = float(np.max(st["compute_end_us"])) if len(st["compute_end_us"]) else 0.0
-    reduce_us = (st["reduce_ticks_end"] - st["reduce_ticks_start"]) / st["timer_hz"] * 1e6
-    reduce_bytes = 4.0 * w.M * w.N * (w.peers + 2)
-    phases = {
-        "kernel_us": kernel_us,
-        "compute_window_us": compute_us,
-        "gemm_tflops_in_compute_window": w.flops / (compute_us * 1e-6) / 1e12 if compute_us else None,
-        "reduce_window_us": reduce_us,
-        "reduce_GBps_in_reduce_window": reduce_bytes / (reduce_us * 1e-6) / 1e9 if reduce_us > 0 else None,
-        "reduce_bytes": reduce_bytes,
-        "xcd_local": st["xcd_local"],
-        "n_reduce_initial": st["n_reduce_initial"],
-        "n_reduce_range": [st["n_reduce_min_seen"], st["n_reduce_max_seen"]],
-        "controller_cap": st["controller_cap"],
-        "help_tiles": int((st["compute_owner"] >> 31).sum()),
-    }
-    print(f"[bench] fused adaptive: {summary(ms_fused)} (n_reduce final {st['n_reduce_final']}, "
-          f"range {st['n_reduce_min_seen']}-{st['n_reduce_max_seen']})", file=sys.stderr, flush=True)
-
-    if args.copy_calibration:
-        n = args.copy_calibration << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"[bench] copy calibration: {args.copy_calibration} MiB x3", file=sys.stderr, flush=True)
-
-    out_extra = {}
-    if not args.fused_only:
-        # consistency of the timed fused result with the two-kernel path, at
-        # sampled positions (the oracle comparison lives in the test suite)
-        C_fused = C.clone()
-        unfused()
-        torch.cuda.synchronize()
-        g = torch.Generator(device="cpu").manual_seed(0)
-        idx = torch.randint(0, w.M * w.N, (1 << 16,), generator=g).to(C.device)
-        fv, uv = C_fused.view(-1)[idx].double(), C.view(-1)[idx].double()
-        diff = float((fv - uv).abs().max())
-        scale = float(uv.abs().max())
-        out_extra["fused_matches_unfused"] = {"max_abs_diff": diff, "scale": scale,
-                                              "ok": diff <= 2e-3 * scale}
-        del C_fused
-        ms_unf, _ = time_leg(unfused, args.steps, args.warmup, flush, stream, torch)
-        print(f"[bench] unfused: {summary(ms_unf)}", file=sys.stderr, flush=True)
-        out_extra["unfused_ms"] = summary(ms_unf)
-        out_extra["fused_vs_unfused"] = statistics.fmean(ms_unf) / statistics.fmean(ms_fused)
-        if not args.no_sweep:
-            sweep = {}
-            for n in STATIC_SWEEP:
-                mk.set_partition("static", n)
-                ms_n, _ = time_leg(fused, max(3, args.steps // 2), 1, flush, stream, torch)
-                sweep[n] = statistics.fmean(ms_n)
-                print(f"[bench] static {n}: {sweep[n]:.4f} ms", file=sys.stderr, flush=True)
-            best_n = min(sweep, key=sweep.get)
-            ext = {}
-            for n in STATIC_SWEEP_EXT:
-                mk.set_partition("static", n)
-                ms_n, _ = time_leg(fused, max(3, args.steps // 2), 1, flush, stream, torch)
-                ext[n] = statistics.fmean(ms_n)
-                print(f"[bench] static {n}: {ext[n]:.4f} ms", file=sys.stderr, flush=True)
-            mk.set_partition("adaptive", 0)
-            best_all = min({**sweep, **ext}.items(), key=lambda kv: kv[1])
-            out_extra["static_sweep_ms"] = {str(k): v for k, v in sweep.items()}
-            out_extra["static_sweep_ext_ms"] = {str(k): v for k, v in ext.items()}
-            out_extra["best_static"] = {"n_reduce": best_n, "ms": sweep[best_n]}
-            out_extra["adaptive_vs_best_static"] = sweep[best_n] / statistics.fmean(ms_fused)
-            out_extra["best_static_any"] = {"n_reduce": best_all[0], "ms": best_all[1]}
-            out_extra["adaptive_vs_best_static_any"] = best_all[1] / statistics.fmean(ms_fused)
-
-    ms = statistics.fmean(ms_fused)
-    sec = ms / 1e3
-    tflops = w.flops / sec / 1e12
-    gbps = w.algorithmic_bytes / sec / 1e9
-    t_mfma = w.flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
-    t_hbm = w.algorithmic_bytes / (HBM_PEAK_GBPS * 1e9)
-    if t_hbm >= t_mfma:
-        roof = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": gbps / HBM_PEAK_GBPS}
-    else:
-        roof = {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS}
-    traffic, traffic_note = measured_traffic(w.name)
-    roof["traffic"] = traffic
-    roof["traffic_unit"] = "bytes/launch"
-    roof["traffic_note"] = traffic_note
-    roof["algorithmic_bytes"] = w.algorithmic_bytes
-    roof["algorithmic_flops"] = w.flops
-    roof["kernel"] = (f"mk::fused_gemm_reduce_kernel<{w.tile_m}, {w.tile_n}, "
-                      f"{'true' if st['xcd_local'] else 'false'}, false>")
-    roof["max_roofline_frac"] = max(t_mfma, t_hbm) / sec
-
+    head = per[head_name]
     result = {
         "metric": "fused GEMM+tile-reduce TFLOP/s & % roofline on 1 MI355X; speedup vs unfused",
-        "value": tflops,
+        "value": head["tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": head["ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded, resident in HBM)",
-        "config": {"workload": w.name, "M": w.M, "N": w.N, "K_local": w.K, "peers": w.peers,
-                   "tile": [w.tile_m, w.tile_n], "tiles_per_chunk": w.tiles_per_chunk,
-                   "partition": "adaptive", "cache_flush_between_steps": not args.no_flush},
-        "roofline": roof,
-        "fused_ms": summary(ms_fused),
-        "hbm_GBps_algorithmic": gbps,
-        "wall_s_fused_leg": wall_fused,
-        "n_reduce_final": st["n_reduce_final"],
-        "fused_phases": phases,
-        **out_extra,
+        "config": {"workload": w_head.name, "M": w_head.M, "N": w_head.N, "K_local": w_head.K,
+                   "peers": w_head.peers, "tile": [w_head.tile_m, w_head.tile_n],
+                   "tiles_per_chunk": w_head.tiles_per_chunk, "partition": head["partition"],
+                   "cache_flush_between_steps": not args.no_flush},
+        "roofline": head["roofline"],
     }
-    if not args.no_cpu and not args.fused_only:
-        result["cpu_baseline"] = cpu_baseline(w, a, b, p, args.cpu_seconds)
+    for key in ("fused_vs_unfused", "adaptive_vs_best_static_2_64", "adaptive_vs_best_static_any",
+                "labelled_variants_gain", "chunk_release_lag", "phases", "counters", "fused_ms",
+                "unfused_ms"):
+        if key in head:
+            result[key] = head[key]
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
+    full = [per[n] for n in FULL_SIZE if n in per]
+    if len(full) == len(FULL_SIZE):
+        result["geomean_full_size"] = {
+            "workloads": list(FULL_SIZE),
+            "fused_vs_unfused": geomean([r.get("fused_vs_unfused") for r in full]),
+            "adaptive_vs_best_static_2_64": geomean([r.get("adaptive_vs_best_static_2_64") for r in full]),
+            "adaptive_vs_best_static_any": geomean([r.get("adaptive_vs_best_static_any") for r in full]),
+            "labelled_variants_gain": geomean([r.get("labelled_variants_gain") for r in full]),
+            "roofline_frac": geomean([r["roofline"]["frac"] for r in full]),
+        }
+        result["min_fused_vs_unfused"] = min(r.get("fused_vs_unfused", float("inf")) for r in full)
+    result["per_config"] = per
     print(json.dumps(result), flush=True)
 
 

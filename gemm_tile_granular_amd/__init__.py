@@ -77,6 +77,8 @@ class Stats(ctypes.Structure):
         ("keep_compute", ctypes.c_uint32),
         ("controller_cap", ctypes.c_uint32),
         ("xcd_bands", ctypes.c_uint32),
+        ("adaptive_help", ctypes.c_uint32),
+        ("sticky_errors", ctypes.c_uint32),
     ]
 
 
@@ -94,6 +96,7 @@ SIGNATURES = {
     "mk_set_controller_cap": (_i32, [_i32]),
     "mk_set_xcd_bands": (_i32, [_i32]),
     "mk_set_num_workgroups": (_i32, [_i32]),
+    "mk_set_adaptive_help": (_i32, [_i32]),
     "mk_set_timeout_us": (_i32, [ctypes.c_uint64]),
     "mk_set_fault_skip_publish": (_i32, [_i64]),
     "mk_get_stats": (_i32, [ctypes.POINTER(Stats), _u32p, ctypes.c_size_t]),
@@ -192,7 +195,9 @@ def gemm_reduce_scatter_local(A, B, peers, C, remote, tile_m: int, tile_n: int, 
                               stream=None) -> None:
     """Rank 0's share of GEMM+ReduceScatter in one persistent launch
     (mk_gemm_reduce_scatter_local): C = A.B + sum_p peers[p] on rank 0's tile
-    rows, A.B elsewhere; remote += A.B on the other ranks' rows."""
+    rows (its shard); the other ranks' rows of A.B are stored into remote (this
+    rank's inbox slots at their owners); C's other rows and remote's shard rows
+    are left untouched."""
     _call_rs(lib.mk_gemm_reduce_scatter_local, A, B, peers, C, remote, tile_m, tile_n, tiles_per_chunk,
              stream)
 
@@ -221,6 +226,11 @@ def set_controller_cap(cap: int) -> None:
 def set_xcd_bands(bands: int) -> None:
     """Column bands of the XCD-local partitions (0: least operand traffic; 1, 2, 4, 8)."""
     _check(lib.mk_set_xcd_bands(int(bands)))
+
+
+def set_adaptive_help(on: bool) -> None:
+    """Adaptive mode: a reducer whose ticket is not ready computes meanwhile (default on)."""
+    _check(lib.mk_set_adaptive_help(1 if on else 0))
 
 
 def set_num_workgroups(num_wg: int) -> None:
@@ -252,7 +262,9 @@ def abi_version() -> int:
 
 def get_stats(maps: bool = False, raise_on_error: bool = True) -> Dict:
     """Stats of the last fused launch (synchronizes).  With maps=True also the
-    tile/chunk maps and the controller trace as numpy arrays."""
+    tile/chunk maps and the controller trace as numpy arrays.  The status is
+    sticky: it reports an error raised by any fused launch since the previous
+    call, not only by the last launch."""
     st = Stats()
     st.struct_size = ctypes.sizeof(Stats)
     buf = None
@@ -263,7 +275,7 @@ def get_stats(maps: bool = False, raise_on_error: bool = True) -> Dict:
         if rc0 not in (MK_OK, MK_ERR_TIMEOUT, MK_ERR_PROTOCOL):
             _check(rc0)
         T, Ch = st.num_tiles, st.num_chunks
-        n = 10 * T + 2 * Ch + 2 * TRACE_CAP
+        n = 10 * T + 3 * Ch + 2 * TRACE_CAP
         buf = np.zeros(n, dtype=np.uint32)
         st = Stats()
         st.struct_size = ctypes.sizeof(Stats)
@@ -277,14 +289,14 @@ def get_stats(maps: bool = False, raise_on_error: bool = True) -> Dict:
                          ("chunk_flag", Ch), ("compute_owner", T), ("reduce_owner", T),
                          ("ns_trace", 2 * TRACE_CAP), ("compute_start", T), ("compute_end", T),
                          ("reduce_start", T), ("reduce_end", T), ("compute_choice_ticks", T),
-                         ("reduce_choice_ticks", T)):
+                         ("reduce_choice_ticks", T), ("chunk_release", Ch)):
             out[key] = buf[o:o + cnt].copy()
             o += cnt
         out["ns_trace"] = out["ns_trace"].reshape(TRACE_CAP, 2)[: st.ns_trace_len]
         # timeline in microseconds since the kernel started
         t0 = np.uint32(st.kernel_ticks_start & 0xFFFFFFFF)
         us = 1e6 / float(st.timer_hz or 100_000_000)
-        for key in ("compute_start", "compute_end", "reduce_start", "reduce_end"):
+        for key in ("compute_start", "compute_end", "reduce_start", "reduce_end", "chunk_release"):
             out[key + "_us"] = (out[key] - t0).astype(np.uint32).astype(np.float64) * us
         out["ns_trace_us"] = (out["ns_trace"][:, 0] - t0).astype(np.uint32).astype(np.float64) * us
         out["compute_choice_us"] = out["compute_choice_ticks"].astype(np.float64) * us

@@ -46,6 +46,7 @@ struct Settings {
     int64_t skip_publish = -1;
     int group_m = 8;
     int xcd_bands = 0;        // 0: the most column bands the shape allows
+    int help = 1;             // adaptive: waiting reducers compute meanwhile
 };
 Settings g_set;
 
@@ -55,7 +56,7 @@ struct Launch {
     bool valid = false;
     uint32_t epoch = 0, calls = 0, nwg = 0, T = 0, Ch = 0, tpc = 0, tm = 0, tn = 0;
     uint32_t mode = 0, ns_init = 0;
-    uint32_t local = 0, keep = 1, cap = 0, bands = 1;
+    uint32_t local = 0, keep = 1, cap = 0, bands = 1, help = 1;
 };
 
 struct DevState {
@@ -77,7 +78,8 @@ DevState g_dev[kMaxDevices];
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Layout {
-    size_t live, snap, trace, tile_flag, tile_cnt, chunk_cnt, chunk_flag, cowner, rowner, timeline, total;
+    size_t live, snap, trace, tile_flag, tile_cnt, chunk_cnt, chunk_flag, chunk_release, cowner, rowner,
+        timeline, total;
 };
 
 Layout layout_for(uint32_t Tcap, uint32_t Chcap) {
@@ -90,6 +92,7 @@ Layout layout_for(uint32_t Tcap, uint32_t Chcap) {
     L.tile_cnt = o; o = align_up(o + 4ull * Tcap, 256);
     L.chunk_cnt = o; o = align_up(o + 4ull * Chcap, 256);
     L.chunk_flag = o; o = align_up(o + 4ull * Chcap, 256);
+    L.chunk_release = o; o = align_up(o + 4ull * Chcap, 256);
     L.cowner = o; o = align_up(o + 4ull * Tcap, 256);
     L.rowner = o; o = align_up(o + 4ull * Tcap, 256);
     L.timeline = o; o = align_up(o + 24ull * Tcap, 256);
@@ -107,6 +110,7 @@ WsView view_of(const DevState &d) {
     v.tile_cnt = (uint32_t *)(d.ws + L.tile_cnt);
     v.chunk_cnt = (uint32_t *)(d.ws + L.chunk_cnt);
     v.chunk_flag = (uint32_t *)(d.ws + L.chunk_flag);
+    v.chunk_release = (uint32_t *)(d.ws + L.chunk_release);
     v.cowner = (uint32_t *)(d.ws + L.cowner);
     v.rowner = (uint32_t *)(d.ws + L.rowner);
     v.timeline = (uint32_t *)(d.ws + L.timeline);
@@ -475,6 +479,7 @@ int run(bool fused, bool rs, const void *A, const void *B, const float *peers, i
     a.peer_mn = M * N;
     a.timeout_ticks = set.timeout_us * (d.timer_hz / 1000000ull);
     a.skip_publish = set.skip_publish;
+    a.help = set.help;
     a.ws = v;
     e = launch_fused(tile_m, tile_n, a, s);
     if (e != hipSuccess) {
@@ -496,6 +501,7 @@ int run(bool fused, bool rs, const void *A, const void *B, const float *peers, i
     d.last.keep = (uint32_t)keep;
     d.last.cap = (uint32_t)cap;
     d.last.bands = local ? (uint32_t)bands : 1u;
+    d.last.help = (uint32_t)set.help;
     return MK_OK;
 }
 
@@ -569,6 +575,13 @@ int mk_set_xcd_bands(int bands) {
     return MK_OK;
 }
 
+int mk_set_adaptive_help(int on) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (on != 0 && on != 1) return fail(MK_ERR_INVALID_ARG, "help must be 0 or 1");
+    g_set.help = on;
+    return MK_OK;
+}
+
 int mk_set_num_workgroups(int num_wg) {
     std::lock_guard<std::mutex> lk(g_mu);
     if (num_wg != 0 && (num_wg < 2 || num_wg > kMaxWG))
@@ -603,7 +616,7 @@ int mk_get_stats(mk_stats *out, uint32_t *maps, size_t maps_len) {
     DevState &d = *dp;
     if (!d.last.valid || !d.ws) return fail(MK_ERR_INVALID_ARG, "no fused launch on this device yet");
     const Launch &l = d.last;
-    const size_t need = 10ull * l.T + 2ull * l.Ch + 2ull * kTraceCap;
+    const size_t need = 10ull * l.T + 3ull * l.Ch + 2ull * kTraceCap;
     if (maps && maps_len < need)
         return fail(MK_ERR_INVALID_ARG, "maps_len %zu < %zu words", maps_len, need);
     hipError_t e = hipDeviceSynchronize();
@@ -650,6 +663,8 @@ int mk_get_stats(mk_stats *out, uint32_t *maps, size_t maps_len) {
     out->keep_compute = l.keep;
     out->controller_cap = l.cap;
     out->xcd_bands = l.bands;
+    out->adaptive_help = l.help;
+    out->sticky_errors = snap.sticky;
 
     if (maps) {
         uint32_t *p = maps;
@@ -658,31 +673,38 @@ int mk_get_stats(mk_stats *out, uint32_t *maps, size_t maps_len) {
             {v.cowner, l.T}, {v.rowner, l.T}, {v.trace, 2ull * kTraceCap},
             {v.timeline, l.T}, {v.timeline + d.Tcap, l.T}, {v.timeline + 2ull * d.Tcap, l.T},
             {v.timeline + 3ull * d.Tcap, l.T}, {v.timeline + 4ull * d.Tcap, l.T},
-            {v.timeline + 5ull * d.Tcap, l.T}};
+            {v.timeline + 5ull * d.Tcap, l.T}, {v.chunk_release, l.Ch}};
         for (auto &pt : parts) {
             e = hipMemcpy(p, pt.src, 4 * pt.n, hipMemcpyDeviceToHost);
             if (e != hipSuccess) return hip_fail(e, "hipMemcpy(maps)");
             p += pt.n;
         }
     }
-    if (snap.error == kErrXcd) {
+    // Errors are sticky across launches: the word gathers every kind any
+    // launch since the last report raised, so a failed launch followed by
+    // clean ones is still reported.  Reporting one marks the workspace for
+    // a clean start (control block, sticky word and per-call counters).
+    const uint32_t sticky = snap.sticky | (snap.error == kErrXcd ? kStickyXcd : 0u) |
+                            (snap.error == kErrTimeout ? kStickyTimeout : 0u) |
+                            (snap.violations ? kStickyProtocol : 0u);
+    if (sticky) d.dirty = true;
+    if (sticky & kStickyXcd) {
         // a workgroup ran on another XCD than its index implies: the launch's
         // hand-off assumption failed, so tiles no longer stay on one XCD
-        d.dirty = true;
         d.xcd_ok = false;
         out->status = MK_ERR_PROTOCOL;
         fail(MK_ERR_PROTOCOL, "a workgroup ran on an unexpected XCD; result not valid");
         return MK_ERR_PROTOCOL;
     }
-    if (snap.error == kErrTimeout) {
-        d.dirty = true;
+    if (sticky & kStickyTimeout) {
         out->status = MK_ERR_TIMEOUT;
-        fail(MK_ERR_TIMEOUT, "a bounded wait in the fused kernel expired");
+        fail(MK_ERR_TIMEOUT, "a bounded wait in the fused kernel expired (this launch or an earlier "
+                             "one since the last report)");
         return MK_ERR_TIMEOUT;
     }
-    if (snap.violations) {
+    if (sticky & kStickyProtocol) {
         out->status = MK_ERR_PROTOCOL;
-        fail(MK_ERR_PROTOCOL, "%u flag/counter violations", snap.violations);
+        fail(MK_ERR_PROTOCOL, "flag/counter violations (%u in the last launch)", snap.violations);
         return MK_ERR_PROTOCOL;
     }
     out->status = MK_OK;

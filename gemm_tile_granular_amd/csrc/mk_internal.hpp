@@ -16,6 +16,11 @@ constexpr int kMaxXcd = 8;            // XCDs on MI355X (tile partitions)
 
 enum Mode : int32_t { kAdaptive = 0, kStatic = 1, kDeterministic = 2 };
 enum Err : uint32_t { kErrNone = 0, kErrTimeout = 1, kErrXcd = 2 };
+// Bits of the sticky error word: every kind of error any launch raised since
+// the word was last cleared (by mk_get_stats, through a workspace reinit).
+constexpr uint32_t kStickyTimeout = 1u << 0;
+constexpr uint32_t kStickyXcd = 1u << 1;
+constexpr uint32_t kStickyProtocol = 1u << 2;
 
 // Per-launch control block in device memory.  The last workgroup to leave a
 // launch copies it into the snapshot and restores the initial values below,
@@ -52,6 +57,7 @@ struct alignas(256) Live {
     uint32_t ns_max;           //                                    (init 0)
     uint32_t trace_len;        // written by workgroup 0 at exit     (init 0)
     uint32_t ns_final;         // written at exit                    (init 0)
+    uint32_t sticky;           // kSticky* bits; NOT restored at launch end (init 0)
     uint64_t t_start;          // min over workgroups                (init ~0)
     uint64_t t_end;            // max                                (init 0)
 };
@@ -59,7 +65,7 @@ struct alignas(256) Live {
 // Workspace: one device allocation per device.
 //   [Live][Live snapshot][trace 2*kTraceCap u32]
 //   [tile_flag Tcap][tile_cnt Tcap][chunk_cnt Chcap][chunk_flag Chcap]
-//   [compute_owner Tcap][reduce_owner Tcap][timeline 6*Tcap]
+//   [chunk_release Chcap][compute_owner Tcap][reduce_owner Tcap][timeline 6*Tcap]
 struct WsView {
     Live *live;
     Live *snap;
@@ -68,6 +74,7 @@ struct WsView {
     uint32_t *tile_cnt;
     uint32_t *chunk_cnt;
     uint32_t *chunk_flag;
+    uint32_t *chunk_release;   // constant-clock ticks (low 32 bits) of each chunk's release
     uint32_t *cowner;
     uint32_t *rowner;
     uint32_t *timeline;   // [6][Tcap]: compute start/end, reduce start/end, choice time compute/reduce
@@ -106,6 +113,7 @@ struct FusedArgs {
     int32_t ns_cap;           // most reduce workgroups the controller sets while compute remains
     uint64_t timeout_ticks;   // bound on any wait, constant-clock ticks
     int64_t skip_publish;     // fault injection: tile whose flag is never set (-1 none)
+    int32_t help;             // adaptive: a reducer whose ticket is not ready computes meanwhile
     WsView ws;
 };
 

@@ -688,10 +688,12 @@ struct ReduceGroup {
 
 // Region of TM rows x BW columns at (m0, n0): the tiles of one compute block.
 // Rows past M are masked; peer p's partial starts p*MN elements into peers.
-template <int TM, int BW, int NT, int PP, int kLoadPol, int kStorePol, int KIB>
+// `issued()` runs once the first group's loads are in flight (before them
+// for the tallest tiles).
+template <int TM, int BW, int NT, int PP, int kLoadPol, int kStorePol, int KIB, class Issued>
 __device__ __forceinline__ void reduce_tile_pp(const float *__restrict__ peers, float *__restrict__ C,
                                                int64_t M, int64_t N, int64_t MN, int P, int64_t m0,
-                                               int64_t n0) {
+                                               int64_t n0, Issued &&issued) {
     using RG = ReduceGeom<TM, BW, NT>;
     constexpr int PB = 8;                   // peer block when PP is the generic 0
     constexpr int UP = ReducePlan<(PP > 0 ? PP : PB), NT, KIB>::U;
@@ -702,7 +704,12 @@ __device__ __forceinline__ void reduce_tile_pp(const float *__restrict__ peers, 
     const int64_t base = m0 * N + n0;
     const int cc = (tid % RG::C4) * 4;
     const int r0 = tid / RG::C4;
-    const bool col_ok = n0 + cc < N;
+    // rows and columns of the region inside the output, compared in 32 bits
+    // (uniform per task; 64-bit per-lane bounds would hold register pairs
+    // across the whole load pipeline)
+    const int mr = (int)(M - m0 < TM ? M - m0 : TM);
+    const int nr = (int)(N - n0 < BW ? N - n0 : BW);
+    const bool col_ok = cc < nr;
 
     if constexpr (PP > 0) {
         // one peer's buffer resource at a time: a resource per peer held
@@ -712,7 +719,7 @@ __device__ __forceinline__ void reduce_tile_pp(const float *__restrict__ peers, 
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int r = (gi * U + u) * RG::RP + r0;
-                g.off[u] = ((int)col_ok & (int)(m0 + r < M)) ? (uint32_t)((r * N + cc) * 4) : kOOB;
+                g.off[u] = ((int)col_ok & (int)(r < mr)) ? (uint32_t)((r * N + cc) * 4) : kOOB;
                 g.v[0][u] = __builtin_amdgcn_raw_buffer_load_b128(rc, g.off[u], 0, kLoadPol);
             }
 #pragma unroll
@@ -734,7 +741,13 @@ __device__ __forceinline__ void reduce_tile_pp(const float *__restrict__ peers, 
             }
         };
         ReduceGroup<PP, U> g0, g1;
+        // Tall tiles (eight waves, every register taken by the GEMM) read the
+        // caller's returns before the first loads: held across them, the
+        // compiler spilled to scratch inside the load pipeline.
+        constexpr bool kFirst = TM >= 256;
+        if constexpr (kFirst) issued();
         load(g0, 0);
+        if constexpr (!kFirst) issued();
 #pragma unroll
         for (int gi = 0; gi < G; gi += 2) {
             if (gi + 1 < G) load(g1, gi + 1);
@@ -746,6 +759,7 @@ __device__ __forceinline__ void reduce_tile_pp(const float *__restrict__ peers, 
         }
     } else {
         // generic peer count: one group at a time, peers in blocks of PB
+        bool first = true;
         for (int gi = 0; gi < G; ++gi) {
             const auto rc = scalar_rsrc(C + base);
             f32x4 acc[U];
@@ -753,8 +767,12 @@ __device__ __forceinline__ void reduce_tile_pp(const float *__restrict__ peers, 
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int r = (gi * U + u) * RG::RP + r0;
-                off[u] = ((int)col_ok & (int)(m0 + r < M)) ? (uint32_t)((r * N + cc) * 4) : kOOB;
+                off[u] = ((int)col_ok & (int)(r < mr)) ? (uint32_t)((r * N + cc) * 4) : kOOB;
                 acc[u] = __builtin_amdgcn_raw_buffer_load_b128(rc, off[u], 0, kLoadPol);
+            }
+            if (first) {
+                issued();
+                first = false;
             }
             int p = 0;
             for (; p + PB <= P; p += PB) {
@@ -786,15 +804,16 @@ __device__ __forceinline__ void reduce_tile_pp(const float *__restrict__ peers, 
 
 // Dispatch on the peer count: the R-1 of 2, 4, 8 and 16 ranks get straight-line
 // pipelined code; other counts take the blocked loop.
-template <int TM, int BW, int NT, int kLoadPol, int kStorePol, int KIB>
+template <int TM, int BW, int NT, int kLoadPol, int kStorePol, int KIB, class Issued>
 __device__ __forceinline__ void reduce_tile(const float *__restrict__ peers, float *__restrict__ C,
-                                            int64_t M, int64_t N, int64_t MN, int P, int64_t m0, int64_t n0) {
+                                            int64_t M, int64_t N, int64_t MN, int P, int64_t m0, int64_t n0,
+                                            Issued &&issued) {
     switch (P) {
 #define MK_REDUCE_CASE(k) \
-    case k: reduce_tile_pp<TM, BW, NT, k, kLoadPol, kStorePol, KIB>(peers, C, M, N, MN, P, m0, n0); break;
+    case k: reduce_tile_pp<TM, BW, NT, k, kLoadPol, kStorePol, KIB>(peers, C, M, N, MN, P, m0, n0, issued); break;
         MK_REDUCE_CASE(1) MK_REDUCE_CASE(3) MK_REDUCE_CASE(7) MK_REDUCE_CASE(15)
 #undef MK_REDUCE_CASE
-        default: reduce_tile_pp<TM, BW, NT, 0, kLoadPol, kStorePol, KIB>(peers, C, M, N, MN, P, m0, n0); break;
+        default: reduce_tile_pp<TM, BW, NT, 0, kLoadPol, kStorePol, KIB>(peers, C, M, N, MN, P, m0, n0, issued); break;
     }
 }
 
@@ -884,16 +903,69 @@ struct Sched {
     uint32_t trace_n;          // workgroup 0: target changes it has recorded
 };
 
+// Exactly-once and chunk counters of a reduced tile (a reduce task is one
+// tile).  Thread 0 issues them as soon as the task's stores have drained at
+// device scope (a released chunk must be complete), and reads what they
+// return once its next task is under way: inside the next reduce task right
+// after that task's first loads are issued, before the next compute task, or
+// before any wait for a tile's flag.  The release therefore follows the
+// chunk's last tile by one atomic round trip, which overlaps other work.
+struct CntRead {
+    uint32_t c;        // chunk of the tile; kNoChunk: nothing pending
+    uint32_t want;     // the chunk's count once this call has reduced all its tiles
+    uint32_t old_t, old_c;
+};
+constexpr uint32_t kNoChunk = 0xFFFFFFFFu;
+
+__device__ __forceinline__ CntRead cnt_issue(const FusedArgs &a, uint32_t t) {
+    CntRead k;
+    k.c = t / a.tpc;
+    const uint32_t first = k.c * a.tpc;
+    const uint32_t size = (a.T - first) < a.tpc ? (a.T - first) : a.tpc;
+    k.want = size * a.calls;
+    k.old_t = add_relaxed(&a.ws.tile_cnt[t], 1u);
+    k.old_c = add_relaxed(&a.ws.chunk_cnt[k.c], 1u);
+    return k;
+}
+
+__device__ __forceinline__ void note_violation(Live *L) {
+    add_relaxed(&L->violations, 1u);
+    __hip_atomic_fetch_or(&L->sticky, kStickyProtocol, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Thread 0: exactly-once check, and release of a chunk whose last tile this
+// was ("【学习】mKernel 分析" section 2.3: the last locally reduced tile of a
+// chunk lets it go, without waiting for the rest of the GEMM).  Clears k.
+__device__ __forceinline__ void cnt_finish(const FusedArgs &a, Live *L, CntRead &k) {
+    if (k.c == kNoChunk) return;
+    const uint32_t c = k.c, want = k.want;
+    k.c = kNoChunk;
+    if (k.old_t != a.calls - 1) note_violation(L);
+    if (k.old_c + 1 == want) {
+        // where a network send of the chunk would be posted: every tile of it
+        // was stored write-through and drained before its count was taken
+        a.ws.chunk_release[c] = (uint32_t)ticks_now();
+        st_relaxed(&a.ws.chunk_flag[c], a.epoch);
+        add_relaxed(&L->chunks_released.v, 1u);
+    } else if (k.old_c + 1 > want) {
+        note_violation(L);
+    }
+}
+
 __device__ __forceinline__ bool timed_out(const FusedArgs &a, Live *L, uint64_t since) {
     if (ticks_now() - since <= a.timeout_ticks) return false;
     __hip_atomic_fetch_max(&L->error, (uint32_t)kErrTimeout, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_or(&L->sticky, kStickyTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return true;
 }
 
 // Wait (bounded) until tile t carries this launch's epoch.  False on timeout or
-// on an error raised by another workgroup.
-__device__ bool wait_ready(const FusedArgs &a, Live *L, uint32_t t) {
+// on an error raised by another workgroup.  Counters still in flight are read
+// (and a chunk released) before the first poll, so no release waits on it.
+__device__ __forceinline__ bool wait_ready(const FusedArgs &a, Live *L, uint32_t t, CntRead &pend) {
+    if (ld_relaxed(&a.ws.tile_flag[t]) == a.epoch) return true;
+    cnt_finish(a, L, pend);
     const uint64_t since = ticks_now();
     for (;;) {
         if (ld_relaxed(&a.ws.tile_flag[t]) == a.epoch) return true;
@@ -941,15 +1013,15 @@ __device__ __forceinline__ bool tile_ready(const FusedArgs &a, uint32_t t) {
 // yet computes a block meanwhile and keeps the ticket: a block waiting for its
 // input helps the other role ("【学习】mKernel 分析" section 2.4, read in the
 // direction data flows here, from compute to reduce).
-__device__ Decision next_task(const FusedArgs &a, const Parts &pt, const Blocks &bk, Live *L, uint32_t wg,
-                             Sched &s) {
+__device__ __forceinline__ Decision next_task(const FusedArgs &a, const Parts &pt, const Blocks &bk, Live *L, uint32_t wg,
+                             Sched &s, CntRead &pend) {
     const uint32_t B = (uint32_t)a.nwg;
     if (a.mode == kDeterministic) {
         const uint32_t ns = (uint32_t)a.ns_init;
         if (wg < ns) {
             const uint32_t t = wg + s.det_i * ns;
             if (t >= a.T) return {kRoleExit, 0, ns};
-            if (!wait_ready(a, L, t)) return {kRoleExit, 0, ns};
+            if (!wait_ready(a, L, t, pend)) return {kRoleExit, 0, ns};
             ++s.det_i;
             return {kRoleReduce, t, ns};
         }
@@ -977,14 +1049,14 @@ __device__ Decision next_task(const FusedArgs &a, const Parts &pt, const Blocks 
                 if (t == kNoTile) continue;     // empty ticket: take another
                 if (!seen) {
                     uint32_t cb;
-                    if (a.mode == kAdaptive && !s.compute_exhausted && !tile_ready(a, t) &&
+                    if (a.mode == kAdaptive && a.help && !s.compute_exhausted && !tile_ready(a, t) &&
                         claim_compute(a, pt, L, wg, s, cb)) {
                         s.pending_role = kRoleReduce;
                         s.pending_q = q;
                         s.pending_ns = ns_seen;
                         return {kRoleCompute, cb, s.target | kHelp};
                     }
-                    if (!wait_ready(a, L, t)) return {kRoleExit, 0, ns_seen};
+                    if (!wait_ready(a, L, t, pend)) return {kRoleExit, 0, ns_seen};
                 }
                 return {kRoleReduce, t, ns_seen};
             }
@@ -1134,6 +1206,7 @@ __device__ void finish_launch(const FusedArgs &a, Live *L) {
     const uint32_t released = ld_relaxed(&L->chunks_released.v);
     const uint32_t violations = ld_relaxed(&L->violations);
     const uint32_t error = ld_relaxed(&L->error);
+    const uint32_t sticky = ld_relaxed(&L->sticky);
     const uint32_t ns_min = ld_relaxed(&L->ns_min);
     const uint32_t ns_max = ld_relaxed(&L->ns_max);
     const uint32_t trace_len = ld_relaxed(&L->trace_len);
@@ -1156,6 +1229,7 @@ __device__ void finish_launch(const FusedArgs &a, Live *L) {
     S->chunks_released.v = released;
     S->violations = violations;
     S->error = error;
+    S->sticky = sticky;   // L->sticky itself stays: errors of every launch are kept
     S->ns_min = ns_min;
     S->ns_max = ns_max;
     S->trace_len = trace_len;
@@ -1231,63 +1305,19 @@ __device__ __forceinline__ void ctl_finish(const FusedArgs &a, Live *L, uint32_t
     s.target = controller_step(a, L, wg, s, cw, rw, c.raw_target);
 }
 
-// Exactly-once and chunk counters of the tiles of a reduced block.  They are
-// taken only after the block's stores have drained (a released chunk must be
-// complete),
-// at the end of the workgroup's next task, where their round trip overlaps
-// that task's own store drain.
-struct CntRead {
-    uint32_t t0, n;    // tiles [t0, t0 + n) of the block; n == 0: nothing pending
-    uint32_t old_t[kMaxTpb], old_c[kMaxTpb];
-};
-
-__device__ __forceinline__ CntRead cnt_issue(const FusedArgs &a, uint32_t t0, uint32_t n) {
-    CntRead k;
-    k.t0 = t0;
-    k.n = n;
-#pragma unroll
-    for (int i = 0; i < kMaxTpb; ++i) {
-        k.old_t[i] = k.old_c[i] = 0;
-        if ((uint32_t)i < n) {
-            k.old_t[i] = add_relaxed(&a.ws.tile_cnt[t0 + i], 1u);
-            k.old_c[i] = add_relaxed(&a.ws.chunk_cnt[(t0 + i) / a.tpc], 1u);
-        }
-    }
-    return k;
-}
-
-// Thread 0: exactly-once check, and release of a chunk whose last tile this
-// was ("【学习】mKernel 分析" section 2.3).
-__device__ __forceinline__ void cnt_finish(const FusedArgs &a, Live *L, const CntRead &k) {
-#pragma unroll
-    for (int i = 0; i < kMaxTpb; ++i) {
-        if ((uint32_t)i >= k.n) break;
-        const uint32_t t = k.t0 + i;
-        const uint32_t c = t / a.tpc;
-        const uint32_t first = c * a.tpc;
-        const uint32_t size = (a.T - first) < a.tpc ? (a.T - first) : a.tpc;
-        const uint32_t want = size * a.calls;
-        if (k.old_t[i] != a.calls - 1) add_relaxed(&L->violations, 1u);
-        if (k.old_c[i] + 1 == want) {
-            // where a network send of the chunk would be posted
-            st_relaxed(&a.ws.chunk_flag[c], a.epoch);
-            add_relaxed(&L->chunks_released.v, 1u);
-        } else if (k.old_c[i] + 1 > want) {
-            add_relaxed(&L->violations, 1u);
-        }
-    }
-}
-
 // Cache policies of the tile hand-off.  When every tile is computed and
 // reduced on one XCD (LOCAL), producer and consumer share that XCD's L2: the
 // partial is stored write-back and read past the reader's L1 (sc0).  Across
 // XCDs, whose L2s are not coherent with each other, the partial is written
-// through (sc1) and read at device scope (sc1).  The reduced tile is streamed
-// out (nt).
+// through (sc1) and read at device scope (sc1).  The reduced tile is what a
+// released chunk hands on (to a sender, in the multi-GPU kernel), so in both
+// modes it is streamed out write-through (nt sc1): once its stores have
+// drained it is visible at device scope, and the chunk's release needs no
+// L2 writeback.
 template <bool LOCAL> struct HandOff {
     static constexpr int kPartialStore = LOCAL ? kPolicyDefault : kPolicyCoherentStore;
     static constexpr int kPartialLoad = LOCAL ? 1 : kPolicyCoherentLoad;
-    static constexpr int kResultStore = LOCAL ? kPolicyStream : kPolicyCoherentStream;
+    static constexpr int kResultStore = kPolicyCoherentStream;
 };
 
 // static LDS of the fused kernel: at least the GEMM ring, and more than
@@ -1344,9 +1374,11 @@ void fused_gemm_reduce_kernel(
         // says (workgroup w on XCD w mod 8); otherwise stop everything
         uint32_t xcc;
         asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-        if ((xcc & 0xFu) != wg % (uint32_t)a.nxcd)
+        if ((xcc & 0xFu) != wg % (uint32_t)a.nxcd) {
             __hip_atomic_fetch_max(&L->error, (uint32_t)kErrXcd, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_or(&L->sticky, kStickyXcd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     if (tid == 0) {
         s.det_i = 0;
@@ -1372,10 +1404,11 @@ void fused_gemm_reduce_kernel(
     // reads the controller inputs and claims its next task (under the target
     // of its previous controller step), all at once; the round trips overlap
     // the task's stores, and the controller step that follows sets the role
-    // for the task after.  The counters of a reduced tile wait for the end
-    // of the workgroup's next task (see CntRead).
-    __shared__ uint32_t sh_pend_t0, sh_pend_n;   // reduced tiles whose counters are pending
-    if (tid == 0) sh_pend_n = 0;
+    // for the task after.  The counters of a reduced tile are issued right
+    // after its stores drain and read during the next task (see CntRead).
+    CntRead pend;   // thread 0 only
+    pend.c = kNoChunk;
+    pend.want = pend.old_t = pend.old_c = 0;
     // reduce-scatter: the other ranks' tile rows, plain GEMM blocks each
     // stored straight into this rank's inbox slot at its owner.  Partition x
     // of the nx column bands of those rows has its own queue, taken row by
@@ -1421,7 +1454,7 @@ void fused_gemm_reduce_kernel(
     for (;;) {
         if (tid == 0) {
             s.decide_t0 = ticks_now();
-            const Decision d = next_task(a, pt, bk, L, wg, s);
+            const Decision d = next_task(a, pt, bk, L, wg, s, pend);
             s.decide_t1 = ticks_now();
             if (d.role == kRoleReduce) prefetch_claim(a, pt, L, wg, s, d);
             sh_dec = d;
@@ -1445,18 +1478,22 @@ void fused_gemm_reduce_kernel(
         const int tj = (int)(t0 % (uint32_t)a.tiles_n);
 
         CtlRead ctl;
-        CntRead cnt;
         Early early;
         // progress is counted in tiles for both roles, so the controller's
         // R_p C_p is the same remaining time whatever the block size
         auto work_done = [&](int role) {
             if (tid == 0) {
-                cnt = cnt_issue(a, sh_pend_t0, sh_pend_n);
                 ctl = ctl_issue(a, L, role, nt, cycles_now() - sh_c0, sh_r0, ticks_now());
                 early = early_issue(a, pt, bk, L, wg, s);
             }
         };
+        // the previous reduce task's counters: read once this task's first
+        // loads are in flight (reduce), or before the K loop (compute)
+        auto counters_back = [&]() {
+            if (tid == 0) cnt_finish(a, L, pend);
+        };
         if (d.role == kRoleCompute) {
+            counters_back();
             G::block(ln, a.A, a.B, a.C, Mp, Np, Kp, (int64_t)ti * TM, (int64_t)tj * TN, lds,
                      [&] { work_done(kRoleCompute); });
         } else {
@@ -1466,15 +1503,18 @@ void fused_gemm_reduce_kernel(
                 // the peers are [P, M_all, N]: the shard's rows come first
                 if constexpr (RS)
                     reduce_tile<TM, TN, G::NT, H::kPartialLoad, H::kResultStore, 64>(
-                        a.peers, a.C, Mp, Np, a.peer_mn, a.P, (int64_t)ti * TM, (int64_t)tj * TN);
+                        a.peers, a.C, Mp, Np, a.peer_mn, a.P, (int64_t)ti * TM, (int64_t)tj * TN,
+                        counters_back);
                 else
                     reduce_tile<TM, TN, G::NT, H::kPartialLoad, H::kResultStore, LOCAL ? 128 : 64>(
-                        a.peers, a.C, Mp, Np, Mp * Np, a.P, (int64_t)ti * TM, (int64_t)tj * TN);
+                        a.peers, a.C, Mp, Np, Mp * Np, a.P, (int64_t)ti * TM, (int64_t)tj * TN,
+                        counters_back);
+            } else {
+                counters_back();
             }
             work_done(kRoleReduce);
         }
         if (tid == 0) {
-            cnt_finish(a, L, cnt);
             ctl_finish(a, L, wg, d.role, ctl, s);
             early_finish(s, early);
         }
@@ -1485,6 +1525,15 @@ void fused_gemm_reduce_kernel(
         __syncthreads();
         if (tid == 0) {
             const uint32_t t_end = (uint32_t)ticks_now();
+            // a reduced tile is complete at device scope: count it now.  (The
+            // whole record is rewritten either way, so none of it stays live
+            // across a compute task.)
+            if (d.role == kRoleReduce) {
+                pend = cnt_issue(a, t0);
+            } else {
+                pend.c = kNoChunk;
+                pend.want = pend.old_t = pend.old_c = 0;
+            }
             for (uint32_t k = 0; k < nt; ++k) {
                 const uint32_t t = t0 + k;
                 if (d.role == kRoleCompute) {
@@ -1501,8 +1550,6 @@ void fused_gemm_reduce_kernel(
                 a.ws.timeline[(d.role == kRoleCompute ? 4u : 5u) * a.Tcap + t] =
                     (uint32_t)(s.decide_t1 - s.decide_t0);
             }
-            sh_pend_t0 = t0;
-            sh_pend_n = d.role == kRoleCompute ? 0u : nt;
             if (s.last_role != kRoleNone && s.last_role != d.role) add_relaxed(&L->role_switches, 1u);
             s.last_role = d.role;
         }
@@ -1510,9 +1557,8 @@ void fused_gemm_reduce_kernel(
         __syncthreads();
     }
     if (tid == 0) {
-        // counters of the last reduced tile; nothing else is in flight
-        const CntRead k = cnt_issue(a, sh_pend_t0, sh_pend_n);
-        cnt_finish(a, L, k);
+        // counters of the last reduced tile
+        cnt_finish(a, L, pend);
     }
     // then whatever is left outside the shard
     if constexpr (RS)
@@ -1619,6 +1665,7 @@ __device__ void live_init(Live *L) {
     L->ns_max = 0;
     L->trace_len = 0;
     L->ns_final = 0;
+    L->sticky = 0;
     L->role_compute.v = 0;
     L->role_reduce.v = 0;
     L->t_start = ~(uint64_t)0;

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MK_ABI_VERSION 1
+#define MK_ABI_VERSION 2
 
 typedef enum {
     MK_OK = 0,
@@ -211,6 +211,15 @@ int mk_set_controller_cap(int cap);
 int mk_set_xcd_bands(int bands);
 
 /*
+ * mk_set_adaptive_help -- 1 (default): under MK_PART_ADAPTIVE, a reduce-role
+ * workgroup whose next tile is not published computes a block meanwhile and
+ * keeps its reduce ticket ("【学习】mKernel 分析" section 2.4: a block waiting
+ * for its input helps the other role).  0: it waits, as in the plain rule.
+ * Static partitions never help.  Errors: MK_ERR_INVALID_ARG unless 0 or 1.
+ */
+int mk_set_adaptive_help(int on);
+
+/*
  * mk_set_num_workgroups -- persistent workgroups per launch (B).  0 (default)
  * = every workgroup that can be resident: the compute-unit count (256 on
  * MI355X) times the workgroups one CU holds for the tile configuration (1 for
@@ -272,31 +281,45 @@ typedef struct mk_stats {
     uint32_t keep_compute;        /* compute workgroups the controller kept      */
     uint32_t controller_cap;      /* most reducers while compute remained        */
     uint32_t xcd_bands;           /* column bands of the XCD partitions (1: rows) */
+    uint32_t adaptive_help;       /* 1: waiting reducers computed meanwhile        */
+    uint32_t sticky_errors;       /* bit 0 timeout, 1 XCD mismatch, 2 protocol:
+                                     every kind raised by any launch since the
+                                     last mk_get_stats (see there)             */
 } mk_stats;
 
 /* Words per map in the optional `maps` output of mk_get_stats, in order:
  *   tile_flag[T] | tile_reduce_cnt[T] | chunk_cnt[Ch] | chunk_flag[Ch] |
  *   compute_owner[T] | reduce_owner[T] | ns_trace[2 * MK_TRACE_CAP] |
  *   compute_start[T] | compute_end[T] | reduce_start[T] | reduce_end[T] |
- *   compute_choice_ticks[T] | reduce_choice_ticks[T]
+ *   compute_choice_ticks[T] | reduce_choice_ticks[T] | chunk_release[Ch]
  * Owner words are (help << 31) | (reduce target seen << 16) | workgroup, where
  * help marks a compute task taken by a workgroup waiting on a reduce ticket
  * (adaptive mode only).  Trace entries are
  * pairs (low 32 bits of the constant clock, new target), one for each step
  * of workgroup 0 that changed the target: a sample of the target's path.  The four timeline
  * maps hold the low 32 bits of the constant clock at each task's start and
- * end (compare with kernel_ticks_start modulo 2^32); the last two, the ticks
- * the workgroup spent choosing the task (claim and readiness wait). */
+ * end (compare with kernel_ticks_start modulo 2^32); the next two, the ticks
+ * the workgroup spent choosing the task (claim and readiness wait).
+ * chunk_release[c] is the constant clock (low 32 bits) at which chunk c was
+ * released: its last tile's counters came back after that tile's stores had
+ * drained, write-through, at device scope ("【学习】mKernel 分析" section 2.3:
+ * the last reduced tile lets the chunk go at once). */
 #define MK_TRACE_CAP 1024
 
 /*
- * mk_get_stats -- waits for the last fused launch on the current device
- * (hipStreamSynchronize of its stream), then fills *out.  If maps is non-NULL
- * it receives the maps above (maps_len is its capacity in uint32 words; it
- * must hold 10T + 2Ch + 2*MK_TRACE_CAP words).  out->struct_size must be set.
- * Returns out->status (MK_OK when the launch was clean), or an argument/HIP
- * error.  A launch that ended in a timeout leaves the workspace to be cleared
- * at the next launch.
+ * mk_get_stats -- waits for all work on the current device
+ * (hipDeviceSynchronize), then fills *out with the statistics of the last
+ * fused launch.  If maps is non-NULL it receives the maps above (maps_len is
+ * its capacity in uint32 words; it must hold 10T + 3Ch + 2*MK_TRACE_CAP
+ * words).  out->struct_size must be set.
+ * Errors are sticky: out->status and the return value report every timeout,
+ * XCD mismatch or flag/counter violation raised by ANY fused launch on this
+ * device since the previous mk_get_stats (MK_ERR_PROTOCOL for an XCD
+ * mismatch or violations, MK_ERR_TIMEOUT for a timeout), not only by the
+ * last one; out->sticky_errors names the kinds.  Reporting an error marks the
+ * workspace so that the next launch starts from a cleared control block and
+ * cleared per-call counters.  Otherwise returns MK_OK, or an argument/HIP
+ * error.
  */
 int mk_get_stats(mk_stats *out, uint32_t *maps, size_t maps_len);
 

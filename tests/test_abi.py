@@ -69,7 +69,7 @@ def test_stats_struct_matches_header(mk):
     got = [(n, t) for n, t in mk.Stats._fields_]
     assert [n for n, _ in got] == [n for n, _ in fields]
     assert all(t == want[c] for (_, t), (_, c) in zip(got, fields))
-    assert ctypes.sizeof(mk.Stats) == 160
+    assert ctypes.sizeof(mk.Stats) == 168
 
 
 def test_abi_version_and_trace_cap(mk):
@@ -219,6 +219,9 @@ def test_kernels_fit_their_register_and_lds_budget(mk):
     for name, r in res.items():
         assert r["LDS Size"] <= 160 * 1024, name
         assert r["ScratchSize"] == 0, (name, r)
+        # no vector register spills either (SGPR spills land in VGPR lanes,
+        # which costs no memory traffic)
+        assert r.get("VGPRs Spill", 0) == 0, (name, r)
     for name, r in fused.items():
         if "ILi256ELi128E" in name:
             assert r["Occupancy"] == 2, (name, r)

@@ -49,3 +49,74 @@ def test_algorithmic_work_of_the_named_workloads():
         w = wl.workload(name)
         assert w.flops == 2 * w.M * w.N * w.K
         assert w.algorithmic_bytes == 2 * w.M * w.K + 2 * w.K * w.N + 4 * w.peers * w.M * w.N + 4 * w.M * w.N
+
+
+class _FakeLib:
+    """Stands in for the binding: launches are counted, and the launch with
+    index `faulty` ends in a timeout that mk_get_stats reports (stickily)
+    at the next call, as the library does."""
+
+    def __init__(self, faulty):
+        self.faulty = faulty
+        self.launches = 0
+        self.pending = 0
+
+    def gemm_reduce_local(self, *a, **k):
+        if self.launches == self.faulty:
+            self.pending |= 1
+        self.launches += 1
+
+    def get_stats(self, maps=False, raise_on_error=True):
+        bits, self.pending = self.pending, 0
+        rc = -4 if bits else 0
+        return {"rc": rc, "status": rc, "status_name": "MK_ERR_TIMEOUT" if bits else "MK_OK",
+                "sticky_errors": bits}
+
+
+@pytest.mark.parametrize("faulty", [0, 7, 19])
+def test_a_failed_launch_anywhere_in_a_leg_fails_the_bench(faulty):
+    """A timeout in any launch of a timed leg (first, middle, last) makes the
+    leg's status check end the bench with a non-zero exit and no line."""
+    import bench
+    fake = _FakeLib(faulty)
+
+    class _Ev:
+        def __init__(self, enable_timing=True):
+            pass
+
+        def record(self, stream):
+            pass
+
+        def elapsed_time(self, other):
+            return 1.0
+
+    class _Torch:
+        class cuda:
+            Event = _Ev
+
+            @staticmethod
+            def synchronize():
+                pass
+
+    bench.time_leg(lambda: fake.gemm_reduce_local(), 20, 0, None, None, _Torch)
+    assert fake.launches == 20
+    with pytest.raises(SystemExit) as e:
+        bench.check_leg(fake, "fused")
+    assert e.value.code == 3
+
+
+def test_a_clean_leg_passes_the_status_check():
+    import bench
+    fake = _FakeLib(faulty=-1)
+    fake.gemm_reduce_local()
+    assert bench.check_leg(fake, "fused")["status"] == 0
+
+
+def test_bench_defaults_to_the_largest_workload():
+    import bench
+    import workloads as wl
+    args = bench.parse([])
+    assert args.workload == "all" and bench.HEADLINE == "compute_heavy"
+    biggest = max(wl.WORKLOADS.values(), key=lambda w: w.flops)
+    assert biggest.name == bench.HEADLINE
+    assert set(bench.SUITE) == set(wl.WORKLOADS)

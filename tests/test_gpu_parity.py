@@ -235,6 +235,90 @@ def test_timeout_is_reported_not_hung(mk):
     check_protocol(st2, w, "static", 2)
 
 
+def test_timeout_in_an_earlier_launch_is_not_lost(mk):
+    """Errors are sticky: a launch that times out, then clean launches of the
+    same shape with no report in between.  The next report still names the
+    timeout, the clean launches' output is right, and after the report a
+    launch starts from cleared counters (protocol state exact again)."""
+    import torch
+    from gemm_tile_granular_amd.tensors import upload
+    w = wl.custom(256, 256, 64, 1, 64, 64, 4, wid=609)
+    a, b, p = wl.make_inputs(w)
+    A, B, P, C = upload(a, b, p)
+    mk.set_partition("static", 2)
+    mk.set_timeout_us(20_000)
+    mk.set_fault_skip_publish(5)
+    try:
+        print("[gpu] sticky timeout: faulted launch", flush=True)
+        mk.gemm_reduce_local(A, B, P, C, 64, 64, 4)
+    finally:
+        mk.set_fault_skip_publish(-1)
+        mk.set_timeout_us(2_000_000)
+    print("[gpu] sticky timeout: two clean launches", flush=True)
+    for _ in range(2):
+        mk.gemm_reduce_local(A, B, P, C, 64, 64, 4)
+    st = mk.get_stats(maps=False, raise_on_error=False)
+    assert st["rc"] == mk.MK_ERR_TIMEOUT and st["status"] == mk.MK_ERR_TIMEOUT, st["status_name"]
+    assert st["sticky_errors"] & 1
+    torch.cuda.synchronize()
+    check_full(C.cpu().numpy(), a, b, p)
+    C2, st2 = run_fused(mk, w, a, b, p, mode="static", n_reduce=2)
+    check_full(C2, a, b, p)
+    check_protocol(st2, w, "static", 2)
+    assert st2["sticky_errors"] == 0
+
+
+def check_release_order(st, w):
+    """Each chunk's release stamp is no earlier than the end of every tile in
+    it (the last reduced tile lets the chunk go), and follows it closely."""
+    T, tpc = w.tiles, w.tiles_per_chunk
+    rel = st["chunk_release"].astype(np.uint32)
+    rend = st["reduce_end"].astype(np.uint32)
+    lags = []
+    for c in range(w.chunks):
+        tiles = np.arange(c * tpc, min(T, (c + 1) * tpc))
+        d = (rel[c] - rend[tiles]).astype(np.uint32).view(np.int32).astype(np.int64)
+        assert np.all(d >= 0), (c, d)
+        lags.append(int(d.min()))
+    hz = float(st["timer_hz"])
+    lags_us = np.array(lags) / hz * 1e6
+    # the release follows its last tile by about one atomic round trip
+    assert float(np.max(lags_us)) < 1000.0, float(np.max(lags_us))
+    return lags_us
+
+
+@pytest.mark.parametrize("mode", ["adaptive", "static", "deterministic"])
+def test_chunk_release_follows_its_last_tile(mk, mode):
+    w = wl.custom(1000, 1000, 512, 3, 128, 128, 4, wid=611)
+    a, b, p = wl.make_inputs(w)
+    C, st = run_fused(mk, w, a, b, p, mode=mode, n_reduce=5)
+    check_full(C, a, b, p)
+    check_protocol(st, w, mode, 5)
+    lags = check_release_order(st, w)
+    print(f"[gpu] {mode}: release lag median {np.median(lags):.2f} us, max {lags.max():.2f} us",
+          flush=True)
+
+
+def test_plain_controller_rule(mk):
+    """The pages' rule without this library's labelled variants: initial
+    target 2, no cap below B - keep, and reducers that wait instead of
+    helping.  Output against the oracle, protocol exact, no help marks."""
+    w = wl.custom(1000, 1000, 1024, 7, 128, 128, 4, wid=612)
+    a, b, p = wl.make_inputs(w)
+    mk.set_adaptive_help(False)
+    mk.set_controller_cap(1024)
+    try:
+        C, st = run_fused(mk, w, a, b, p, mode="adaptive", n_reduce=2)
+    finally:
+        mk.set_adaptive_help(True)
+        mk.set_controller_cap(0)
+    check_full(C, a, b, p)
+    check_protocol(st, w, "adaptive", 2)
+    assert st["adaptive_help"] == 0
+    assert not np.any(st["compute_owner"] >> 31)
+    assert st["controller_cap"] == st["num_wg"] - st["keep_compute"]
+
+
 FULL = ["tp_share", "reduce_heavy", "compute_heavy", "wide_many_peer"]
 
 
@@ -247,6 +331,7 @@ def test_full_size_workload_sampled(mk, name):
     # initial target (the controller cap) and cap
     C, st = run_fused(mk, w, a, b, p, mode="adaptive", n_reduce=0)
     check_protocol(st, w, "adaptive", 0)
+    check_release_order(st, w)
     tiles_m, tiles_n = oracle.tile_grid(w.M, w.N, w.tile_m, w.tile_n)
     rng = np.random.default_rng(7)
     check_sampled(C, a, b, p, rng, tiles=[(0, 0), (tiles_m - 1, tiles_n - 1),

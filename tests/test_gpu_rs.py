@@ -118,6 +118,29 @@ def test_reduce_scatter_full_oracle(mk, shape, mode):
     assert np.array_equal(R, Ru)
 
 
+STATIC_RS_SHAPES = [(1000, 1000, 1024, 3, 128, 128, 4), (600, 520, 512, 2, 256, 128, 4),
+                    (200, 136, 72, 3, 64, 64, 4)]
+
+
+@pytest.mark.parametrize("shape", STATIC_RS_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("which", ["2", "8", "B-8"])
+def test_reduce_scatter_static_partitions(mk, shape, which):
+    """Static partitions on the reduce-scatter share: few reducers (compute
+    workgroups leave for the outside rows early), one per XCD (the smallest
+    XCD-local static split) and all but one per XCD (the largest)."""
+    M, N, K, P, tm, tn, tpc = shape
+    n = {"2": 2, "8": 8, "B-8": mk.device_cu_count() - 8}[which]
+    w = wl.custom(M, N, K, P, tm, tn, tpc, wid=720 + M % 83)
+    a, b, p = wl.make_inputs(w)
+    r0 = wl.make_remote(w)
+    C, R, st = run_rs(mk, True, w, a, b, p, r0, mode="static", n_reduce=n)
+    check_rs_full(C, R, a, b, p, r0, w)
+    check_rs_protocol(st, w, "static", n)
+    Cu, Ru, _ = run_rs(mk, False, w, a, b, p, r0)
+    assert np.array_equal(C, Cu)
+    assert np.array_equal(R, Ru)
+
+
 def test_reduce_scatter_one_rank_is_the_gemm(mk):
     # R = 1: rank 0 owns every row; no remote buffer
     import torch
@@ -131,17 +154,24 @@ def test_reduce_scatter_one_rank_is_the_gemm(mk):
     check_full(C.cpu().numpy(), a, b, p)
 
 
-@pytest.mark.parametrize("name", ["tp_share", "compute_heavy"])
-def test_reduce_scatter_full_size_sampled(mk, name):
+@pytest.mark.parametrize("name,mode,n", [("tp_share", "adaptive", 3), ("compute_heavy", "adaptive", 3),
+                                         ("tp_share", "static", 2), ("tp_share", "static", 8),
+                                         ("tp_share", "static", -8)])
+def test_reduce_scatter_full_size_sampled(mk, name, mode, n):
     """The 4096x4096x1792 (128x128 tiles) and 16384x8192x8192 (256x128 tiles)
-    8-rank shares at full size, in the launch the bench times: sampled
-    elements against the oracle one at a time, the untouched rows
+    8-rank shares at full size, in the launch the bench times (and the
+    4096x4096x1792 share under static partitions, XCD-local at 8 and B-8):
+    sampled elements against the oracle one at a time, the untouched rows
     bit-exact, and fused equal to unfused everywhere."""
     w = wl.workload(name)
+    if n < 0:
+        n = mk.device_cu_count() + n
     a, b, p = wl.make_inputs(w)
     r0 = wl.make_remote(w)
-    C, R, st = run_rs(mk, True, w, a, b, p, r0, mode="adaptive")
-    check_rs_protocol(st, w, "adaptive", 3)
+    C, R, st = run_rs(mk, True, w, a, b, p, r0, mode=mode, n_reduce=n)
+    check_rs_protocol(st, w, mode, n)
+    if mode == "static" and 8 <= n <= mk.device_cu_count() - 8:
+        assert st["xcd_local"] == 1
     own = own_rows(w)
     rng = np.random.default_rng(11)
     for lo, hi, reduced in ((0, own, True), (own, w.M, False)):
