@@ -86,6 +86,8 @@ _vp, _i32, _i64, _u32p = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.P
 
 SIGNATURES = {
     "mk_gemm_reduce_local": (_i32, [_vp, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp]),
+    "mk_gemm_reduce_local_noalloc": (_i32, [_vp, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _i32, _i32, _i32,
+                                             _vp]),
     "mk_gemm_reduce_unfused": (_i32, [_vp, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp]),
     "mk_gemm_reduce_scatter_local": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32,
                                              _vp]),
@@ -169,6 +171,13 @@ def gemm_reduce_local(A, B, peers, C, tile_m: int, tile_n: int, tiles_per_chunk:
                       stream=None) -> None:
     """C = A.B + sum_p peers[p] in one persistent launch (mk_gemm_reduce_local)."""
     _call(lib.mk_gemm_reduce_local, A, B, peers, C, tile_m, tile_n, tiles_per_chunk, stream)
+
+
+def gemm_reduce_local_noalloc(A, B, peers, C, tile_m: int, tile_n: int, tiles_per_chunk: int = 4,
+                              stream=None) -> None:
+    """The same launch on the library's static workspace: the call allocates
+    no device memory (mk_gemm_reduce_local_noalloc; at most 8192 tiles)."""
+    _call(lib.mk_gemm_reduce_local_noalloc, A, B, peers, C, tile_m, tile_n, tiles_per_chunk, stream)
 
 
 def gemm_reduce_unfused(A, B, peers, C, tile_m: int, tile_n: int, tiles_per_chunk: int = 4,

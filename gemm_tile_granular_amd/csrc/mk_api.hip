@@ -6,9 +6,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <mutex>
-#include <string>
 #include <cstring>
-#include <vector>
 #include <cstdio>
 
 #include "mk.h"
@@ -18,7 +16,8 @@ namespace {
 
 using namespace mk;
 
-thread_local std::string g_last_error;
+// fixed buffer: recording an error allocates nothing
+thread_local char g_last_error[512];
 std::mutex g_mu;
 
 int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -28,7 +27,8 @@ int fail(int code, const char *fmt, ...) {
     va_start(ap, fmt);
     vsnprintf(buf, sizeof buf, fmt, ap);
     va_end(ap);
-    g_last_error = buf;
+    std::memcpy(g_last_error, buf, sizeof g_last_error);
+    g_last_error[sizeof g_last_error - 1] = '\0';
     return code;
 }
 
@@ -59,10 +59,11 @@ struct Launch {
     uint32_t local = 0, keep = 1, cap = 0, bands = 1, help = 1;
 };
 
-struct DevState {
-    bool init = false;
-    int num_cu = 0;
-    uint64_t timer_hz = 100000000ull;
+// Flags, counters, maps and control block of the fused launches, plus the
+// host-side bookkeeping of the epochs and calls made on them.  Each device
+// has two: one allocated (and grown) by the library, and one in the static
+// device array below, used only by mk_gemm_reduce_local_noalloc.
+struct Workspace {
     char *ws = nullptr;
     size_t ws_bytes = 0;
     uint32_t Tcap = 0, Chcap = 0;
@@ -70,20 +71,30 @@ struct DevState {
     uint32_t calls = 0;
     uint32_t shape_T = 0, shape_tpc = 0;
     bool dirty = false;
-    bool xcd_ok = false;   // workgroup w of a one-per-CU grid runs on XCD w mod 8
+    bool fixed = false;    // the static array: never freed, never grown
     Launch last;
+};
+
+struct DevState {
+    bool init = false;
+    int num_cu = 0;
+    uint64_t timer_hz = 100000000ull;
+    bool xcd_ok = false;   // workgroup w of a one-per-CU grid runs on XCD w mod 8
+    char *fixed_base = nullptr;   // this device's copy of `scratch` (hipGetSymbolAddress)
+    Workspace heap, fixed;
+    Workspace *recent = nullptr;  // the workspace of the last fused launch
 };
 DevState g_dev[kMaxDevices];
 
-size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Layout {
     size_t live, snap, trace, tile_flag, tile_cnt, chunk_cnt, chunk_flag, chunk_release, cowner, rowner,
         timeline, total;
 };
 
-Layout layout_for(uint32_t Tcap, uint32_t Chcap) {
-    Layout L;
+constexpr Layout layout_for(uint32_t Tcap, uint32_t Chcap) {
+    Layout L{};
     size_t o = 0;
     L.live = o; o += sizeof(Live);
     L.snap = o; o += sizeof(Live);
@@ -100,7 +111,19 @@ Layout layout_for(uint32_t Tcap, uint32_t Chcap) {
     return L;
 }
 
-WsView view_of(const DevState &d) {
+// The allocation-free entry point's workspace: a static device array, one
+// copy per device, kept until the process ends.  Capacity: 8192 tiles and
+// 8192 chunks (every workload here has at most 4096 tiles), about 0.4 MiB.
+// Host code never passes the array's name to a kernel or a copy (on the host
+// it is only a stand-in for the symbol): each device's copy is reached
+// through the address hipGetSymbolAddress returns for it (DevState::fixed_base).
+constexpr uint32_t kFixedTiles = 8192;
+constexpr uint32_t kFixedChunks = 8192;
+constexpr size_t kFixedBytes = layout_for(kFixedTiles, kFixedChunks).total;
+static_assert(kFixedBytes >= sizeof(uint32_t) * kMaxWG, "the XCD probe writes one word per workgroup");
+static __device__ __align__(256) char scratch[kFixedBytes];
+
+WsView view_of(const Workspace &d) {
     const Layout L = layout_for(d.Tcap, d.Chcap);
     WsView v;
     v.live = (Live *)(d.ws + L.live);
@@ -217,22 +240,20 @@ int current_device(int *dev) {
 
 // Whether workgroups are dealt to XCDs round-robin (workgroup w on XCD
 // w mod 8), read from each workgroup's XCC id register once per device.
-// Tiles are kept on one XCD only when this holds.
+// Tiles are kept on one XCD only when this holds.  The probe writes into the
+// device's static array (before any workspace lives there), so setting up a
+// device allocates nothing.
 int probe_xcd_mapping(DevState &d) {
     d.xcd_ok = false;
-    if (d.num_cu <= 0 || d.num_cu % kMaxXcd != 0) return MK_OK;
-    uint32_t *buf = nullptr;
-    hipError_t e = hipMalloc((void **)&buf, sizeof(uint32_t) * (size_t)d.num_cu);
-    if (e != hipSuccess) return hip_fail(e, "hipMalloc(xcd probe)");
-    std::vector<uint32_t> host((size_t)d.num_cu, 0xFFFFFFFFu);
-    e = launch_xcc_probe(buf, d.num_cu, nullptr);
+    if (d.num_cu <= 0 || d.num_cu % kMaxXcd != 0 || d.num_cu > kMaxWG) return MK_OK;
+    uint32_t *buf = (uint32_t *)d.fixed_base;
+    uint32_t host[kMaxWG];
+    hipError_t e = launch_xcc_probe(buf, d.num_cu, nullptr);
     if (e == hipSuccess) e = hipDeviceSynchronize();
-    if (e == hipSuccess) e = hipMemcpy(host.data(), buf, sizeof(uint32_t) * host.size(), hipMemcpyDeviceToHost);
-    const hipError_t ef = hipFree(buf);
+    if (e == hipSuccess) e = hipMemcpy(host, buf, sizeof(uint32_t) * (size_t)d.num_cu, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "xcd probe");
-    if (ef != hipSuccess) return hip_fail(ef, "hipFree(xcd probe)");
     bool ok = true;
-    for (int w = 0; w < d.num_cu; ++w) ok = ok && host[(size_t)w] == (uint32_t)(w % kMaxXcd);
+    for (int w = 0; w < d.num_cu; ++w) ok = ok && host[w] == (uint32_t)(w % kMaxXcd);
     d.xcd_ok = ok;
     return MK_OK;
 }
@@ -250,6 +271,12 @@ int device_state(DevState **out) {
         int khz = 0;
         if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0)
             d.timer_hz = (uint64_t)khz * 1000ull;
+        // this device's copy of the static array: its address, not the
+        // host-side symbol, is what kernels and copies are given
+        void *base = nullptr;
+        e = hipGetSymbolAddress(&base, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !base) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        d.fixed_base = (char *)base;
         rc = probe_xcd_mapping(d);
         if (rc) return rc;
         d.init = true;
@@ -258,9 +285,45 @@ int device_state(DevState **out) {
     return MK_OK;
 }
 
-// Make room for T tiles and Ch chunks.  A new workspace is zeroed (flags at
-// 0 never equal an epoch, which starts at 1) and its control blocks set.
-int ensure_workspace(DevState &d, uint32_t T, uint32_t Ch, hipStream_t s) {
+// Zero a workspace (flags at 0 never equal an epoch, which starts at 1), set
+// its control blocks and restart its bookkeeping.  Fill kernels, not
+// hipMemsetAsync, so the sequence stays valid inside a captured graph.
+int clear_workspace(Workspace &d, hipStream_t s) {
+    const Layout L = layout_for(d.Tcap, d.Chcap);
+    hipError_t e = launch_fill_u32((uint32_t *)d.ws, 0u, (int64_t)(L.total / 4), s);
+    if (e != hipSuccess) return hip_fail(e, "workspace clear launch");
+    WsView v = view_of(d);
+    e = launch_ws_init(v.live, v.snap, s);
+    if (e != hipSuccess) return hip_fail(e, "workspace init launch");
+    d.epoch = 0;
+    d.calls = 0;
+    d.shape_T = 0;
+    d.shape_tpc = 0;
+    d.dirty = false;
+    d.last.valid = false;
+    return MK_OK;
+}
+
+// The static workspace: its capacity is fixed, it is set up on its first
+// use, and a launch that needs more is refused.
+int ensure_fixed_workspace(DevState &dev, uint32_t T, uint32_t Ch, hipStream_t s) {
+    Workspace &d = dev.fixed;
+    if (T > kFixedTiles || Ch > kFixedChunks)
+        return fail(MK_ERR_SHAPE,
+                    "%u tiles / %u chunks exceed the allocation-free workspace (at most %u tiles and "
+                    "%u chunks); use mk_gemm_reduce_local", T, Ch, kFixedTiles, kFixedChunks);
+    if (d.ws) return MK_OK;
+    d.ws = dev.fixed_base;
+    d.fixed = true;
+    d.Tcap = kFixedTiles;
+    d.Chcap = kFixedChunks;
+    d.ws_bytes = layout_for(kFixedTiles, kFixedChunks).total;
+    return clear_workspace(d, s);
+}
+
+// Make room for T tiles and Ch chunks in the library's own workspace; a new
+// one is cleared.
+int ensure_workspace(Workspace &d, uint32_t T, uint32_t Ch, hipStream_t s) {
     if (d.ws && T <= d.Tcap && Ch <= d.Chcap) return MK_OK;
     uint32_t Tcap = d.Tcap, Chcap = d.Chcap;
     while (Tcap < T) Tcap = Tcap ? 2 * Tcap : 4096;
@@ -281,20 +344,7 @@ int ensure_workspace(DevState &d, uint32_t T, uint32_t Ch, hipStream_t s) {
     d.ws_bytes = L.total;
     d.Tcap = Tcap;
     d.Chcap = Chcap;
-    // a fill kernel rather than hipMemsetAsync, so the sequence stays valid
-    // inside a captured graph
-    e = launch_fill_u32((uint32_t *)d.ws, 0u, (int64_t)(L.total / 4), s);
-    if (e != hipSuccess) return hip_fail(e, "workspace clear launch");
-    WsView v = view_of(d);
-    e = launch_ws_init(v.live, v.snap, s);
-    if (e != hipSuccess) return hip_fail(e, "workspace init launch");
-    d.epoch = 0;
-    d.calls = 0;
-    d.shape_T = 0;
-    d.shape_tpc = 0;
-    d.dirty = false;
-    d.last.valid = false;
-    return MK_OK;
+    return clear_workspace(d, s);
 }
 
 // `rs`: one rank's share of GEMM+ReduceScatter (rank 0 of num_peers + 1):
@@ -302,8 +352,11 @@ int ensure_workspace(DevState &d, uint32_t T, uint32_t Ch, hipStream_t s) {
 // the GEMM stores every other tile row straight into `remote` (this rank's
 // inbox slots at the other owners) and leaves those rows of C untouched.
 // Otherwise GEMM+AllReduce.
+// `noalloc`: the fused launch uses the device's static workspace and the
+// call allocates nothing.
 int run(bool fused, bool rs, const void *A, const void *B, const float *peers, int num_peers, float *C,
-        float *remote, int64_t M, int64_t N, int64_t K, int tile_m, int tile_n, int tpc, void *stream) {
+        float *remote, int64_t M, int64_t N, int64_t K, int tile_m, int tile_n, int tpc, void *stream,
+        bool noalloc = false) {
     int rc = check_args(A, B, peers, num_peers, C, M, N, K, tile_m, tile_n, tpc);
     if (rc) return rc;
     if (!rs && remote) return fail(MK_ERR_INVALID_ARG, "remote is for reduce-scatter only");
@@ -324,7 +377,7 @@ int run(bool fused, bool rs, const void *A, const void *B, const float *peers, i
     DevState *dp = nullptr;
     rc = device_state(&dp);
     if (rc) return rc;
-    DevState &d = *dp;
+    DevState &dev = *dp;
     hipStream_t s = (hipStream_t)stream;
 
     const int tiles_m_all = (int)((M + tile_m - 1) / tile_m);
@@ -348,11 +401,11 @@ int run(bool fused, bool rs, const void *A, const void *B, const float *peers, i
         g.group_m = set.group_m;
         g.own_tile_rows = own_tile_rows;
         g.remote = own_tile_rows < tiles_m ? remote : nullptr;
-        g.nxcd = xcd_partitions(d.num_cu, d.num_cu);
+        g.nxcd = xcd_partitions(dev.num_cu, dev.num_cu);
         g.xcd_cols = g.nxcd == kMaxXcd
                          ? gemm_xcd_bands(g.nxcd, tiles_m, tiles_n, tile_m, tile_n, tpc, set.xcd_bands)
                          : 1;
-        hipError_t e = launch_gemm(tile_m, tile_n, g, d.num_cu, s);
+        hipError_t e = launch_gemm(tile_m, tile_n, g, dev.num_cu, s);
         if (e != hipSuccess) return hip_fail(e, "GEMM launch");
         if (num_peers > 0 && own_tile_rows > 0) {
             ReduceArgs r;
@@ -362,7 +415,7 @@ int run(bool fused, bool rs, const void *A, const void *B, const float *peers, i
             r.count4 = M * N / 4;
             r.own4 = std::min<int64_t>(M, (int64_t)own_tile_rows * tile_m) * N / 4;
             r.P = num_peers;
-            e = launch_reduce(r, d.num_cu, s);
+            e = launch_reduce(r, dev.num_cu, s);
             if (e != hipSuccess) return hip_fail(e, "reduce launch");
         }
         return MK_OK;
@@ -379,7 +432,7 @@ int run(bool fused, bool rs, const void *A, const void *B, const float *peers, i
     // every workgroup of the persistent grid must be resident at once
     const int per_cu = workgroups_per_cu(tile_m, tile_n);
     if (per_cu < 1) return fail(MK_ERR_HIP, "occupancy query for the fused kernel failed");
-    const int resident = d.num_cu * per_cu;
+    const int resident = dev.num_cu * per_cu;
     const int nwg = set.num_wg ? set.num_wg : (resident < kMaxWG ? resident : kMaxWG);
     if (nwg < 2 || nwg > resident)
         return fail(MK_ERR_INVALID_ARG, "workgroups %d outside [2, %d resident workgroups]", nwg,
@@ -393,10 +446,10 @@ int run(bool fused, bool rs, const void *A, const void *B, const float *peers, i
     // compute workgroup per XCD, and a static partition must give each XCD a
     // reducer and a compute workgroup (8 <= n_reduce <= B - 8).  Otherwise
     // tiles cross XCDs with write-through hand-off.
-    const int nxcd = xcd_partitions(nwg, d.num_cu);
+    const int nxcd = xcd_partitions(nwg, dev.num_cu);
     const int bands = nxcd == kMaxXcd ? xcd_bands(nxcd, tiles_m, tiles_n, tile_m, tile_n, tpc, set.xcd_bands)
                                       : 0;
-    const bool local = d.xcd_ok && nxcd == kMaxXcd && bands > 0 &&
+    const bool local = dev.xcd_ok && nxcd == kMaxXcd && bands > 0 &&
                        set.mode != MK_PART_STATIC_DETERMINISTIC &&
                        (set.mode == MK_PART_ADAPTIVE || (ns_init >= nxcd && ns_init <= nwg - nxcd));
     const int keep = local ? nxcd : 1;
@@ -415,8 +468,9 @@ int run(bool fused, bool rs, const void *A, const void *B, const float *peers, i
         if (ns_init < 1) ns_init = 1;
     }
 
-    rc = ensure_workspace(d, T, Ch, s);
+    rc = noalloc ? ensure_fixed_workspace(dev, T, Ch, s) : ensure_workspace(dev.heap, T, Ch, s);
     if (rc) return rc;
+    Workspace &d = noalloc ? dev.fixed : dev.heap;
     WsView v = view_of(d);
     hipError_t e;
     if (d.dirty) {
@@ -477,7 +531,7 @@ int run(bool fused, bool rs, const void *A, const void *B, const float *peers, i
     a.M_all = M;
     a.tiles_m_all = tiles_m_all;
     a.peer_mn = M * N;
-    a.timeout_ticks = set.timeout_us * (d.timer_hz / 1000000ull);
+    a.timeout_ticks = set.timeout_us * (dev.timer_hz / 1000000ull);
     a.skip_publish = set.skip_publish;
     a.help = set.help;
     a.ws = v;
@@ -486,6 +540,7 @@ int run(bool fused, bool rs, const void *A, const void *B, const float *peers, i
         d.dirty = true;
         return hip_fail(e, "fused launch");
     }
+    dev.recent = &d;
     d.last.valid = true;
     d.last.epoch = d.epoch;
     d.last.calls = d.calls;
@@ -515,6 +570,14 @@ int mk_gemm_reduce_local(const void *A, const void *B, const float *peers, int n
     std::lock_guard<std::mutex> lk(g_mu);
     return run(true, false, A, B, peers, num_peers, C, nullptr, M, N, K, tile_m, tile_n, tiles_per_chunk,
                stream);
+}
+
+int mk_gemm_reduce_local_noalloc(const void *A, const void *B, const float *peers, int num_peers, float *C,
+                                 int64_t M, int64_t N, int64_t K, int tile_m, int tile_n,
+                                 int tiles_per_chunk, void *stream) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    return run(true, false, A, B, peers, num_peers, C, nullptr, M, N, K, tile_m, tile_n, tiles_per_chunk,
+               stream, true);
 }
 
 int mk_gemm_reduce_unfused(const void *A, const void *B, const float *peers, int num_peers,
@@ -613,8 +676,10 @@ int mk_get_stats(mk_stats *out, uint32_t *maps, size_t maps_len) {
     DevState *dp = nullptr;
     int rc = device_state(&dp);
     if (rc) return rc;
-    DevState &d = *dp;
-    if (!d.last.valid || !d.ws) return fail(MK_ERR_INVALID_ARG, "no fused launch on this device yet");
+    DevState &dev = *dp;
+    if (!dev.recent || !dev.recent->last.valid || !dev.recent->ws)
+        return fail(MK_ERR_INVALID_ARG, "no fused launch on this device yet");
+    Workspace &d = *dev.recent;
     const Launch &l = d.last;
     const size_t need = 10ull * l.T + 3ull * l.Ch + 2ull * kTraceCap;
     if (maps && maps_len < need)
@@ -658,7 +723,7 @@ int mk_get_stats(mk_stats *out, uint32_t *maps, size_t maps_len) {
     out->kernel_ticks_end = snap.t_end;
     out->reduce_ticks_start = snap.r_start;
     out->reduce_ticks_end = snap.r_end;
-    out->timer_hz = d.timer_hz;
+    out->timer_hz = dev.timer_hz;
     out->xcd_local = l.local;
     out->keep_compute = l.keep;
     out->controller_cap = l.cap;
@@ -691,7 +756,7 @@ int mk_get_stats(mk_stats *out, uint32_t *maps, size_t maps_len) {
     if (sticky & kStickyXcd) {
         // a workgroup ran on another XCD than its index implies: the launch's
         // hand-off assumption failed, so tiles no longer stay on one XCD
-        d.xcd_ok = false;
+        dev.xcd_ok = false;
         out->status = MK_ERR_PROTOCOL;
         fail(MK_ERR_PROTOCOL, "a workgroup ran on an unexpected XCD; result not valid");
         return MK_ERR_PROTOCOL;
@@ -737,7 +802,7 @@ int mk_release_workspace(void) {
     int dev = 0;
     int rc = current_device(&dev);
     if (rc) return rc;
-    DevState &d = g_dev[dev];
+    Workspace &d = g_dev[dev].heap;
     if (d.ws) {
         hipError_t e = hipDeviceSynchronize();
         if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
@@ -748,10 +813,11 @@ int mk_release_workspace(void) {
     d.ws_bytes = 0;
     d.Tcap = d.Chcap = 0;
     d.last.valid = false;
+    if (g_dev[dev].recent == &d) g_dev[dev].recent = nullptr;
     return MK_OK;
 }
 
-const char *mk_last_error(void) { return g_last_error.c_str(); }
+const char *mk_last_error(void) { return g_last_error; }
 
 int mk_abi_version(void) { return MK_ABI_VERSION; }
 

@@ -114,6 +114,26 @@ int mk_gemm_reduce_local(const void *A, const void *B, const float *peers, int n
                          int tile_m, int tile_n, int tiles_per_chunk, void *stream);
 
 /*
+ * mk_gemm_reduce_local_noalloc -- mk_gemm_reduce_local for callers that
+ * cannot allocate device memory: code being captured into a HIP graph, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments, result,
+ * kernels, partition settings and statistics (mk_get_stats reports whichever
+ * of the two entry points launched last).  The call allocates nothing (no
+ * hipMalloc, hipFree, or allocating library routine): its flags, counters,
+ * maps and control block live in a static device array of about 0.4 MiB,
+ * one copy per device, held until the process ends and shared by every call
+ * of this entry point on that device (it keeps the last call's contents; per
+ * call state starts from epoch-valued flags and counters the call itself
+ * clears when the tile grid changes).  Calls that overlap in time on one
+ * device race on that array: serialize them (one stream, or events).
+ * Limits: at most 8192 output tiles and 8192 chunks; larger grids fail with
+ * MK_ERR_SHAPE before any launch (use mk_gemm_reduce_local).
+ */
+int mk_gemm_reduce_local_noalloc(const void *A, const void *B, const float *peers, int num_peers,
+                                 float *C, int64_t M, int64_t N, int64_t K,
+                                 int tile_m, int tile_n, int tiles_per_chunk, void *stream);
+
+/*
  * mk_gemm_reduce_unfused -- the unfused two-kernel baseline with the same
  * arguments and result: a GEMM kernel writes the fp32 partial into C, then a
  * separate reduce kernel adds the peers (the host-driven, kernel-granular
