@@ -468,3 +468,146 @@ def check_state(maps: Dict[str, np.ndarray], T: int, tiles_per_chunk: int, epoch
         if np.any(ro_ns != n_reduce):
             bad.append("static partition changed during the launch (reduce side)")
     return bad
+
+
+# ---------------------------------------------------------------------------
+# AllGather+GEMM, one rank's share
+# ---------------------------------------------------------------------------
+#
+# AllGather + GEMM row of the MarkTechPost page's five-kernel table: every
+# rank holds a shard of A; while the shards of the other ranks are gathered,
+# the local GEMM consumes A's tiles as they arrive.  "【学习】mKernel 分析"
+# section 2.6, Table 3: the dependency runs from communication to compute,
+# the transfer unit is 128 rows, input shards are submitted at launch, and
+# compute tiles are taken in order of input availability (local first);
+# section 2.4: when communication feeds compute, a compute block waiting for
+# its input helps communication.
+#
+# The readings used (the pages fix no layout):
+# - R = P + 1 ranks, this rank is rank 0; every shard has Ms rows, and the
+#   gathered A stacks the shards by rank: rank r's rows are
+#   [r Ms, (r + 1) Ms).  The result is C = A_gathered . B over all R Ms rows
+#   (a column-parallel layer whose input is sequence-sharded), and the
+#   gathered A itself, which every rank holds after an AllGather.
+# - A chunk is one tile row of A: tile_m rows (128 on the pages), K columns.
+# - Copy order: the other ranks' chunks first, by rank and row (they gate
+#   compute), then this rank's own (nothing waits for them: the local rows
+#   are computed from the local shard directly).  Compute order: local tile
+#   rows first, then the other ranks' rows in the order they are copied,
+#   which is plain row order; blocks left to right inside a tile row.
+
+
+def allgather_gemm(a_local_bits: np.ndarray, a_peers_bits: np.ndarray,
+                   b_bits: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Rank 0's share of AllGather+GEMM.
+
+    a_local_bits [Ms, K] (uint16 bfloat16 patterns), a_peers_bits [P, Ms, K]
+    (the other ranks' shards, rank 1 first), b_bits [K, N].  Returns
+    (gathered, C): gathered [R Ms, K] uint16 is the shards stacked by rank,
+    C [R Ms, N] float64 is gathered . B on the exact bfloat16 values."""
+    a0 = np.asarray(a_local_bits, dtype=np.uint16)
+    ap = np.asarray(a_peers_bits, dtype=np.uint16)
+    b = np.asarray(b_bits, dtype=np.uint16)
+    if a0.ndim != 2 or ap.ndim != 3 or b.ndim != 2:
+        raise ValueError("A_local [Ms,K], A_peers [P,Ms,K], B [K,N]")
+    if ap.shape[0] and ap.shape[1:] != a0.shape:
+        raise ValueError("every shard must have the local shard's shape")
+    if a0.shape[1] != b.shape[0]:
+        raise ValueError("A's columns must match B's rows")
+    gathered = np.concatenate([a0] + [ap[p] for p in range(ap.shape[0])], axis=0)
+    return gathered, gemm_part(gathered, b)
+
+
+def ag_copy_order(ranks: int, chunks_per_shard: int) -> np.ndarray:
+    """Chunk ids (tile rows of the gathered A) in copy-claim order: the other
+    ranks' chunks by rank and row, then this rank's own."""
+    if ranks < 1 or chunks_per_shard < 0:
+        raise ValueError("ranks >= 1, chunks_per_shard >= 0")
+    peers = np.arange(chunks_per_shard, ranks * chunks_per_shard, dtype=np.int64)
+    local = np.arange(0, chunks_per_shard, dtype=np.int64)
+    return np.concatenate([peers, local])
+
+
+def ag_expected_state(n_chunks: int, n_tiles: int, epoch: int, calls: int) -> Dict[str, np.ndarray]:
+    """Integer state after `calls` complete launches of one shape: every
+    chunk's arrival flag holds the last epoch, every chunk was copied and
+    every tile computed exactly once per call."""
+    return {
+        "chunk_flag": np.full(n_chunks, epoch, dtype=np.int64),
+        "chunk_copy_cnt": np.full(n_chunks, calls, dtype=np.int64),
+        "tile_compute_cnt": np.full(n_tiles, calls, dtype=np.int64),
+    }
+
+
+def ag_deterministic_owners(ranks: int, chunks_per_shard: int, tiles_n: int, B: int, n_copy: int,
+                            tiles_per_task: int = 1) -> Tuple[np.ndarray, np.ndarray]:
+    """Owner maps of the deterministic static schedule: workgroups
+    [0, n_copy) copy, the others compute.  Copy task i (in copy order) goes
+    to workgroup i mod n_copy; compute task j (blocks of `tiles_per_task`
+    adjacent tiles, row by row) to n_copy + j mod (B - n_copy).  Returns
+    (copy owner per chunk id, compute owner per tile)."""
+    order = ag_copy_order(ranks, chunks_per_shard)
+    copy_owner = np.zeros(order.shape[0], dtype=np.int64)
+    copy_owner[order] = np.arange(order.shape[0]) % n_copy
+    T = ranks * chunks_per_shard * tiles_n
+    task = compute_task_of_tile(T, tiles_n, tiles_per_task)
+    return copy_owner, n_copy + task % (B - n_copy)
+
+
+def ag_check_state(maps: Dict[str, np.ndarray], ranks: int, chunks_per_shard: int, tiles_n: int,
+                   epoch: int, calls: int, B: int, mode: str, n_copy: int,
+                   tiles_per_task: int = 1) -> List[str]:
+    """Compare an AllGather+GEMM launch's protocol state with its closed form.
+
+    Owner words are (mark << 31) | (copy target seen << 16) | workgroup.  A
+    copy task by a workgroup at or above the copy target is legal only with
+    the mark (a compute-role workgroup waiting for its input helped copy),
+    and only in adaptive mode; a compute task needs an index at or above the
+    target and never carries the mark."""
+    bad: List[str] = []
+    n_chunks = ranks * chunks_per_shard
+    T = n_chunks * tiles_n
+    for key, want in ag_expected_state(n_chunks, T, epoch, calls).items():
+        got = np.asarray(maps[key], dtype=np.int64)
+        if got.shape != want.shape:
+            bad.append(f"{key}: shape {got.shape} != {want.shape}")
+            continue
+        idx = np.nonzero(got != want)[0]
+        if idx.size:
+            i = int(idx[0])
+            bad.append(f"{key}[{i}] = {int(got[i])}, expected {int(want[i])} ({idx.size} mismatches)")
+    co = np.asarray(maps["copy_owner"], dtype=np.int64)
+    po = np.asarray(maps["compute_owner"], dtype=np.int64)
+    co_wg, co_ns, co_help = co & OWNER_WG_MASK, (co >> 16) & OWNER_NS_MASK, (co & OWNER_HELP) != 0
+    po_wg, po_ns, po_mark = po & OWNER_WG_MASK, (po >> 16) & OWNER_NS_MASK, (po & OWNER_HELP) != 0
+    if np.any(co_wg >= B) or np.any(po_wg >= B):
+        bad.append("owner outside [0, B)")
+    if mode == "deterministic":
+        dc, dp = ag_deterministic_owners(ranks, chunks_per_shard, tiles_n, B, n_copy, tiles_per_task)
+        if not np.array_equal(co_wg, dc):
+            i = int(np.nonzero(co_wg != dc)[0][0])
+            bad.append(f"copy_owner[{i}] = {int(co_wg[i])}, expected {int(dc[i])}")
+        if not np.array_equal(po_wg, dp):
+            i = int(np.nonzero(po_wg != dp)[0][0])
+            bad.append(f"compute_owner[{i}] = {int(po_wg[i])}, expected {int(dp[i])}")
+    if tiles_per_task > 1 and T:
+        task = compute_task_of_tile(T, tiles_n, tiles_per_task)
+        first = np.zeros(int(task.max()) + 1, dtype=np.int64)
+        first[task[::-1]] = po[::-1]
+        if np.any(po != first[task]):
+            i = int(np.nonzero(po != first[task])[0][0])
+            bad.append(f"tile {i}: compute owner differs from the rest of its task")
+    if np.any(po_mark):
+        bad.append(f"tile {int(np.nonzero(po_mark)[0][0])}: compute owner carries the help mark")
+    if mode != "adaptive" and np.any(co_help):
+        bad.append(f"chunk {int(np.nonzero(co_help)[0][0])}: help copy outside adaptive mode")
+    if np.any((co_wg >= co_ns) & ~co_help):
+        i = int(np.nonzero((co_wg >= co_ns) & ~co_help)[0][0])
+        bad.append(f"chunk {i} copied by workgroup {int(co_wg[i])} while the copy target was {int(co_ns[i])}")
+    if np.any(po_wg < po_ns):
+        i = int(np.nonzero(po_wg < po_ns)[0][0])
+        bad.append(f"tile {i} computed by workgroup {int(po_wg[i])} while the copy target was {int(po_ns[i])}")
+    if mode in ("static", "deterministic"):
+        if np.any(co_ns != n_copy) or np.any(po_ns != n_copy):
+            bad.append("static partition changed during the launch")
+    return bad

@@ -187,3 +187,45 @@ def make_remote(w: Workload, seed: int = DEFAULT_SEED) -> np.ndarray:
     for the other ranks' outputs in GEMM+ReduceScatter (the peers'
     distribution, a stream of its own after every peer's)."""
     return _draw(_rng(seed, w.wid, 2 + w.peers), (w.M, w.N), w.dist_peer)
+
+
+# ---------------------------------------------------------------------------
+# AllGather+GEMM, one rank's share
+# ---------------------------------------------------------------------------
+# Each of R = peers + 1 ranks holds a shard of Ms = M rows of A ([Ms, K]); this
+# rank's own shard is buffer 0, B [K, N] is buffer 1, the other ranks' shards
+# are buffers 2 + p (all from dist_ab, rounded to bfloat16).  The pages give
+# no shapes for this kernel; the workloads below take the GEMM+AllReduce
+# workloads' token and hidden sizes as a sequence-sharded input gathered for a
+# column-parallel layer (M tokens in total, R Ms = M).
+
+AG_WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("ag_tiny", 10, 64, 256, 256, 3, ("uniform", -1.0, 1.0), ("zeros",),
+                 64, 64, 1, "static", 2,
+                 description="4 ranks x 64 rows, K 256, N 256, 64x64 tiles (64-row chunks)"),
+        Workload("ag_tp_share", 11, 512, 1792, 4096, 7, ("normal", 0.02), ("zeros",),
+                 128, 128, 1, "adaptive", 0,
+                 description="8 ranks x 512 tokens (4096), hidden 4096, N_local 1792, 128-row chunks"),
+        Workload("ag_compute_heavy", 12, 2048, 8192, 8192, 7, ("normal", 0.01), ("zeros",),
+                 256, 128, 1, "adaptive", 0,
+                 description="8 ranks x 2048 tokens (16384), K 8192, N 8192, 256-row chunks"),
+    ]
+}
+
+
+def ag_workload(name: str) -> Workload:
+    return AG_WORKLOADS[name]
+
+
+def make_ag_inputs(w: Workload, seed: int = DEFAULT_SEED):
+    """Draw (A_local [Ms,K] uint16, A_peers [P,Ms,K] uint16, B [K,N] uint16)
+    for one rank's share of AllGather+GEMM (w.M is the shard's rows)."""
+    Ms, N, K, P = w.M, w.N, w.K, w.peers
+    a_local = round_to_bf16_bits(_draw(_rng(seed, w.wid, 0), (Ms, K), w.dist_ab))
+    b = round_to_bf16_bits(_draw(_rng(seed, w.wid, 1), (K, N), w.dist_ab))
+    a_peers = np.empty((P, Ms, K), dtype=np.uint16)
+    for p in range(P):
+        a_peers[p] = round_to_bf16_bits(_draw(_rng(seed, w.wid, 2 + p), (Ms, K), w.dist_ab))
+    return a_local, a_peers, b
