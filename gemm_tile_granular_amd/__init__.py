@@ -79,6 +79,7 @@ class Stats(ctypes.Structure):
         ("xcd_bands", ctypes.c_uint32),
         ("adaptive_help", ctypes.c_uint32),
         ("sticky_errors", ctypes.c_uint32),
+        ("kind", ctypes.c_uint32),
     ]
 
 
@@ -93,6 +94,8 @@ SIGNATURES = {
                                              _vp]),
     "mk_gemm_reduce_scatter_unfused": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32,
                                                _vp]),
+    "mk_allgather_gemm_local": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp]),
+    "mk_allgather_gemm_unfused": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp]),
     "mk_set_partition": (_i32, [_i32, _i32]),
     "mk_set_controller_floor": (_i32, [_i32]),
     "mk_set_controller_cap": (_i32, [_i32]),
@@ -216,6 +219,41 @@ def gemm_reduce_scatter_unfused(A, B, peers, C, remote, tile_m: int, tile_n: int
     """Same result from two launches (mk_gemm_reduce_scatter_unfused)."""
     _call_rs(lib.mk_gemm_reduce_scatter_unfused, A, B, peers, C, remote, tile_m, tile_n, tiles_per_chunk,
              stream)
+
+
+def _call_ag(fn, A_local, A_peers, A_gathered, B, C, tile_m, tile_n, stream):
+    torch = _torch()
+    for name, t, dt in (("A_local", A_local, torch.bfloat16), ("A_gathered", A_gathered, torch.bfloat16),
+                        ("B", B, torch.bfloat16), ("C", C, torch.float32)):
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous() or t.dim() != 2:
+            raise ValueError(f"{name} must be a contiguous 2-D {dt} CUDA tensor")
+    Ms, K = A_local.shape
+    K2, N = B.shape
+    P = 0
+    if A_peers is not None:
+        if (A_peers.dtype != torch.bfloat16 or not A_peers.is_cuda or not A_peers.is_contiguous()
+                or A_peers.dim() != 3 or tuple(A_peers.shape[1:]) != (Ms, K)):
+            raise ValueError("A_peers must be a contiguous [P, Ms, K] bfloat16 CUDA tensor")
+        P = A_peers.shape[0]
+    M = (P + 1) * Ms
+    if K2 != K or tuple(A_gathered.shape) != (M, K) or tuple(C.shape) != (M, N):
+        raise ValueError("shape mismatch: A_local [Ms,K], A_peers [P,Ms,K], A_gathered [(P+1)Ms,K], "
+                         "B [K,N], C [(P+1)Ms,N]")
+    pp = A_peers.data_ptr() if (A_peers is not None and P > 0) else None
+    _check(fn(A_local.data_ptr(), pp, P, A_gathered.data_ptr(), B.data_ptr(), C.data_ptr(), Ms, N, K,
+              tile_m, tile_n, _stream_handle(stream)))
+
+
+def allgather_gemm_local(A_local, A_peers, A_gathered, B, C, tile_m: int, tile_n: int, stream=None) -> None:
+    """Rank 0's share of AllGather+GEMM in one persistent launch
+    (mk_allgather_gemm_local): A_gathered = the shards stacked by rank,
+    C = A_gathered . B."""
+    _call_ag(lib.mk_allgather_gemm_local, A_local, A_peers, A_gathered, B, C, tile_m, tile_n, stream)
+
+
+def allgather_gemm_unfused(A_local, A_peers, A_gathered, B, C, tile_m: int, tile_n: int, stream=None) -> None:
+    """The same from two launches: gather, then GEMM (mk_allgather_gemm_unfused)."""
+    _call_ag(lib.mk_allgather_gemm_unfused, A_local, A_peers, A_gathered, B, C, tile_m, tile_n, stream)
 
 
 def set_partition(mode, n_reduce: int = 0) -> None:

@@ -54,6 +54,7 @@ constexpr int kMaxDevices = 64;
 
 struct Launch {
     bool valid = false;
+    uint32_t kind = 0;   // 0 GEMM+AllReduce, 1 GEMM+ReduceScatter, 2 AllGather+GEMM
     uint32_t epoch = 0, calls = 0, nwg = 0, T = 0, Ch = 0, tpc = 0, tm = 0, tn = 0;
     uint32_t mode = 0, ns_init = 0;
     uint32_t local = 0, keep = 1, cap = 0, bands = 1, help = 1;
@@ -347,6 +348,42 @@ int ensure_workspace(Workspace &d, uint32_t T, uint32_t Ch, hipStream_t s) {
     return clear_workspace(d, s);
 }
 
+// Per-launch bookkeeping of a workspace: a clean control block after an
+// early-ended launch, per-call counters cleared when the shape changes (`key`
+// tells the launch kinds and chunk sizes apart: counters of one kind mean
+// nothing to another), flags cleared before the epoch wraps; then the
+// launch's epoch and call number.
+int prepare_launch(Workspace &d, uint32_t T, uint32_t key, hipStream_t s) {
+    WsView v = view_of(d);
+    hipError_t e;
+    if (d.dirty) {
+        // a launch ended early: control block and counters are not trustworthy
+        e = launch_ws_init(v.live, v.snap, s);
+        if (e != hipSuccess) return hip_fail(e, "workspace reinit launch");
+        d.shape_T = 0;
+        d.dirty = false;
+    }
+    if (T != d.shape_T || key != d.shape_tpc) {
+        // new shape: per-call counters restart from zero (flags are epoch
+        // valued and need no clearing)
+        e = launch_fill_u32(v.tile_cnt, 0, d.Tcap, s);
+        if (e == hipSuccess) e = launch_fill_u32(v.chunk_cnt, 0, d.Chcap, s);
+        if (e != hipSuccess) return hip_fail(e, "counter clear launch");
+        d.calls = 0;
+        d.shape_T = T;
+        d.shape_tpc = key;
+    }
+    if (d.epoch == 0xFFFFFFFFu) {
+        e = launch_fill_u32(v.tile_flag, 0, d.Tcap, s);
+        if (e == hipSuccess) e = launch_fill_u32(v.chunk_flag, 0, d.Chcap, s);
+        if (e != hipSuccess) return hip_fail(e, "flag clear launch");
+        d.epoch = 0;
+    }
+    d.epoch += 1;
+    d.calls += 1;
+    return MK_OK;
+}
+
 // `rs`: one rank's share of GEMM+ReduceScatter (rank 0 of num_peers + 1):
 // tile rows [0, floor(tiles_m / R)) are computed into C and reduced there;
 // the GEMM stores every other tile row straight into `remote` (this rank's
@@ -471,33 +508,10 @@ int run(bool fused, bool rs, const void *A, const void *B, const float *peers, i
     rc = noalloc ? ensure_fixed_workspace(dev, T, Ch, s) : ensure_workspace(dev.heap, T, Ch, s);
     if (rc) return rc;
     Workspace &d = noalloc ? dev.fixed : dev.heap;
+    rc = prepare_launch(d, T, (uint32_t)tpc, s);
+    if (rc) return rc;
     WsView v = view_of(d);
     hipError_t e;
-    if (d.dirty) {
-        // a launch ended early: control block and counters are not trustworthy
-        e = launch_ws_init(v.live, v.snap, s);
-        if (e != hipSuccess) return hip_fail(e, "workspace reinit launch");
-        d.shape_T = 0;
-        d.dirty = false;
-    }
-    if (T != d.shape_T || (uint32_t)tpc != d.shape_tpc) {
-        // new shape: per-call counters restart from zero (flags are epoch
-        // valued and need no clearing)
-        e = launch_fill_u32(v.tile_cnt, 0, d.Tcap, s);
-        if (e == hipSuccess) e = launch_fill_u32(v.chunk_cnt, 0, d.Chcap, s);
-        if (e != hipSuccess) return hip_fail(e, "counter clear launch");
-        d.calls = 0;
-        d.shape_T = T;
-        d.shape_tpc = (uint32_t)tpc;
-    }
-    if (d.epoch == 0xFFFFFFFFu) {
-        e = launch_fill_u32(v.tile_flag, 0, d.Tcap, s);
-        if (e == hipSuccess) e = launch_fill_u32(v.chunk_flag, 0, d.Chcap, s);
-        if (e != hipSuccess) return hip_fail(e, "flag clear launch");
-        d.epoch = 0;
-    }
-    d.epoch += 1;
-    d.calls += 1;
 
     FusedArgs a;
     std::memset(&a, 0, sizeof a);
@@ -542,6 +556,7 @@ int run(bool fused, bool rs, const void *A, const void *B, const float *peers, i
     }
     dev.recent = &d;
     d.last.valid = true;
+    d.last.kind = rs ? 1u : 0u;
     d.last.epoch = d.epoch;
     d.last.calls = d.calls;
     d.last.nwg = (uint32_t)nwg;
@@ -560,9 +575,171 @@ int run(bool fused, bool rs, const void *A, const void *B, const float *peers, i
     return MK_OK;
 }
 
+// One rank's share of AllGather+GEMM (fused: one persistent launch; else the
+// gather kernel, then the GEMM kernel on the gathered A).
+int run_allgather(bool fused, const void *A_local, const void *A_peers, int num_peers, void *A_gath,
+                  const void *B, float *C, int64_t Ms, int64_t N, int64_t K, int tile_m, int tile_n,
+                  void *stream) {
+    if (Ms < 0 || N < 0 || K < 0) return fail(MK_ERR_INVALID_ARG, "negative dimension");
+    if (num_peers < 0) return fail(MK_ERR_INVALID_ARG, "num_peers < 0");
+    if (!tile_supported(tile_m, tile_n))
+        return fail(MK_ERR_INVALID_ARG, "tile %dx%d not supported (64x64, 128x128, 256x128)", tile_m, tile_n);
+    if (N % 8 != 0 || K % 8 != 0)
+        return fail(MK_ERR_SHAPE, "N (%lld) and K (%lld) must be multiples of 8", (long long)N, (long long)K);
+    if (Ms % tile_m != 0)
+        return fail(MK_ERR_SHAPE, "shard rows (%lld) must be a multiple of tile_m (%d): a chunk is one tile row",
+                    (long long)Ms, tile_m);
+    const int64_t R = (int64_t)num_peers + 1;
+    const int64_t M = R * Ms;
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(MK_ERR_SHAPE, "dimension exceeds 2^31-1");
+    if (M == 0 || N == 0) return MK_OK;
+    if ((int64_t)tile_m * N * 4 >= (int64_t)INT32_MAX || (int64_t)tile_m * K * 2 >= (int64_t)INT32_MAX ||
+        (int64_t)64 * N * 2 >= (int64_t)INT32_MAX)
+        return fail(MK_ERR_SHAPE, "N or K too large for 32-bit in-tile offsets");
+    const int64_t tiles_n = (N + tile_n - 1) / tile_n;
+    const int64_t T = (M / tile_m) * tiles_n;
+    if (T >= (int64_t)kMaxTiles) return fail(MK_ERR_SHAPE, "too many tiles (%lld)", (long long)T);
+    if (!C || !A_gath || !B || !A_local) return fail(MK_ERR_INVALID_ARG, "NULL pointer");
+    if (num_peers > 0 && !A_peers) return fail(MK_ERR_INVALID_ARG, "A_peers is NULL with num_peers > 0");
+    if (!aligned16(C) || !aligned16(A_gath) || !aligned16(B) || !aligned16(A_local) ||
+        (A_peers && !aligned16(A_peers)))
+        return fail(MK_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+    const int64_t gb = M * K * 2, cb = M * N * 4, lb = Ms * K * 2, pb = (int64_t)num_peers * Ms * K * 2;
+    if (overlaps(A_gath, gb, A_local, lb) || overlaps(A_gath, gb, A_peers, pb) || overlaps(A_gath, gb, B, K * N * 2) ||
+        overlaps(A_gath, gb, C, cb) || overlaps(C, cb, A_local, lb) || overlaps(C, cb, A_peers, pb) ||
+        overlaps(C, cb, B, K * N * 2))
+        return fail(MK_ERR_INVALID_ARG, "outputs (gathered A, C) overlap each other or an input");
+    const Settings set = g_set;
+    DevState *dp = nullptr;
+    int rc = device_state(&dp);
+    if (rc) return rc;
+    DevState &dev = *dp;
+    hipStream_t s = (hipStream_t)stream;
+    const int tpb = tiles_per_block(tile_m, tile_n);
+
+    AgArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.A_local = (const uint16_t *)A_local;
+    a.A_peers = (const uint16_t *)A_peers;
+    a.A_gath = (uint16_t *)A_gath;
+    a.B = (const uint16_t *)B;
+    a.C = C;
+    a.Ms = Ms;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.P = num_peers;
+    a.cps = (uint32_t)(Ms / tile_m);
+    a.Ch = (uint32_t)(M / tile_m);
+    a.tiles_n = (uint32_t)tiles_n;
+    a.bn = (uint32_t)((tiles_n + tpb - 1) / tpb);
+    a.T = (uint32_t)T;
+    a.TB = a.Ch * a.bn;
+
+    if (!fused) {
+        hipError_t e = launch_gather(a, dev.num_cu, s);
+        if (e != hipSuccess) return hip_fail(e, "gather launch");
+        GemmArgs g;
+        std::memset(&g, 0, sizeof g);
+        g.A = (const uint16_t *)A_gath;
+        g.B = (const uint16_t *)B;
+        g.C = C;
+        g.M = M;
+        g.N = N;
+        g.K = K;
+        g.tiles_m = (int32_t)(M / tile_m);
+        g.tiles_n = (int32_t)tiles_n;
+        g.tpc = 4;
+        g.group_m = set.group_m;
+        g.own_tile_rows = g.tiles_m;
+        g.remote = nullptr;
+        g.nxcd = xcd_partitions(dev.num_cu, dev.num_cu);
+        g.xcd_cols = g.nxcd == kMaxXcd
+                         ? gemm_xcd_bands(g.nxcd, g.tiles_m, g.tiles_n, tile_m, tile_n, 4, set.xcd_bands)
+                         : 1;
+        e = launch_gemm(tile_m, tile_n, g, dev.num_cu, s);
+        if (e != hipSuccess) return hip_fail(e, "GEMM launch");
+        return MK_OK;
+    }
+
+    const int per_cu = allgather_workgroups_per_cu(tile_m, tile_n);
+    if (per_cu < 1) return fail(MK_ERR_HIP, "occupancy query for the AllGather+GEMM kernel failed");
+    const int resident = dev.num_cu * per_cu;
+    const int nwg = set.num_wg ? set.num_wg : (resident < kMaxWG ? resident : kMaxWG);
+    if (nwg < 2 || nwg > resident)
+        return fail(MK_ERR_INVALID_ARG, "workgroups %d outside [2, %d resident workgroups]", nwg, resident);
+    int ns_init = set.n_reduce;
+    if (set.mode != MK_PART_ADAPTIVE && (ns_init < 1 || ns_init > nwg - 1))
+        return fail(MK_ERR_INVALID_ARG, "static copy count %d outside [1, %d]", ns_init, nwg - 1);
+    int cap = set.cap ? set.cap : nwg - 1;
+    if (cap > nwg - 1) cap = nwg - 1;
+    if (cap < 1) cap = 1;
+    if (set.mode == MK_PART_ADAPTIVE) {
+        // default start: the controller's floor; compute workgroups whose
+        // input has not arrived copy meanwhile, so a low start idles nobody
+        if (ns_init == 0) ns_init = set.floor;
+        if (ns_init > cap) ns_init = cap;
+        if (ns_init < 1) ns_init = 1;
+    }
+    rc = ensure_workspace(dev.heap, a.T, a.Ch, s);
+    if (rc) return rc;
+    Workspace &d = dev.heap;
+    rc = prepare_launch(d, a.T, 0x80000000u | a.Ch, s);
+    if (rc) return rc;
+    a.Tcap = d.Tcap;
+    a.epoch = d.epoch;
+    a.calls = d.calls;
+    a.mode = set.mode;
+    a.ns_init = ns_init;
+    a.ns_floor = set.floor;
+    a.ns_cap = cap;
+    a.nwg = nwg;
+    a.help = set.help;
+    a.timeout_ticks = set.timeout_us * (dev.timer_hz / 1000000ull);
+    a.skip_publish = set.skip_publish;
+    a.ws = view_of(d);
+    hipError_t e = launch_allgather_gemm(tile_m, tile_n, a, s);
+    if (e != hipSuccess) {
+        d.dirty = true;
+        return hip_fail(e, "AllGather+GEMM launch");
+    }
+    dev.recent = &d;
+    d.last = Launch();
+    d.last.valid = true;
+    d.last.kind = 2;
+    d.last.epoch = d.epoch;
+    d.last.calls = d.calls;
+    d.last.nwg = (uint32_t)nwg;
+    d.last.T = a.T;
+    d.last.Ch = a.Ch;
+    d.last.tpc = 0;
+    d.last.tm = (uint32_t)tile_m;
+    d.last.tn = (uint32_t)tile_n;
+    d.last.mode = (uint32_t)set.mode;
+    d.last.ns_init = (uint32_t)ns_init;
+    d.last.cap = (uint32_t)cap;
+    d.last.help = (uint32_t)set.help;
+    return MK_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int mk_allgather_gemm_local(const void *A_local, const void *A_peers, int num_peers, void *A_gathered,
+                            const void *B, float *C, int64_t Ms, int64_t N, int64_t K, int tile_m, int tile_n,
+                            void *stream) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    return run_allgather(true, A_local, A_peers, num_peers, A_gathered, B, C, Ms, N, K, tile_m, tile_n, stream);
+}
+
+int mk_allgather_gemm_unfused(const void *A_local, const void *A_peers, int num_peers, void *A_gathered,
+                              const void *B, float *C, int64_t Ms, int64_t N, int64_t K, int tile_m, int tile_n,
+                              void *stream) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    return run_allgather(false, A_local, A_peers, num_peers, A_gathered, B, C, Ms, N, K, tile_m, tile_n, stream);
+}
+
 
 int mk_gemm_reduce_local(const void *A, const void *B, const float *peers, int num_peers, float *C,
                          int64_t M, int64_t N, int64_t K, int tile_m, int tile_n,
@@ -728,6 +905,7 @@ int mk_get_stats(mk_stats *out, uint32_t *maps, size_t maps_len) {
     out->keep_compute = l.keep;
     out->controller_cap = l.cap;
     out->xcd_bands = l.bands;
+    out->kind = l.kind;
     out->adaptive_help = l.help;
     out->sticky_errors = snap.sticky;
 

@@ -183,6 +183,65 @@ int mk_gemm_reduce_scatter_unfused(const void *A, const void *B, const float *pe
                                    int tile_m, int tile_n, int tiles_per_chunk, void *stream);
 
 /*
+ * mk_allgather_gemm_local -- one rank's share of AllGather+GEMM in one
+ * persistent launch (AllGather + GEMM row of the MarkTechPost page's
+ * five-kernel table: every rank holds a shard of A; while the shards are
+ * gathered, the local GEMM consumes tiles as they arrive.  "【学习】mKernel
+ * 分析" section 2.6, Table 3: communication feeds compute, 128-row chunks,
+ * shards submitted at launch, tiles in order of input availability, local
+ * first; section 2.4: the same controller sets the communication-role size,
+ * and a compute block waiting for its input helps communication).  This
+ * rank is rank 0 of R = num_peers + 1; after the call
+ *     A_gathered[r*Ms + i][k] = (r == 0 ? A_local[i][k] : A_peers[r-1][i][k])
+ *     C[i][j] = sum_k A_gathered[i][k] * B[k][j]        for i < R*Ms.
+ * Workgroups take a copy role (one chunk: tile_m rows of a shard into
+ * A_gathered, written through, then the chunk's arrival flag) or a compute
+ * role (one block of adjacent tiles of one tile row, taken once its chunk
+ * has arrived; this rank's own rows read A_local directly).  Copy claims take
+ * the other ranks' chunks first (rank, then row), this rank's own last;
+ * compute claims go in row order, so local rows come first.
+ *
+ *   A_local    bfloat16 [Ms, K], row-major (device, read only).
+ *   A_peers    bfloat16 [num_peers, Ms, K], contiguous, rank 1 first (device,
+ *              read only; stands in for the other ranks' shards); NULL only
+ *              when num_peers == 0.
+ *   A_gathered bfloat16 [R*Ms, K] (device, written).
+ *   B          bfloat16 [K, N] (device, read only).
+ *   C          fp32 [R*Ms, N] (device, written).
+ *   Ms         rows per shard; a multiple of tile_m (a chunk is one tile row).
+ *   N, K       multiples of 8.
+ *   tile_m, tile_n   64x64, 128x128 or 256x128.
+ * Pointers 16-byte aligned; A_gathered and C must not overlap each other or
+ * any input (MK_ERR_INVALID_ARG).  Partition (mk_set_partition): the count is
+ * the copy role's; adaptive starts at the controller floor unless set (0),
+ * and its cap is B - 1 unless mk_set_controller_cap sets one; static copiers
+ * leave once every chunk is claimed; the deterministic schedule deals copy
+ * tasks (in copy order) round-robin to workgroups [0, n) and compute blocks
+ * (row-major) to [n, B).  mk_set_adaptive_help(0) makes a waiting compute
+ * workgroup wait instead of copying.  mk_get_stats reports kind 2, with
+ * num_chunks = R*Ms/tile_m chunks, compute_tasks = tiles computed,
+ * reduce_tasks = chunks_released = chunks copied, and in the maps:
+ * chunk_flag = arrival flags, chunk_cnt = copies per chunk,
+ * tile_reduce_cnt = computations per tile, compute_owner per tile,
+ * reduce_owner[c] = the owner of chunk c's copy (bit 31: copied by a compute
+ * workgroup waiting for input), reduce_start/end[c] = that copy's span.
+ * Errors as for mk_gemm_reduce_local; MK_ERR_SHAPE also when Ms is not a
+ * multiple of tile_m.
+ */
+int mk_allgather_gemm_local(const void *A_local, const void *A_peers, int num_peers, void *A_gathered,
+                            const void *B, float *C, int64_t Ms, int64_t N, int64_t K, int tile_m,
+                            int tile_n, void *stream);
+
+/*
+ * mk_allgather_gemm_unfused -- the same result from two launches: a gather
+ * kernel stacks every shard into A_gathered, then the GEMM kernel computes C
+ * from it.  Arguments as above; touches no workspace state.
+ */
+int mk_allgather_gemm_unfused(const void *A_local, const void *A_peers, int num_peers, void *A_gathered,
+                              const void *B, float *C, int64_t Ms, int64_t N, int64_t K, int tile_m,
+                              int tile_n, void *stream);
+
+/*
  * mk_set_partition -- partition of the persistent workgroups into reduce and
  * compute roles for subsequent mk_gemm_reduce_local launches (process-wide).
  *   mode       mk_part_mode.
@@ -265,7 +324,7 @@ int mk_set_timeout_us(uint64_t timeout_us);
  */
 int mk_set_fault_skip_publish(int64_t tile);
 
-/* Statistics of the most recent completed mk_gemm_reduce_local launch. */
+/* Statistics of the most recent fused launch on the device (any kind). */
 typedef struct mk_stats {
     uint32_t struct_size;         /* in: sizeof(mk_stats) as the caller knows it */
     int32_t status;               /* MK_OK, MK_ERR_TIMEOUT or MK_ERR_PROTOCOL    */
@@ -305,6 +364,9 @@ typedef struct mk_stats {
     uint32_t sticky_errors;       /* bit 0 timeout, 1 XCD mismatch, 2 protocol:
                                      every kind raised by any launch since the
                                      last mk_get_stats (see there)             */
+    uint32_t kind;                /* 0 GEMM+AllReduce, 1 GEMM+ReduceScatter,
+                                     2 AllGather+GEMM (see mk_allgather_gemm_local
+                                     for how its statistics map onto these)  */
 } mk_stats;
 
 /* Words per map in the optional `maps` output of mk_get_stats, in order:
