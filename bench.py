@@ -74,6 +74,11 @@ def parse(argv=None):
     ap.add_argument("--reduce-scatter", action="store_true",
                     help="one rank's share of GEMM+ReduceScatter instead (fused and unfused legs); "
                          "prints its own JSON line")
+    ap.add_argument("--allgather", default=None, metavar="WORKLOAD",
+                    help="only one AllGather+GEMM workload (ag_tiny, ag_tp_share, ag_compute_heavy); "
+                         "prints its own JSON line")
+    ap.add_argument("--no-allgather", action="store_true",
+                    help="leave the AllGather+GEMM share out of the default line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of this size (counter calibration)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -403,6 +408,101 @@ def measure(args, w, mk, wl, upload, np, torch, keep_host=False):
     return rec, host
 
 
+AG_SUITE = ("ag_tiny", "ag_tp_share", "ag_compute_heavy")
+
+
+def ag_algorithmic_bytes(w):
+    """One rank's share of AllGather+GEMM: every shard read once and written
+    once into the gathered A, B read once, C written once."""
+    R = w.peers + 1
+    return 2 * R * w.M * w.K * 2 + 2 * w.K * w.N + 4 * R * w.M * w.N
+
+
+def measure_allgather(args, w, mk, wl, np, torch, sweep=True):
+    """One rank's share of AllGather+GEMM: fused (adaptive, and the pages'
+    plain rule), unfused (gather kernel then GEMM kernel), static copy
+    partitions 2..64."""
+    a0, ap, b = wl.make_ag_inputs(w)
+    dev = "cuda:0"
+    A0 = torch.from_numpy(a0.view(np.int16)).to(dev).view(torch.bfloat16)
+    AP = torch.from_numpy(ap.view(np.int16)).to(dev).view(torch.bfloat16)
+    B = torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16)
+    R = w.peers + 1
+    G = torch.empty((R * w.M, w.K), dtype=torch.bfloat16, device=dev)
+    C = torch.empty((R * w.M, w.N), dtype=torch.float32, device=dev)
+    del a0, ap, b
+    stream = torch.cuda.current_stream()
+    flush = None
+    if not args.no_flush:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+        def flush():
+            scratch.fill_(1)
+
+    def fused():
+        mk.allgather_gemm_local(A0, AP, G, B, C, w.tile_m, w.tile_n)
+
+    def unfused():
+        mk.allgather_gemm_unfused(A0, AP, G, B, C, w.tile_m, w.tile_n)
+
+    static_only = w.mode != "adaptive"
+    set_adaptive_defaults(mk)
+    if static_only:
+        mk.set_partition(w.mode, w.n_reduce)
+    ms_f, _ = time_leg(fused, args.steps, args.warmup, flush, stream, torch)
+    st = check_leg(mk, f"{w.name} fused", maps=True)
+    ms = statistics.fmean(ms_f)
+    M = R * w.M
+    flops = 2 * M * w.N * w.K
+    bytes_ = ag_algorithmic_bytes(w)
+    t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    t_hbm = bytes_ / (HBM_PEAK_GBPS * 1e9)
+    sec = ms / 1e3
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": bytes_ / sec / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / sec / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    copy_us = (st["reduce_ticks_end"] - st["reduce_ticks_start"]) / st["timer_hz"] * 1e6
+    rec = {"config": {"ranks": R, "rows_per_rank": w.M, "M": M, "N": w.N, "K": w.K,
+                      "tile": [w.tile_m, w.tile_n], "chunk_rows": w.tile_m},
+           "partition": w.mode if static_only else "adaptive",
+           "fused_ms": summary(ms_f), "ms": ms, "tflops": flops / sec / 1e12, "roofline": roof,
+           "algorithmic_flops": flops, "algorithmic_bytes": bytes_,
+           "copy_window_us": copy_us,
+           "n_reduce_range": [st["n_reduce_min_seen"], st["n_reduce_max_seen"]],
+           "help_copies": int((st["reduce_owner"][:st["num_chunks"]] >> 31).sum())}
+    print(f"[bench] {w.name} fused: {summary(ms_f)}", file=sys.stderr, flush=True)
+    ms_u, _ = time_leg(unfused, args.steps, args.warmup, flush, stream, torch)
+    rec["unfused_ms"] = summary(ms_u)
+    rec["fused_vs_unfused"] = statistics.fmean(ms_u) / ms
+    print(f"[bench] {w.name} unfused: {summary(ms_u)}", file=sys.stderr, flush=True)
+    if static_only or not sweep:
+        set_adaptive_defaults(mk)
+        return rec
+    mk.set_partition("adaptive", 2)
+    mk.set_adaptive_help(False)
+    mk.set_controller_cap(1024)
+    ms_p, _ = time_leg(fused, args.steps, args.warmup, flush, stream, torch)
+    check_leg(mk, f"{w.name} plain rule")
+    set_adaptive_defaults(mk)
+    rec["plain_rule_ms"] = summary(ms_p)
+    rec["labelled_variants_gain"] = statistics.fmean(ms_p) / ms
+    table = {}
+    for n in STATIC_SWEEP:
+        mk.set_partition("static", n)
+        ms_n, _ = time_leg(fused, max(3, args.steps // 2), 1, flush, stream, torch)
+        check_leg(mk, f"{w.name} static {n}")
+        table[n] = statistics.fmean(ms_n)
+    set_adaptive_defaults(mk)
+    best = min(table, key=table.get)
+    rec["static_sweep_ms"] = {str(k): v for k, v in table.items()}
+    rec["best_static_2_64"] = {"n_copy": best, "ms": table[best]}
+    rec["adaptive_vs_best_static_2_64"] = table[best] / ms
+    print(f"[bench] {w.name} static sweep: {table}", file=sys.stderr, flush=True)
+    return rec
+
+
 def geomean(xs):
     xs = [x for x in xs if x]
     return math.exp(sum(math.log(x) for x in xs) / len(xs)) if xs else None
@@ -488,6 +588,15 @@ def main(argv=None):
     if args.reduce_scatter:
         reduce_scatter(args, w_head, mk, wl, upload, np, torch)
         return
+    if args.allgather:
+        rec = measure_allgather(args, wl.ag_workload(args.allgather), mk, wl, np, torch,
+                                sweep=not (args.no_sweep or args.fused_only))
+        print(json.dumps({"metric": "AllGather+GEMM TFLOP/s (one rank's share, fused adaptive)",
+                          "value": rec["tflops"], "unit": "TFLOP/s", "ms_per_step": rec["ms"],
+                          "steps": args.steps, "warmup": args.warmup, "dtype": "bf16",
+                          "data": "synthetic", "config": {"workload": args.allgather, **rec["config"]},
+                          **{k: v for k, v in rec.items() if k != "config"}}), flush=True)
+        return
 
     names = [head_name] if (args.workload != "all" or args.fused_only) else \
         [head_name] + [n for n in SUITE if n != head_name]
@@ -543,6 +652,14 @@ def main(argv=None):
         }
         result["min_fused_vs_unfused"] = min(r.get("fused_vs_unfused", float("inf")) for r in full)
     result["per_config"] = per
+    if args.workload == "all" and not (args.fused_only or args.no_allgather):
+        ag = {}
+        for name in AG_SUITE:
+            ag[name] = measure_allgather(args, wl.ag_workload(name), mk, wl, np, torch,
+                                         sweep=not args.no_sweep)
+            torch.cuda.empty_cache()
+        result["allgather_gemm"] = ag
+        result["allgather_min_fused_vs_unfused"] = min(r["fused_vs_unfused"] for r in ag.values())
     print(json.dumps(result), flush=True)
 
 

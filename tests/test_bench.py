@@ -120,3 +120,15 @@ def test_bench_defaults_to_the_largest_workload():
     biggest = max(wl.WORKLOADS.values(), key=lambda w: w.flops)
     assert biggest.name == bench.HEADLINE
     assert set(bench.SUITE) == set(wl.WORKLOADS)
+
+
+def test_allgather_algorithmic_bytes():
+    """AllGather+GEMM share: every shard read once and written once into the
+    gathered A, B read once, C written once."""
+    import bench
+    import workloads as wl
+    w = wl.ag_workload("ag_tp_share")
+    R = w.peers + 1
+    assert bench.ag_algorithmic_bytes(w) == (2 * R * w.M * w.K * 2 + 2 * w.K * w.N
+                                            + 4 * R * w.M * w.N)
+    assert set(bench.AG_SUITE) == set(wl.AG_WORKLOADS)
