@@ -165,6 +165,7 @@ def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
     for rel in ("gemm_tile_granular_amd/csrc/mk_kernels.hip",
+                "gemm_tile_granular_amd/csrc/mk_device.hpp",
                 "gemm_tile_granular_amd/csrc/mk_internal.hpp"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())

@@ -1,0 +1,354 @@
+// Kernels of the AllGather+GEMM share (communication feeds compute) and its
+// unfused baseline's gather, on the GEMM core of the fused library.
+#include "mk_device.hpp"
+
+namespace mk {
+
+// ---------------------------------------------------------------------------
+// AllGather+GEMM, one rank's share (communication feeds compute)
+//
+// AllGather + GEMM row of the MarkTechPost page's five-kernel table: every
+// rank holds a shard of A, and the local GEMM consumes the gathered tiles as
+// they arrive.  "【学习】mKernel 分析" section 2.6 (Table 3): 128-row chunks,
+// shards submitted at launch, compute tiles taken in order of input
+// availability (local first); section 2.4: the same on-GPU controller sets
+// the communication-role size, and a compute block waiting for its input
+// helps communication.
+//
+// On one GPU the other ranks' shards are buffers in local HBM and the copy
+// role stands in for their transfer: a copy task moves one chunk (one tile
+// row of A: TM rows x K) into the gathered A, stores it write-through, and
+// publishes the chunk's arrival flag once the stores have drained.  A compute
+// task is one block of TPB adjacent tiles of one tile row; tiles of this
+// rank's own rows read the local shard at once, the others read the gathered
+// A once their chunk's flag carries the launch's epoch.  Claims: copy tasks
+// take the other ranks' chunks first (rank, then row), this rank's own last;
+// compute blocks go in row-major order, so this rank's rows come first and
+// the others follow in the order they are copied.  Roles follow the
+// workgroup index against the target (copy iff w < target), re-read at
+// every task boundary.
+// ---------------------------------------------------------------------------
+
+enum AgRole : int { kAgCompute = 0, kAgCopy = 1, kAgExit = 2 };
+
+struct AgDecision {
+    int role;
+    uint32_t unit;      // compute: block; copy: chunk
+    uint32_t ns_seen;   // copy target the task was taken under | kHelp (copy by a waiting compute workgroup)
+};
+
+struct AgSched {
+    uint32_t target;
+    uint32_t det_i;
+    bool copy_exhausted, compute_exhausted;
+    bool have_block;        // a claimed compute block waiting for its input
+    uint32_t block, block_ns;
+    int last_role;
+};
+
+__device__ __forceinline__ uint32_t ag_copy_chunk(const AgArgs &a, uint32_t q) {
+    const uint32_t peer_chunks = a.Ch - a.cps;
+    return q < peer_chunks ? a.cps + q : q - peer_chunks;
+}
+
+// the input rows of tile row `row` are there: this rank's own from the start,
+// the others once their chunk has arrived (one read, no wait)
+__device__ __forceinline__ bool ag_ready(const AgArgs &a, uint32_t row) {
+    return row < a.cps || ld_relaxed(&a.ws.chunk_flag[row]) == a.epoch;
+}
+
+__device__ __forceinline__ bool ag_timed_out(const AgArgs &a, Live *L, uint64_t since) {
+    if (ticks_now() - since <= a.timeout_ticks) return false;
+    __hip_atomic_fetch_max(&L->error, (uint32_t)kErrTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_or(&L->sticky, kStickyTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+}
+
+// wait (bounded) for tile row `row`'s input; false on timeout or another
+// workgroup's error
+__device__ bool ag_wait(const AgArgs &a, Live *L, uint32_t row) {
+    const uint64_t since = ticks_now();
+    for (;;) {
+        if (ag_ready(a, row)) return true;
+        if (ld_relaxed(&L->error) != kErrNone) return false;
+        if (ag_timed_out(a, L, since)) return false;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// Thread 0: the next task.
+__device__ AgDecision ag_next(const AgArgs &a, Live *L, uint32_t wg, AgSched &s) {
+    const uint32_t B = (uint32_t)a.nwg;
+    if (a.mode == kDeterministic) {
+        const uint32_t ns = (uint32_t)a.ns_init;
+        if (wg < ns) {
+            const uint32_t q = wg + s.det_i * ns;
+            if (q >= a.Ch) return {kAgExit, 0, ns};
+            ++s.det_i;
+            return {kAgCopy, ag_copy_chunk(a, q), ns};
+        }
+        const uint32_t j = (wg - ns) + s.det_i * (B - ns);
+        if (j >= a.TB) return {kAgExit, 0, ns};
+        ++s.det_i;
+        if (!ag_wait(a, L, j / a.bn)) return {kAgExit, 0, ns};
+        return {kAgCompute, j, ns};
+    }
+    for (;;) {
+        const uint32_t ns = s.target;
+        if (s.have_block) {
+            const uint32_t row = s.block / a.bn;
+            if (ag_ready(a, row)) {
+                s.have_block = false;
+                return {kAgCompute, s.block, s.block_ns};
+            }
+            // waiting for its input: help the copy role meanwhile
+            if (a.mode == kAdaptive && a.help && !s.copy_exhausted) {
+                const uint32_t q = add_relaxed(&L->compute_claim[1].v, 1u);
+                if (q < a.Ch) return {kAgCopy, ag_copy_chunk(a, q), ns | kHelp};
+                s.copy_exhausted = true;
+            }
+            if (!ag_wait(a, L, row)) return {kAgExit, 0, ns};
+            s.have_block = false;
+            return {kAgCompute, s.block, s.block_ns};
+        }
+        const bool copy_role = wg < ns;
+        if (copy_role && !s.copy_exhausted) {
+            const uint32_t q = add_relaxed(&L->compute_claim[1].v, 1u);
+            if (q < a.Ch) return {kAgCopy, ag_copy_chunk(a, q), ns};
+            s.copy_exhausted = true;
+        }
+        // static copiers leave once every chunk is claimed
+        if (copy_role && a.mode != kAdaptive) return {kAgExit, 0, ns};
+        if (!s.compute_exhausted) {
+            const uint32_t j = add_relaxed(&L->compute_claim[0].v, 1u);
+            if (j < a.TB) {
+                s.have_block = true;
+                s.block = j;
+                // a copy-role workgroup computes only once no chunk is left
+                // to claim: no copy role remains (logged as target 0)
+                s.block_ns = copy_role ? 0u : ns;
+                continue;
+            }
+            s.compute_exhausted = true;
+        }
+        // adaptive: no compute left to claim, every workgroup copies (the
+        // controller's target is B once no compute remains; logged as such)
+        if (a.mode == kAdaptive && !s.copy_exhausted) {
+            const uint32_t q = add_relaxed(&L->compute_claim[1].v, 1u);
+            if (q < a.Ch) return {kAgCopy, ag_copy_chunk(a, q), copy_role ? ns : B};
+            s.copy_exhausted = true;
+        }
+        return {kAgExit, 0, ns};
+    }
+}
+
+// one chunk: TM rows x K of a shard into the gathered A.  Source read once
+// (nt); destination written through (nt sc1), visible at device scope once
+// the stores have drained.
+template <int NT, int TM>
+__device__ __forceinline__ void ag_copy(const AgArgs &a, uint32_t c) {
+    const uint32_t r = c / a.cps, lr = c % a.cps;
+    const uint16_t *src = r == 0 ? a.A_local + (int64_t)lr * TM * a.K
+                                 : a.A_peers + ((int64_t)(r - 1) * a.Ms + (int64_t)lr * TM) * a.K;
+    uint16_t *dst = a.A_gath + (int64_t)c * TM * a.K;
+    const auto rs = scalar_rsrc(src);
+    const auto rd = scalar_rsrc(dst);
+    const uint32_t n16 = (uint32_t)(TM * a.K / 8);   // 16-byte pieces of the chunk
+    constexpr int U = 8;
+    uint32_t i = threadIdx.x;
+    for (; i + (U - 1) * NT < n16; i += U * NT) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (i + u * NT) * 16u, 0,
+                                                                                   kPolicyStream));
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(f32x4, v[u]), rd, (i + u * NT) * 16u, 0,
+                                                   kPolicyCoherentStream);
+    }
+    for (; i < n16; i += NT) {
+        const f32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, i * 16u, 0, kPolicyStream);
+        __builtin_amdgcn_raw_buffer_store_b128(v, rd, i * 16u, 0, kPolicyCoherentStream);
+    }
+}
+
+template <int TM, int TN>
+__global__ __launch_bounds__((GemmFor<TM, TN, kPolicyDefault>::NT),
+                             (TileCfg<TM, TN>::WPC * GemmFor<TM, TN, kPolicyDefault>::NWAVES / 4))
+void allgather_gemm_kernel(AgArgs a) {
+    using G = GemmFor<TM, TN, kPolicyDefault>;
+    constexpr int TPB = TileCfg<TM, TN>::TPB;
+    __shared__ __attribute__((aligned(1024))) char lds_raw[fused_lds_bytes<TM, TN>()];
+    __shared__ AgDecision sh_dec;
+    __shared__ AgSched sh_sched;
+    __shared__ uint64_t sh_c0, sh_r0;
+    lchar *lds = (lchar *)lds_raw;
+    const int tid = threadIdx.x;
+    const uint32_t wg = blockIdx.x;
+    Live *L = a.ws.live;
+    typename G::Lane ln;
+    G::init_lane(ln, a.N, a.K);
+    AgSched &s = sh_sched;
+    if (tid == 0) {
+        s.target = (uint32_t)a.ns_init;
+        s.det_i = 0;
+        s.copy_exhausted = s.compute_exhausted = false;
+        s.have_block = false;
+        s.block = s.block_ns = 0;
+        s.last_role = -1;
+        min_relaxed(&L->t_start, ticks_now());
+    }
+    for (;;) {
+        if (tid == 0) {
+            sh_dec = ag_next(a, L, wg, s);
+            sh_c0 = cycles_now();
+            sh_r0 = ticks_now();
+        }
+        __syncthreads();
+        AgDecision d;
+        d.role = __builtin_amdgcn_readfirstlane(sh_dec.role);
+        d.unit = __builtin_amdgcn_readfirstlane(sh_dec.unit);
+        d.ns_seen = __builtin_amdgcn_readfirstlane(sh_dec.ns_seen);
+        if (d.role == kAgExit) break;
+        const int64_t Kp = opaque(a.K), Np = opaque(a.N), Mp = opaque(a.M);
+        uint32_t t0 = 0, nt = 1;
+        if (d.role == kAgCopy) {
+            ag_copy<G::NT, TM>(a, d.unit);
+        } else {
+            const uint32_t row = d.unit / a.bn, bc = d.unit % a.bn;
+            t0 = row * a.tiles_n + bc * TPB;
+            nt = a.tiles_n - bc * TPB < (uint32_t)TPB ? a.tiles_n - bc * TPB : (uint32_t)TPB;
+            // this rank's own rows straight from its shard, the others from
+            // the gathered A (the chunk's flag was seen before the barrier)
+            const uint16_t *Asrc = row < a.cps ? a.A_local : a.A_gath;
+            G::block(ln, Asrc, a.B, a.C, Mp, Np, Kp, (int64_t)row * TM, (int64_t)bc * (TPB * TN), lds, [] {});
+        }
+        // payload before flag ("【学习】mKernel 分析" section 2.5)
+        drain_vmem();
+        __syncthreads();
+        if (tid == 0) {
+            const uint32_t t_end = (uint32_t)ticks_now();
+            const uint64_t dt = cycles_now() - sh_c0;
+            if (d.role == kAgCopy) {
+                const uint32_t c = d.unit;
+                if ((int64_t)c != a.skip_publish) st_relaxed(&a.ws.chunk_flag[c], a.epoch);
+                const uint32_t old = add_relaxed(&a.ws.chunk_cnt[c], 1u);
+                if (old != a.calls - 1) note_violation(L);
+                a.ws.rowner[c] = (d.ns_seen << 16) | wg;
+                a.ws.timeline[2u * a.Tcap + c] = (uint32_t)sh_r0;
+                a.ws.timeline[3u * a.Tcap + c] = t_end;
+                add_relaxed(&L->chunks_released.v, 1u);
+            } else {
+                for (uint32_t k = 0; k < nt; ++k) {
+                    const uint32_t t = t0 + k;
+                    const uint32_t old = add_relaxed(&a.ws.tile_cnt[t], 1u);
+                    if (old != a.calls - 1) note_violation(L);
+                    a.ws.cowner[t] = (d.ns_seen << 16) | wg;
+                    a.ws.timeline[t] = (uint32_t)sh_r0;
+                    a.ws.timeline[a.Tcap + t] = t_end;
+                }
+            }
+            // progress words, and one controller step: the copy role is the
+            // communication role s (chunks), compute is p (tiles)
+            const bool copying = d.role == kAgCopy;
+            const uint64_t inc = (dt << kCountBits) | (copying ? 1u : nt);
+            const uint64_t mine = add_relaxed(copying ? &L->role_reduce.v : &L->role_compute.v, inc) + inc;
+            const uint64_t other = ld_relaxed(copying ? &L->role_compute.v : &L->role_reduce.v);
+            if (copying) {
+                min_relaxed(&L->r_start, (uint64_t)sh_r0);
+                max_relaxed(&L->r_end, ticks_now());
+            }
+            if (a.mode == kAdaptive) {
+                const uint64_t cw = copying ? other : mine, sw = copying ? mine : other;
+                const uint32_t raw = ld_relaxed(&L->target_ns.v);
+                const uint32_t cur = raw ? raw : (uint32_t)a.ns_init;
+                const uint32_t n = controller_update_totals(
+                    (uint32_t)a.nwg, a.T, a.Ch, (uint32_t)(cw & kCountMask), (uint32_t)(sw & kCountMask),
+                    cw >> kCountBits, sw >> kCountBits, cur, (uint32_t)a.ns_floor, 1u, (uint32_t)a.ns_cap);
+                if (n != cur || raw == 0) {
+                    st_relaxed(&L->target_ns.v, n);
+                    min_relaxed(&L->ns_min, n);
+                    max_relaxed(&L->ns_max, n);
+                }
+                s.target = n;
+            }
+            if (s.last_role >= 0 && s.last_role != d.role) add_relaxed(&L->role_switches, 1u);
+            s.last_role = d.role;
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        max_relaxed(&L->t_end, ticks_now());
+        drain_vmem();
+        const uint32_t old = add_relaxed(&L->exit_count, 1u);
+        if (old == (uint32_t)a.nwg - 1) {
+            FusedArgs f;
+            f.mode = a.mode;
+            f.ns_init = a.ns_init;
+            f.ws = a.ws;
+            finish_launch(f, L);
+        }
+    }
+}
+
+// the unfused baseline's first kernel: every shard into the gathered A
+__global__ __launch_bounds__(256) void gather_kernel(AgArgs a) {
+    const int64_t row16 = a.K / 8;                     // 16-byte pieces per row
+    const int64_t shard16 = a.Ms * row16;
+    const int64_t total = shard16 * (a.P + 1);
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    u32x4 *dst = (u32x4 *)a.A_gath;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += stride) {
+        const int64_t r = i / shard16, o = i - r * shard16;
+        const u32x4 *src = (const u32x4 *)(r == 0 ? a.A_local : a.A_peers + (r - 1) * a.Ms * a.K);
+        __builtin_nontemporal_store(__builtin_nontemporal_load(src + o), dst + i);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+template <int TM, int TN>
+static int ag_residency() {
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &blocks, reinterpret_cast<const void *>(&allgather_gemm_kernel<TM, TN>),
+            GemmFor<TM, TN, kPolicyDefault>::NT, 0) != hipSuccess)
+        return 0;
+    return blocks < TileCfg<TM, TN>::WPC ? blocks : TileCfg<TM, TN>::WPC;
+}
+
+int allgather_workgroups_per_cu(int tm, int tn) {
+    if (tm == 64 && tn == 64) return ag_residency<64, 64>();
+    if (tm == 128 && tn == 128) return ag_residency<128, 128>();
+    if (tm == 256 && tn == 128) return ag_residency<256, 128>();
+    return 0;
+}
+
+template <int TM, int TN>
+static hipError_t launch_ag_t(const AgArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL((allgather_gemm_kernel<TM, TN>), dim3(a.nwg), dim3(GemmFor<TM, TN, kPolicyDefault>::NT),
+                       0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_allgather_gemm(int tm, int tn, const AgArgs &a, hipStream_t s) {
+    if (tm == 64 && tn == 64) return launch_ag_t<64, 64>(a, s);
+    if (tm == 128 && tn == 128) return launch_ag_t<128, 128>(a, s);
+    if (tm == 256 && tn == 128) return launch_ag_t<256, 128>(a, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_gather(const AgArgs &a, int num_cu, hipStream_t s) {
+    const int64_t total = a.Ms * (a.K / 8) * (a.P + 1);
+    int64_t blocks = (total + 255) / 256;
+    const int64_t cap = (int64_t)num_cu * 8;
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(gather_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace mk
