@@ -200,8 +200,10 @@ def measured_traffic(workload):
 def counter_figures(workload):
     """Counter-derived figures of the fused kernel from the committed
     rocprofv3 passes, when they match the current kernel sources:
-      - GEMM TFLOP/s: MFMA work counted by SQ_INSTS_VALU_MFMA_MOPS_BF16
-        (512 flops per count) over the kernel-trace average duration;
+      - GEMM TFLOP/s: SQ_INSTS_MFMA (one v_mfma_f32_32x32x16_bf16 per count,
+        32768 flops) over the kernel-trace average duration;
+      - MFMA busy: SQ_INSTS_MFMA x 32 SIMD cycles over 1024 SIMDs times
+        GRBM_GUI_ACTIVE / 8 (cycles of one XCD over the dispatch);
       - HBM GB/s over the launch: copy-calibrated FETCH_SIZE + WRITE_SIZE
         over the same duration (the reduce role moves nearly all of it)."""
     rec = _traffic_record()
@@ -212,10 +214,12 @@ def counter_figures(workload):
         return None
     sec = wrec["kernel_trace_avg_us"] * 1e-6
     out = {"kernel_trace_avg_us": wrec["kernel_trace_avg_us"], "source": "profiles/traffic.json"}
-    if "mfma_mops_bf16" in wrec:
-        flops = wrec["mfma_mops_bf16"] * 512.0
+    if "sq_insts_mfma" in wrec:
+        flops = wrec["sq_insts_mfma"] * 32768.0
         out["gemm_tflops_counters"] = flops / sec / 1e12
         out["mfma_flops_per_launch_counters"] = flops
+        if wrec.get("grbm_gui_active"):
+            out["mfma_busy"] = wrec["sq_insts_mfma"] * 32.0 / (1024.0 * wrec["grbm_gui_active"] / 8.0)
     if "hbm_bytes_per_launch" in wrec:
         out["hbm_GBps_counters"] = wrec["hbm_bytes_per_launch"] / sec / 1e9
     return out

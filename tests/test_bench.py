@@ -30,7 +30,8 @@ def test_traffic_record_is_reported_only_for_its_kernel():
             got, note = bench.measured_traffic(name)
             assert got is None and "changed" in note
         return
-    for name in ("tp_share", "compute_heavy"):
+    import workloads as wl
+    for name in wl.WORKLOADS:
         got, note = bench.measured_traffic(name)
         want = rec["workloads"][name]
         assert got == pytest.approx(want["hbm_bytes_per_launch"]), note
@@ -39,7 +40,11 @@ def test_traffic_record_is_reported_only_for_its_kernel():
                   + want["write_size_kib"] * rec["calibration"]["WRITE_SIZE"]["factor"]) * 1024
         assert got == pytest.approx(scaled, rel=1e-9)
         assert got >= want["algorithmic_bytes"]
-    assert bench.measured_traffic("tiny")[0] is None
+        cf = bench.counter_figures(name)
+        # the MFMA instruction count is the GEMM's own flop count, 2MNK
+        assert cf["mfma_flops_per_launch_counters"] == wl.workload(name).flops
+        assert 0.0 < cf["mfma_busy"] < 1.0
+    assert bench.measured_traffic("no_such_workload")[0] is None
 
 
 def test_algorithmic_work_of_the_named_workloads():
