@@ -322,16 +322,14 @@ def measure(args, w, mk, wl, upload, np, torch, keep_host=False):
     def unfused():
         mk.gemm_reduce_unfused(A, B, P, C, w.tile_m, w.tile_n, w.tiles_per_chunk)
 
-    # the tiny workload runs its fixed partition (2 static reducers); the
-    # others the adaptive controller
-    static_only = w.mode != "adaptive"
+    # every workload's fused leg runs the adaptive controller; a workload
+    # whose recipe fixes a partition (tiny: 2 static reducers) also times
+    # that partition as a leg of its own, and skips the sweep
+    fixed = w.mode != "adaptive"
     set_adaptive_defaults(mk)
-    if static_only:
-        mk.set_partition(w.mode, w.n_reduce)
     ms_fused, wall = time_leg(fused, args.steps, args.warmup, flush, stream, torch)
     st = check_leg(mk, f"{w.name} fused", maps=True)
-    rec = {"partition": w.mode if static_only else "adaptive", "fused_ms": summary(ms_fused),
-           "wall_s_fused_leg": wall}
+    rec = {"partition": "adaptive", "fused_ms": summary(ms_fused), "wall_s_fused_leg": wall}
     ms = statistics.fmean(ms_fused)
     roof, tflops, gbps = roofline(w, ms)
     roof["kernel"] = (f"mk::fused_gemm_reduce_kernel<{w.tile_m}, {w.tile_n}, "
@@ -375,7 +373,15 @@ def measure(args, w, mk, wl, upload, np, torch, keep_host=False):
     rec["fused_vs_unfused"] = statistics.fmean(ms_unf) / ms
     print(f"[bench] {w.name} unfused: {summary(ms_unf)}", file=sys.stderr, flush=True)
 
-    if static_only or args.no_sweep:
+    if fixed:
+        mk.set_partition(w.mode, w.n_reduce)
+        ms_fix, _ = time_leg(fused, args.steps, args.warmup, flush, stream, torch)
+        check_leg(mk, f"{w.name} {w.mode} {w.n_reduce}")
+        set_adaptive_defaults(mk)
+        rec["recipe_partition"] = {"mode": w.mode, "n_reduce": w.n_reduce, "fused_ms": summary(ms_fix),
+                                   "fused_vs_unfused": statistics.fmean(ms_unf) / statistics.fmean(ms_fix)}
+        print(f"[bench] {w.name} fused, {w.mode} {w.n_reduce}: {summary(ms_fix)}", file=sys.stderr, flush=True)
+    if fixed or args.no_sweep:
         set_adaptive_defaults(mk)
         return rec, host
 
@@ -450,10 +456,8 @@ def measure_allgather(args, w, mk, wl, np, torch, sweep=True):
     def unfused():
         mk.allgather_gemm_unfused(A0, AP, G, B, C, w.tile_m, w.tile_n)
 
-    static_only = w.mode != "adaptive"
+    fixed = w.mode != "adaptive"
     set_adaptive_defaults(mk)
-    if static_only:
-        mk.set_partition(w.mode, w.n_reduce)
     ms_f, _ = time_leg(fused, args.steps, args.warmup, flush, stream, torch)
     st = check_leg(mk, f"{w.name} fused", maps=True)
     ms = statistics.fmean(ms_f)
@@ -471,7 +475,7 @@ def measure_allgather(args, w, mk, wl, np, torch, sweep=True):
     copy_us = (st["reduce_ticks_end"] - st["reduce_ticks_start"]) / st["timer_hz"] * 1e6
     rec = {"config": {"ranks": R, "rows_per_rank": w.M, "M": M, "N": w.N, "K": w.K,
                       "tile": [w.tile_m, w.tile_n], "chunk_rows": w.tile_m},
-           "partition": w.mode if static_only else "adaptive",
+           "partition": "adaptive",
            "fused_ms": summary(ms_f), "ms": ms, "tflops": flops / sec / 1e12, "roofline": roof,
            "algorithmic_flops": flops, "algorithmic_bytes": bytes_,
            "copy_window_us": copy_us,
@@ -482,7 +486,14 @@ def measure_allgather(args, w, mk, wl, np, torch, sweep=True):
     rec["unfused_ms"] = summary(ms_u)
     rec["fused_vs_unfused"] = statistics.fmean(ms_u) / ms
     print(f"[bench] {w.name} unfused: {summary(ms_u)}", file=sys.stderr, flush=True)
-    if static_only or not sweep:
+    if fixed:
+        mk.set_partition(w.mode, w.n_reduce)
+        ms_x, _ = time_leg(fused, args.steps, args.warmup, flush, stream, torch)
+        check_leg(mk, f"{w.name} {w.mode} {w.n_reduce}")
+        set_adaptive_defaults(mk)
+        rec["recipe_partition"] = {"mode": w.mode, "n_copy": w.n_reduce, "fused_ms": summary(ms_x),
+                                   "fused_vs_unfused": statistics.fmean(ms_u) / statistics.fmean(ms_x)}
+    if fixed or not sweep:
         set_adaptive_defaults(mk)
         return rec
     mk.set_partition("adaptive", 2)

@@ -1,6 +1,7 @@
 // Kernels of the AllGather+GEMM share (communication feeds compute) and its
 // unfused baseline's gather, on the GEMM core of the fused library.
 #include "mk_device.hpp"
+#include "mk_allgather.hpp"
 
 namespace mk {
 
@@ -23,8 +24,13 @@ namespace mk {
 // rank's own rows read the local shard at once, the others read the gathered
 // A once their chunk's flag carries the launch's epoch.  Claims: copy tasks
 // take the other ranks' chunks first (rank, then row), this rank's own last;
-// compute blocks go in row-major order, so this rank's rows come first and
-// the others follow in the order they are copied.  Roles follow the
+// compute blocks go in row order, so this rank's rows come first and the
+// others follow in the order they are copied.  With column bands (one per
+// XCD, workgroup w on XCD w mod 8) each band is its own row-order queue:
+// the workgroups of one XCD share its band's B columns in their L2 and the
+// chip reads B about once per band row group instead of once per XCD per
+// row; a workgroup whose band is exhausted takes blocks from the next bands.
+// Roles follow the
 // workgroup index against the target (copy iff w < target), re-read at
 // every task boundary.
 // ---------------------------------------------------------------------------
@@ -43,6 +49,7 @@ struct AgSched {
     bool copy_exhausted, compute_exhausted;
     bool have_block;        // a claimed compute block waiting for its input
     uint32_t block, block_ns;
+    uint32_t bands_done;    // bit x: band x has no compute block left
     int last_role;
 };
 
@@ -74,6 +81,33 @@ __device__ bool ag_wait(const AgArgs &a, Live *L, uint32_t row) {
         if (ag_timed_out(a, L, since)) return false;
         __builtin_amdgcn_s_sleep(1);
     }
+}
+
+// Thread 0: claim a compute block.  One band: the row-major queue.  Bands:
+// block columns split as evenly as possible (the first bn mod bands bands
+// one wider), band x's i-th claim is row i / cols, column col0 + i mod cols;
+// the home band (the workgroup's XCD) first, then the others in turn.
+__device__ __forceinline__ bool ag_claim_block(const AgArgs &a, Live *L, uint32_t wg, AgSched &s,
+                                               uint32_t &j) {
+    const uint32_t nb = a.bands;
+    if (nb <= 1) {
+        j = add_relaxed(&L->compute_claim[0].v, 1u);
+        return j < a.TB;
+    }
+    const uint32_t cmin = a.bn / nb, crem = a.bn % nb;
+    for (uint32_t k = 0; k < nb; ++k) {
+        const uint32_t x = (wg + k) % nb;
+        if ((s.bands_done >> x) & 1u) continue;
+        const uint32_t cols = cmin + (x < crem ? 1u : 0u);
+        const uint32_t col0 = x * cmin + (x < crem ? x : crem);
+        const uint32_t i = add_relaxed(&L->extra_claim[x].v, 1u);
+        if (i < a.Ch * cols) {
+            j = (i / cols) * a.bn + col0 + i % cols;
+            return true;
+        }
+        s.bands_done |= 1u << x;
+    }
+    return false;
 }
 
 // Thread 0: the next task.
@@ -120,8 +154,8 @@ __device__ AgDecision ag_next(const AgArgs &a, Live *L, uint32_t wg, AgSched &s)
         // static copiers leave once every chunk is claimed
         if (copy_role && a.mode != kAdaptive) return {kAgExit, 0, ns};
         if (!s.compute_exhausted) {
-            const uint32_t j = add_relaxed(&L->compute_claim[0].v, 1u);
-            if (j < a.TB) {
+            uint32_t j;
+            if (ag_claim_block(a, L, wg, s, j)) {
                 s.have_block = true;
                 s.block = j;
                 // a copy-role workgroup computes only once no chunk is left
@@ -196,6 +230,7 @@ void allgather_gemm_kernel(AgArgs a) {
         s.copy_exhausted = s.compute_exhausted = false;
         s.have_block = false;
         s.block = s.block_ns = 0;
+        s.bands_done = 0;
         s.last_role = -1;
         min_relaxed(&L->t_start, ticks_now());
     }

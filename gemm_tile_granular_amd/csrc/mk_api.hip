@@ -11,6 +11,7 @@
 
 #include "mk.h"
 #include "mk_internal.hpp"
+#include "mk_allgather.hpp"
 
 namespace {
 
@@ -635,6 +636,12 @@ int run_allgather(bool fused, const void *A_local, const void *A_peers, int num_
     a.bn = (uint32_t)((tiles_n + tpb - 1) / tpb);
     a.T = (uint32_t)T;
     a.TB = a.Ch * a.bn;
+    // compute claims in column bands, one per XCD, when workgroups map to
+    // XCDs round-robin and every band gets a block column
+    {
+        const int want = set.xcd_bands ? set.xcd_bands : kMaxXcd;
+        a.bands = (dev.xcd_ok && (int64_t)a.bn >= want) ? (uint32_t)want : 1u;
+    }
 
     if (!fused) {
         hipError_t e = launch_gather(a, dev.num_cu, s);
@@ -719,6 +726,7 @@ int run_allgather(bool fused, const void *A_local, const void *A_peers, int num_
     d.last.ns_init = (uint32_t)ns_init;
     d.last.cap = (uint32_t)cap;
     d.last.help = (uint32_t)set.help;
+    d.last.bands = a.bands;
     return MK_OK;
 }
 

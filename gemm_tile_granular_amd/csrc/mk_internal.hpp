@@ -117,30 +117,6 @@ struct FusedArgs {
     WsView ws;
 };
 
-// One rank's share of AllGather+GEMM: this rank's shard A_local [Ms, K], the
-// other ranks' shards A_peers [P, Ms, K] (rank 1 first), the gathered A
-// [R Ms, K] (output, shards stacked by rank) and C = gathered . B [R Ms, N].
-// A chunk is one tile row of A (TM rows); chunk c holds rows [c TM, (c+1) TM).
-struct AgArgs {
-    const uint16_t *A_local;
-    const uint16_t *A_peers;
-    uint16_t *A_gath;
-    const uint16_t *B;
-    float *C;
-    int64_t Ms, M, N, K;      // M = R Ms
-    int32_t P;
-    uint32_t cps;             // chunks per shard (Ms / TM)
-    uint32_t Ch;              // chunks: R cps
-    uint32_t tiles_n, bn;     // tiles per tile row, compute blocks per tile row
-    uint32_t T, TB;           // tiles, compute blocks
-    uint32_t Tcap;
-    uint32_t epoch, calls;
-    int32_t mode, ns_init, ns_floor, ns_cap, nwg, help;
-    uint64_t timeout_ticks;
-    int64_t skip_publish;     // fault injection: chunk whose arrival flag is never set (-1 none)
-    WsView ws;
-};
-
 struct GemmArgs {
     const uint16_t *A;
     const uint16_t *B;
@@ -168,10 +144,6 @@ struct ReduceArgs {
 hipError_t launch_fused(int tile_m, int tile_n, const FusedArgs &a, hipStream_t s);
 hipError_t launch_gemm(int tile_m, int tile_n, const GemmArgs &a, int num_cu, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs &a, int num_cu, hipStream_t s);
-hipError_t launch_allgather_gemm(int tile_m, int tile_n, const AgArgs &a, hipStream_t s);
-// gather every shard into A_gath (the unfused baseline's first kernel)
-hipError_t launch_gather(const AgArgs &a, int num_cu, hipStream_t s);
-int allgather_workgroups_per_cu(int tile_m, int tile_n);
 hipError_t launch_ws_init(Live *live, Live *snap, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t *p, uint32_t value, int64_t n, hipStream_t s);
 hipError_t launch_controller_eval(const uint64_t *in, uint32_t *out, int n, hipStream_t s);

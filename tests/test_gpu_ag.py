@@ -94,6 +94,8 @@ AG_SHAPES = [
     (1, 128, 64, 128, 128, 128),        # one rank: the gather is a copy of the local shard
     (8, 128, 128, 136, 64, 64),
     (5, 384, 1024, 512, 128, 128),      # K a whole number of slabs: the fast K loop
+    (3, 128, 256, 1000, 64, 64),        # 16 block columns (ragged last tile): 8 bands of 2
+    (4, 256, 512, 2600, 128, 128),      # 11 block columns, the last ragged: bands of 2 and 1
 ]
 
 
@@ -193,3 +195,28 @@ def test_allgather_full_size_sampled(mk, name):
     assert err <= REL_TOL * float(np.max(np.abs(ref))), err
     gu, Cu, _ = run_ag(mk, False, w, a0, ap, b)
     assert np.array_equal(C, Cu) and np.array_equal(g, gu)
+
+
+@pytest.mark.parametrize("shape", [(3, 128, 256, 1000, 64, 64), (4, 256, 512, 2600, 128, 128)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_allgather_column_bands_change_no_result(mk, shape):
+    """Compute claims in 1, 2, 4 or 8 column bands (one queue per XCD) move
+    blocks between workgroups only: the gathered A and C are bit-identical
+    for every band count, and the protocol state matches its closed form."""
+    R, Ms, K, N, tm, tn = shape
+    w = wl.custom(Ms, N, K, R - 1, tm, tn, 1, wid=840 + R)
+    a0, ap, b = wl.make_ag_inputs(w)
+    base = None
+    try:
+        for bands in (1, 2, 4, 8):
+            mk.set_xcd_bands(bands)
+            g, C, st = run_ag(mk, True, w, a0, ap, b, "adaptive", 0)
+            ag_protocol(st, w, "adaptive", 0)
+            assert st["xcd_bands"] in (1, bands)
+            if base is None:
+                check_ag(g, C, a0, ap, b)
+                base = (g, C)
+            else:
+                assert np.array_equal(g, base[0]) and np.array_equal(C, base[1])
+    finally:
+        mk.set_xcd_bands(0)
