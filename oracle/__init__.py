@@ -528,27 +528,41 @@ def ag_copy_order(ranks: int, chunks_per_shard: int) -> np.ndarray:
     return np.concatenate([peers, local])
 
 
-def ag_expected_state(n_chunks: int, n_tiles: int, epoch: int, calls: int) -> Dict[str, np.ndarray]:
+def ag_parts_per_chunk(tile_m: int, K: int, tiles_n: int) -> int:
+    """Copy tasks one chunk is split into.  The pages fix the chunk (the
+    arrival unit, one tile row of A) but not how many movers share it; here
+    one copy task moves at most 64 KiB of the chunk's tile_m x K bf16 bytes:
+    ceil(2 tile_m K / 65536) parts, at least 1 and at most min(tiles_n, 64)."""
+    parts = -(-(2 * tile_m * K) // 65536)
+    return int(max(1, min(parts, tiles_n, 64)))
+
+
+def ag_expected_state(n_chunks: int, n_tiles: int, epoch: int, calls: int,
+                      parts: int = 1) -> Dict[str, np.ndarray]:
     """Integer state after `calls` complete launches of one shape: every
-    chunk's arrival flag holds the last epoch, every chunk was copied and
-    every tile computed exactly once per call."""
+    chunk's arrival flag holds the last epoch, each of a chunk's `parts`
+    copy tasks ran and every tile was computed exactly once per call."""
     return {
         "chunk_flag": np.full(n_chunks, epoch, dtype=np.int64),
-        "chunk_copy_cnt": np.full(n_chunks, calls, dtype=np.int64),
+        "chunk_copy_cnt": np.full(n_chunks, parts * calls, dtype=np.int64),
         "tile_compute_cnt": np.full(n_tiles, calls, dtype=np.int64),
     }
 
 
 def ag_deterministic_owners(ranks: int, chunks_per_shard: int, tiles_n: int, B: int, n_copy: int,
-                            tiles_per_task: int = 1) -> Tuple[np.ndarray, np.ndarray]:
+                            tiles_per_task: int = 1, parts: int = 1) -> Tuple[np.ndarray, np.ndarray]:
     """Owner maps of the deterministic static schedule: workgroups
-    [0, n_copy) copy, the others compute.  Copy task i (in copy order) goes
-    to workgroup i mod n_copy; compute task j (blocks of `tiles_per_task`
-    adjacent tiles, row by row) to n_copy + j mod (B - n_copy).  Returns
-    (copy owner per chunk id, compute owner per tile)."""
+    [0, n_copy) copy, the others compute.  Copy tasks are the chunks in copy
+    order, each split into `parts` consecutive tasks; copy task i goes to
+    workgroup i mod n_copy.  Compute task j (blocks of `tiles_per_task`
+    adjacent tiles, row by row) goes to n_copy + j mod (B - n_copy).
+    Returns (copy owner per copy task, indexed chunk id * parts + part;
+    compute owner per tile)."""
     order = ag_copy_order(ranks, chunks_per_shard)
-    copy_owner = np.zeros(order.shape[0], dtype=np.int64)
-    copy_owner[order] = np.arange(order.shape[0]) % n_copy
+    n_tasks = order.shape[0] * parts
+    i = np.arange(n_tasks, dtype=np.int64)
+    copy_owner = np.zeros(n_tasks, dtype=np.int64)
+    copy_owner[order[i // parts] * parts + i % parts] = i % n_copy
     T = ranks * chunks_per_shard * tiles_n
     task = compute_task_of_tile(T, tiles_n, tiles_per_task)
     return copy_owner, n_copy + task % (B - n_copy)
@@ -556,7 +570,7 @@ def ag_deterministic_owners(ranks: int, chunks_per_shard: int, tiles_n: int, B: 
 
 def ag_check_state(maps: Dict[str, np.ndarray], ranks: int, chunks_per_shard: int, tiles_n: int,
                    epoch: int, calls: int, B: int, mode: str, n_copy: int,
-                   tiles_per_task: int = 1) -> List[str]:
+                   tiles_per_task: int = 1, parts: int = 1) -> List[str]:
     """Compare an AllGather+GEMM launch's protocol state with its closed form.
 
     Owner words are (mark << 31) | (copy target seen << 16) | workgroup.  A
@@ -567,7 +581,7 @@ def ag_check_state(maps: Dict[str, np.ndarray], ranks: int, chunks_per_shard: in
     bad: List[str] = []
     n_chunks = ranks * chunks_per_shard
     T = n_chunks * tiles_n
-    for key, want in ag_expected_state(n_chunks, T, epoch, calls).items():
+    for key, want in ag_expected_state(n_chunks, T, epoch, calls, parts).items():
         got = np.asarray(maps[key], dtype=np.int64)
         if got.shape != want.shape:
             bad.append(f"{key}: shape {got.shape} != {want.shape}")
@@ -578,12 +592,14 @@ def ag_check_state(maps: Dict[str, np.ndarray], ranks: int, chunks_per_shard: in
             bad.append(f"{key}[{i}] = {int(got[i])}, expected {int(want[i])} ({idx.size} mismatches)")
     co = np.asarray(maps["copy_owner"], dtype=np.int64)
     po = np.asarray(maps["compute_owner"], dtype=np.int64)
+    if co.shape != (n_chunks * parts,):
+        return bad + [f"copy_owner: shape {co.shape} != ({n_chunks * parts},)"]
     co_wg, co_ns, co_help = co & OWNER_WG_MASK, (co >> 16) & OWNER_NS_MASK, (co & OWNER_HELP) != 0
     po_wg, po_ns, po_mark = po & OWNER_WG_MASK, (po >> 16) & OWNER_NS_MASK, (po & OWNER_HELP) != 0
     if np.any(co_wg >= B) or np.any(po_wg >= B):
         bad.append("owner outside [0, B)")
     if mode == "deterministic":
-        dc, dp = ag_deterministic_owners(ranks, chunks_per_shard, tiles_n, B, n_copy, tiles_per_task)
+        dc, dp = ag_deterministic_owners(ranks, chunks_per_shard, tiles_n, B, n_copy, tiles_per_task, parts)
         if not np.array_equal(co_wg, dc):
             i = int(np.nonzero(co_wg != dc)[0][0])
             bad.append(f"copy_owner[{i}] = {int(co_wg[i])}, expected {int(dc[i])}")
@@ -600,10 +616,10 @@ def ag_check_state(maps: Dict[str, np.ndarray], ranks: int, chunks_per_shard: in
     if np.any(po_mark):
         bad.append(f"tile {int(np.nonzero(po_mark)[0][0])}: compute owner carries the help mark")
     if mode != "adaptive" and np.any(co_help):
-        bad.append(f"chunk {int(np.nonzero(co_help)[0][0])}: help copy outside adaptive mode")
+        bad.append(f"copy task {int(np.nonzero(co_help)[0][0])}: help copy outside adaptive mode")
     if np.any((co_wg >= co_ns) & ~co_help):
         i = int(np.nonzero((co_wg >= co_ns) & ~co_help)[0][0])
-        bad.append(f"chunk {i} copied by workgroup {int(co_wg[i])} while the copy target was {int(co_ns[i])}")
+        bad.append(f"copy task {i} run by workgroup {int(co_wg[i])} while the copy target was {int(co_ns[i])}")
     if np.any(po_wg < po_ns):
         i = int(np.nonzero(po_wg < po_ns)[0][0])
         bad.append(f"tile {i} computed by workgroup {int(po_wg[i])} while the copy target was {int(po_ns[i])}")

@@ -186,3 +186,42 @@ def test_ag_check_state_roles_and_help_mark():
     maps = _good()
     maps["compute_owner"][0:2] = 1 | (2 << 16)
     assert oracle.ag_check_state(maps, 2, 2, 3, 3, 2, 5, "adaptive", 2, 2)
+
+
+def test_parts_per_chunk_hand_values():
+    # ceil(2 tile_m K / 64 KiB), at least 1, at most min(tiles_n, 64)
+    assert oracle.ag_parts_per_chunk(64, 256, 4) == 1          # 32 KiB chunk
+    assert oracle.ag_parts_per_chunk(64, 512, 4) == 1          # exactly 64 KiB
+    assert oracle.ag_parts_per_chunk(64, 520, 4) == 2          # just over
+    assert oracle.ag_parts_per_chunk(128, 1792, 32) == 7       # 448 KiB
+    assert oracle.ag_parts_per_chunk(256, 8192, 64) == 64      # 4 MiB
+    assert oracle.ag_parts_per_chunk(256, 16384, 64) == 64     # capped at 64
+    assert oracle.ag_parts_per_chunk(128, 4096, 2) == 2        # capped at tiles_n
+
+
+def test_deterministic_owners_with_parts_hand_example():
+    # 2 ranks x 1 chunk, 2 parts, 3 copiers: copy order [1, 0]; tasks in
+    # order (1,0) (1,1) (0,0) (0,1) dealt to 0 1 2 0; indexed chunk*2 + part
+    co, _ = oracle.ag_deterministic_owners(2, 1, 1, 5, 3, 1, parts=2)
+    np.testing.assert_array_equal(co, [2, 0, 0, 1])
+
+
+def test_ag_check_state_with_parts():
+    exp = oracle.ag_expected_state(4, 12, 3, 2, parts=3)
+    np.testing.assert_array_equal(exp["chunk_copy_cnt"], [6, 6, 6, 6])
+    co, po = oracle.ag_deterministic_owners(2, 2, 3, 5, 2, 2, parts=3)
+    maps = {k: v.copy() for k, v in exp.items()}
+    maps["copy_owner"] = co | (2 << 16)
+    maps["compute_owner"] = po | (2 << 16)
+    assert oracle.ag_check_state(maps, 2, 2, 3, 3, 2, 5, "deterministic", 2, 2, parts=3) == []
+    # one part short of a chunk, or a map of one owner per chunk, is caught
+    bad = {k: v.copy() for k, v in maps.items()}
+    bad["chunk_copy_cnt"][2] = 5
+    assert oracle.ag_check_state(bad, 2, 2, 3, 3, 2, 5, "deterministic", 2, 2, parts=3)
+    bad = {k: v.copy() for k, v in maps.items()}
+    bad["copy_owner"] = bad["copy_owner"][:4]
+    assert oracle.ag_check_state(bad, 2, 2, 3, 3, 2, 5, "deterministic", 2, 2, parts=3)
+    # swapping two parts' owners breaks the deterministic deal
+    bad = {k: v.copy() for k, v in maps.items()}
+    bad["copy_owner"][[0, 1]] = bad["copy_owner"][[1, 0]]
+    assert oracle.ag_check_state(bad, 2, 2, 3, 3, 2, 5, "deterministic", 2, 2, parts=3)
