@@ -17,13 +17,19 @@ namespace mk {
 // helps communication.
 //
 // On one GPU the other ranks' shards are buffers in local HBM and the copy
-// role stands in for their transfer: a copy task moves one chunk (one tile
-// row of A: TM rows x K) into the gathered A, stores it write-through, and
-// publishes the chunk's arrival flag once the stores have drained.  A compute
+// role stands in for their transfer: a copy task moves one part of a chunk
+// (one tile row of A: TM rows x K) into the gathered A and stores it
+// write-through; once its stores have drained it counts the part into the
+// chunk's counter, and the task whose count completes the chunk publishes
+// the chunk's arrival flag.  One copy task moves at most 64 KiB: a single
+// workgroup keeps only so many bytes in flight, and a chunk shared by many
+// copiers arrives sooner (and a waiting compute workgroup helps in short
+// steps).  A compute
 // task is one block of TPB adjacent tiles of one tile row; tiles of this
 // rank's own rows read the local shard at once, the others read the gathered
 // A once their chunk's flag carries the launch's epoch.  Claims: copy tasks
-// take the other ranks' chunks first (rank, then row), this rank's own last;
+// take the other ranks' chunks first (rank, then row), this rank's own last,
+// the parts of a chunk one after another;
 // compute blocks go in row order, so this rank's rows come first and the
 // others follow in the order they are copied.  With column bands (one per
 // XCD, workgroup w on XCD w mod 8) each band is its own row-order queue:
@@ -39,7 +45,7 @@ enum AgRole : int { kAgCompute = 0, kAgCopy = 1, kAgExit = 2 };
 
 struct AgDecision {
     int role;
-    uint32_t unit;      // compute: block; copy: chunk
+    uint32_t unit;      // compute: block; copy: copy task (chunk * parts + part)
     uint32_t ns_seen;   // copy target the task was taken under | kHelp (copy by a waiting compute workgroup)
 };
 
@@ -53,9 +59,13 @@ struct AgSched {
     int last_role;
 };
 
-__device__ __forceinline__ uint32_t ag_copy_chunk(const AgArgs &a, uint32_t q) {
+// copy task of the q-th copy claim: chunks in copy order (the other ranks'
+// first), the parts of each in order
+__device__ __forceinline__ uint32_t ag_copy_task(const AgArgs &a, uint32_t q) {
+    const uint32_t k = q / a.parts, part = q % a.parts;
     const uint32_t peer_chunks = a.Ch - a.cps;
-    return q < peer_chunks ? a.cps + q : q - peer_chunks;
+    const uint32_t c = k < peer_chunks ? a.cps + k : k - peer_chunks;
+    return c * a.parts + part;
 }
 
 // the input rows of tile row `row` are there: this rank's own from the start,
@@ -117,9 +127,9 @@ __device__ AgDecision ag_next(const AgArgs &a, Live *L, uint32_t wg, AgSched &s)
         const uint32_t ns = (uint32_t)a.ns_init;
         if (wg < ns) {
             const uint32_t q = wg + s.det_i * ns;
-            if (q >= a.Ch) return {kAgExit, 0, ns};
+            if (q >= a.Q) return {kAgExit, 0, ns};
             ++s.det_i;
-            return {kAgCopy, ag_copy_chunk(a, q), ns};
+            return {kAgCopy, ag_copy_task(a, q), ns};
         }
         const uint32_t j = (wg - ns) + s.det_i * (B - ns);
         if (j >= a.TB) return {kAgExit, 0, ns};
@@ -138,7 +148,7 @@ __device__ AgDecision ag_next(const AgArgs &a, Live *L, uint32_t wg, AgSched &s)
             // waiting for its input: help the copy role meanwhile
             if (a.mode == kAdaptive && a.help && !s.copy_exhausted) {
                 const uint32_t q = add_relaxed(&L->compute_claim[1].v, 1u);
-                if (q < a.Ch) return {kAgCopy, ag_copy_chunk(a, q), ns | kHelp};
+                if (q < a.Q) return {kAgCopy, ag_copy_task(a, q), ns | kHelp};
                 s.copy_exhausted = true;
             }
             if (!ag_wait(a, L, row)) return {kAgExit, 0, ns};
@@ -148,7 +158,7 @@ __device__ AgDecision ag_next(const AgArgs &a, Live *L, uint32_t wg, AgSched &s)
         const bool copy_role = wg < ns;
         if (copy_role && !s.copy_exhausted) {
             const uint32_t q = add_relaxed(&L->compute_claim[1].v, 1u);
-            if (q < a.Ch) return {kAgCopy, ag_copy_chunk(a, q), ns};
+            if (q < a.Q) return {kAgCopy, ag_copy_task(a, q), ns};
             s.copy_exhausted = true;
         }
         // static copiers leave once every chunk is claimed
@@ -169,26 +179,29 @@ __device__ AgDecision ag_next(const AgArgs &a, Live *L, uint32_t wg, AgSched &s)
         // controller's target is B once no compute remains; logged as such)
         if (a.mode == kAdaptive && !s.copy_exhausted) {
             const uint32_t q = add_relaxed(&L->compute_claim[1].v, 1u);
-            if (q < a.Ch) return {kAgCopy, ag_copy_chunk(a, q), copy_role ? ns : B};
+            if (q < a.Q) return {kAgCopy, ag_copy_task(a, q), copy_role ? ns : B};
             s.copy_exhausted = true;
         }
         return {kAgExit, 0, ns};
     }
 }
 
-// one chunk: TM rows x K of a shard into the gathered A.  Source read once
-// (nt); destination written through (nt sc1), visible at device scope once
-// the stores have drained.
+// one copy task: part `u mod parts` of chunk `u / parts` (TM rows x K of a
+// shard) into the gathered A.  Source read once (nt); destination written
+// through (nt sc1), visible at device scope once the stores have drained.
 template <int NT, int TM>
-__device__ __forceinline__ void ag_copy(const AgArgs &a, uint32_t c) {
+__device__ __forceinline__ void ag_copy(const AgArgs &a, uint32_t u) {
+    const uint32_t c = u / a.parts, part = u % a.parts;
     const uint32_t r = c / a.cps, lr = c % a.cps;
     const uint16_t *src = r == 0 ? a.A_local + (int64_t)lr * TM * a.K
                                  : a.A_peers + ((int64_t)(r - 1) * a.Ms + (int64_t)lr * TM) * a.K;
     uint16_t *dst = a.A_gath + (int64_t)c * TM * a.K;
-    const auto rs = scalar_rsrc(src);
-    const auto rd = scalar_rsrc(dst);
-    const uint32_t n16 = (uint32_t)(TM * a.K / 8);   // 16-byte pieces of the chunk
-    constexpr int U = 8;
+    const uint64_t n16c = (uint64_t)TM * (uint64_t)a.K / 8;   // 16-byte pieces of the chunk
+    const uint32_t i0 = (uint32_t)(n16c * part / a.parts);
+    const uint32_t n16 = (uint32_t)(n16c * (part + 1) / a.parts) - i0;
+    const auto rs = scalar_rsrc(src + (int64_t)i0 * 8);
+    const auto rd = scalar_rsrc(dst + (int64_t)i0 * 8);
+    constexpr int U = NT >= 512 ? 8 : 16;   // 64 KiB in flight per workgroup
     uint32_t i = threadIdx.x;
     for (; i + (U - 1) * NT < n16; i += U * NT) {
         u32x4 v[U];
@@ -265,41 +278,53 @@ void allgather_gemm_kernel(AgArgs a) {
         if (tid == 0) {
             const uint32_t t_end = (uint32_t)ticks_now();
             const uint64_t dt = cycles_now() - sh_c0;
-            if (d.role == kAgCopy) {
-                const uint32_t c = d.unit;
-                if ((int64_t)c != a.skip_publish) st_relaxed(&a.ws.chunk_flag[c], a.epoch);
-                const uint32_t old = add_relaxed(&a.ws.chunk_cnt[c], 1u);
-                if (old != a.calls - 1) note_violation(L);
-                a.ws.rowner[c] = (d.ns_seen << 16) | wg;
-                a.ws.timeline[2u * a.Tcap + c] = (uint32_t)sh_r0;
-                a.ws.timeline[3u * a.Tcap + c] = t_end;
-                add_relaxed(&L->chunks_released.v, 1u);
+            // every returning atomic and load of the task's bookkeeping is
+            // issued before the first result is used: one round trip
+            const bool copying = d.role == kAgCopy;
+            const uint32_t u = d.unit, c = copying ? u / a.parts : 0u;
+            uint32_t old0 = 0, old1 = 0;
+            if (copying) {
+                old0 = add_relaxed(&a.ws.chunk_cnt[c], 1u);
             } else {
+                old0 = add_relaxed(&a.ws.tile_cnt[t0], 1u);
+                if (nt > 1) old1 = add_relaxed(&a.ws.tile_cnt[t0 + 1], 1u);
+            }
+            // progress words, and one controller step: the copy role is the
+            // communication role s (copy tasks), compute is p (tiles)
+            const uint64_t inc = (dt << kCountBits) | (copying ? 1u : nt);
+            const uint64_t mine = add_relaxed(copying ? &L->role_reduce.v : &L->role_compute.v, inc) + inc;
+            const uint64_t other = ld_relaxed(copying ? &L->role_compute.v : &L->role_reduce.v);
+            const uint32_t raw = a.mode == kAdaptive ? ld_relaxed(&L->target_ns.v) : 0u;
+            if (copying) {
+                // this part's stores drained before its count: the task
+                // whose count completes the chunk sees every part landed
+                const uint32_t base = (a.calls - 1) * a.parts;
+                if (old0 < base || old0 >= base + a.parts) note_violation(L);
+                if (old0 + 1 == base + a.parts) {
+                    a.ws.chunk_release[c] = (uint32_t)ticks_now();
+                    if ((int64_t)c != a.skip_publish) st_relaxed(&a.ws.chunk_flag[c], a.epoch);
+                    add_relaxed(&L->chunks_released.v, 1u);
+                }
+                a.ws.rowner[u] = (d.ns_seen << 16) | wg;
+                a.ws.timeline[2u * a.Tcap + u] = (uint32_t)sh_r0;
+                a.ws.timeline[3u * a.Tcap + u] = t_end;
+                min_relaxed(&L->r_start, (uint64_t)sh_r0);
+                max_relaxed(&L->r_end, ticks_now());
+            } else {
+                static_assert(TPB <= 2, "bookkeeping issues at most two tile counts");
+                if (old0 != a.calls - 1 || (nt > 1 && old1 != a.calls - 1)) note_violation(L);
                 for (uint32_t k = 0; k < nt; ++k) {
                     const uint32_t t = t0 + k;
-                    const uint32_t old = add_relaxed(&a.ws.tile_cnt[t], 1u);
-                    if (old != a.calls - 1) note_violation(L);
                     a.ws.cowner[t] = (d.ns_seen << 16) | wg;
                     a.ws.timeline[t] = (uint32_t)sh_r0;
                     a.ws.timeline[a.Tcap + t] = t_end;
                 }
             }
-            // progress words, and one controller step: the copy role is the
-            // communication role s (chunks), compute is p (tiles)
-            const bool copying = d.role == kAgCopy;
-            const uint64_t inc = (dt << kCountBits) | (copying ? 1u : nt);
-            const uint64_t mine = add_relaxed(copying ? &L->role_reduce.v : &L->role_compute.v, inc) + inc;
-            const uint64_t other = ld_relaxed(copying ? &L->role_compute.v : &L->role_reduce.v);
-            if (copying) {
-                min_relaxed(&L->r_start, (uint64_t)sh_r0);
-                max_relaxed(&L->r_end, ticks_now());
-            }
             if (a.mode == kAdaptive) {
                 const uint64_t cw = copying ? other : mine, sw = copying ? mine : other;
-                const uint32_t raw = ld_relaxed(&L->target_ns.v);
                 const uint32_t cur = raw ? raw : (uint32_t)a.ns_init;
                 const uint32_t n = controller_update_totals(
-                    (uint32_t)a.nwg, a.T, a.Ch, (uint32_t)(cw & kCountMask), (uint32_t)(sw & kCountMask),
+                    (uint32_t)a.nwg, a.T, a.Q, (uint32_t)(cw & kCountMask), (uint32_t)(sw & kCountMask),
                     cw >> kCountBits, sw >> kCountBits, cur, (uint32_t)a.ns_floor, 1u, (uint32_t)a.ns_cap);
                 if (n != cur || raw == 0) {
                     st_relaxed(&L->target_ns.v, n);

@@ -8,6 +8,8 @@ namespace mk {
 // other ranks' shards A_peers [P, Ms, K] (rank 1 first), the gathered A
 // [R Ms, K] (output, shards stacked by rank) and C = gathered . B [R Ms, N].
 // A chunk is one tile row of A (TM rows); chunk c holds rows [c TM, (c+1) TM).
+// Its bytes are moved by `parts` copy tasks; task u = c parts + p moves the
+// p-th of `parts` near-equal runs of the chunk's 16-byte pieces.
 struct AgArgs {
     const uint16_t *A_local;
     const uint16_t *A_peers;
@@ -18,6 +20,8 @@ struct AgArgs {
     int32_t P;
     uint32_t cps;             // chunks per shard (Ms / TM)
     uint32_t Ch;              // chunks: R cps
+    uint32_t parts;           // copy tasks per chunk (consecutive pieces of its bytes)
+    uint32_t Q;               // copy tasks: Ch parts
     uint32_t tiles_n, bn;     // tiles per tile row, compute blocks per tile row
     uint32_t bands;           // column bands of the compute claims (1: one row-major queue)
     uint32_t T, TB;           // tiles, compute blocks

@@ -636,6 +636,16 @@ int run_allgather(bool fused, const void *A_local, const void *A_peers, int num_
     a.bn = (uint32_t)((tiles_n + tpb - 1) / tpb);
     a.T = (uint32_t)T;
     a.TB = a.Ch * a.bn;
+    // a copy task moves at most 64 KiB of a chunk: ceil(chunk bytes / 64 KiB)
+    // parts, at least 1, at most min(tiles_n, 64) (so copy tasks <= tiles)
+    {
+        int64_t parts = (2 * (int64_t)tile_m * K + 65535) / 65536;
+        if (parts > tiles_n) parts = tiles_n;
+        if (parts > 64) parts = 64;
+        if (parts < 1) parts = 1;
+        a.parts = (uint32_t)parts;
+        a.Q = a.Ch * a.parts;
+    }
     // compute claims in column bands, one per XCD, when workgroups map to
     // XCDs round-robin and every band gets a block column
     {
@@ -682,16 +692,21 @@ int run_allgather(bool fused, const void *A_local, const void *A_peers, int num_
     if (cap > nwg - 1) cap = nwg - 1;
     if (cap < 1) cap = 1;
     if (set.mode == MK_PART_ADAPTIVE) {
-        // default start: the controller's floor; compute workgroups whose
-        // input has not arrived copy meanwhile, so a low start idles nobody
-        if (ns_init == 0) ns_init = set.floor;
+        // default start: the cap.  Communication feeds compute here, and the
+        // analysis page's section 2.4 lets the data dependency decide the
+        // initial split: rows must arrive before they are computed, so the
+        // copy role starts at its largest and the controller shrinks it once
+        // both roles have measured costs
+        if (ns_init == 0) ns_init = cap;
         if (ns_init > cap) ns_init = cap;
         if (ns_init < 1) ns_init = 1;
     }
     rc = ensure_workspace(dev.heap, a.T, a.Ch, s);
     if (rc) return rc;
     Workspace &d = dev.heap;
-    rc = prepare_launch(d, a.T, 0x80000000u | a.Ch, s);
+    // counters restart when the tile grid, the chunk count or the copy
+    // tasks per chunk change (chunk_cnt grows by `parts` per call)
+    rc = prepare_launch(d, a.T, 0x80000000u | ((a.parts - 1u) << 24) | a.Ch, s);
     if (rc) return rc;
     a.Tcap = d.Tcap;
     a.epoch = d.epoch;
@@ -719,7 +734,7 @@ int run_allgather(bool fused, const void *A_local, const void *A_peers, int num_
     d.last.nwg = (uint32_t)nwg;
     d.last.T = a.T;
     d.last.Ch = a.Ch;
-    d.last.tpc = 0;
+    d.last.tpc = a.parts;   // reported as copy tasks per chunk
     d.last.tm = (uint32_t)tile_m;
     d.last.tn = (uint32_t)tile_n;
     d.last.mode = (uint32_t)set.mode;

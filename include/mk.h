@@ -194,12 +194,16 @@ int mk_gemm_reduce_scatter_unfused(const void *A, const void *B, const float *pe
  * rank is rank 0 of R = num_peers + 1; after the call
  *     A_gathered[r*Ms + i][k] = (r == 0 ? A_local[i][k] : A_peers[r-1][i][k])
  *     C[i][j] = sum_k A_gathered[i][k] * B[k][j]        for i < R*Ms.
- * Workgroups take a copy role (one chunk: tile_m rows of a shard into
- * A_gathered, written through, then the chunk's arrival flag) or a compute
- * role (one block of adjacent tiles of one tile row, taken once its chunk
- * has arrived; this rank's own rows read A_local directly).  Copy claims take
- * the other ranks' chunks first (rank, then row), this rank's own last;
- * compute claims go in row order, so local rows come first.
+ * Workgroups take a copy role or a compute role.  A chunk (tile_m rows of a
+ * shard) is moved by P_c = min(ceil(2 tile_m K / 64 KiB), tiles per row, 64)
+ * copy tasks, each a run of its bytes written through into A_gathered; the
+ * task that completes the chunk's count sets its arrival flag.  A compute
+ * task is one block of adjacent tiles of one tile row, taken once its chunk
+ * has arrived (this rank's own rows read A_local directly).  Copy claims take
+ * the other ranks' chunks first (rank, then row), this rank's own last, the
+ * parts of a chunk in order; compute claims go in row order, so local rows
+ * come first, in one queue per XCD column band when the block columns allow
+ * (mk_set_xcd_bands).
  *
  *   A_local    bfloat16 [Ms, K], row-major (device, read only).
  *   A_peers    bfloat16 [num_peers, Ms, K], contiguous, rank 1 first (device,
@@ -213,18 +217,21 @@ int mk_gemm_reduce_scatter_unfused(const void *A, const void *B, const float *pe
  *   tile_m, tile_n   64x64, 128x128 or 256x128.
  * Pointers 16-byte aligned; A_gathered and C must not overlap each other or
  * any input (MK_ERR_INVALID_ARG).  Partition (mk_set_partition): the count is
- * the copy role's; adaptive starts at the controller floor unless set (0),
- * and its cap is B - 1 unless mk_set_controller_cap sets one; static copiers
+ * the copy role's; adaptive starts at the cap unless set (0: communication
+ * feeds compute, so the data dependency sets a copy-heavy start), and the
+ * cap is B - 1 unless mk_set_controller_cap sets one; static copiers
  * leave once every chunk is claimed; the deterministic schedule deals copy
  * tasks (in copy order) round-robin to workgroups [0, n) and compute blocks
  * (row-major) to [n, B).  mk_set_adaptive_help(0) makes a waiting compute
  * workgroup wait instead of copying.  mk_get_stats reports kind 2, with
- * num_chunks = R*Ms/tile_m chunks, compute_tasks = tiles computed,
- * reduce_tasks = chunks_released = chunks copied, and in the maps:
- * chunk_flag = arrival flags, chunk_cnt = copies per chunk,
- * tile_reduce_cnt = computations per tile, compute_owner per tile,
- * reduce_owner[c] = the owner of chunk c's copy (bit 31: copied by a compute
- * workgroup waiting for input), reduce_start/end[c] = that copy's span.
+ * num_chunks = R*Ms/tile_m chunks, tiles_per_chunk = P_c (copy tasks per
+ * chunk), compute_tasks = tiles computed, reduce_tasks = copy tasks run,
+ * chunks_released = chunks arrived, xcd_bands = compute-claim bands, and in
+ * the maps: chunk_flag = arrival flags, chunk_cnt = copy tasks per chunk
+ * (P_c per call), tile_reduce_cnt = computations per tile, compute_owner per
+ * tile, reduce_owner[c*P_c + p] = the owner of chunk c's copy task p (bit
+ * 31: run by a compute workgroup waiting for input), reduce_start/end[same
+ * index] = that task's span, chunk_release[c] = when chunk c arrived.
  * Errors as for mk_gemm_reduce_local; MK_ERR_SHAPE also when Ms is not a
  * multiple of tile_m.
  */

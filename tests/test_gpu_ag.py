@@ -66,16 +66,20 @@ def ag_protocol(st, w, mode, n):
     T = Ch * tiles_n
     assert st["kind"] == 2 and st["num_tiles"] == T and st["num_chunks"] == Ch
     assert st["status"] == 0, st["status_name"]
-    assert st["compute_tasks"] == T and st["reduce_tasks"] == Ch and st["chunks_released"] == Ch
+    parts = oracle.ag_parts_per_chunk(w.tile_m, w.K, tiles_n)
+    assert st["tiles_per_chunk"] == parts          # reported as copy tasks per chunk
+    Q = Ch * parts
+    assert st["compute_tasks"] == T and st["reduce_tasks"] == Q and st["chunks_released"] == Ch
     tpt = oracle.tiles_per_task(w.tile_m, w.tile_n)
     assert st["tiles_per_task"] == tpt
     maps = {"chunk_flag": st["chunk_flag"], "chunk_copy_cnt": st["chunk_cnt"],
-            "tile_compute_cnt": st["tile_reduce_cnt"], "copy_owner": st["reduce_owner"][:Ch],
+            "tile_compute_cnt": st["tile_reduce_cnt"], "copy_owner": st["reduce_owner"][:Q],
             "compute_owner": st["compute_owner"]}
     bad = oracle.ag_check_state(maps, R, cps, tiles_n, st["epoch"], st["calls_since_reset"],
                                 st["num_wg"], mode, n if mode != "adaptive" else st["n_reduce_initial"],
-                                tpt)
+                                tpt, parts)
     assert not bad, bad
+    return Q
 
 
 def check_ag(g, C, a0, ap, b):
@@ -96,6 +100,8 @@ AG_SHAPES = [
     (5, 384, 1024, 512, 128, 128),      # K a whole number of slabs: the fast K loop
     (3, 128, 256, 1000, 64, 64),        # 16 block columns (ragged last tile): 8 bands of 2
     (4, 256, 512, 2600, 128, 128),      # 11 block columns, the last ragged: bands of 2 and 1
+    (3, 256, 1784, 1024, 128, 128),     # 446 KiB chunks: 7 copy parts of unequal length
+    (2, 512, 4104, 512, 256, 128),      # 2 MiB chunks, parts capped at tiles_n = 4
 ]
 
 
@@ -137,16 +143,15 @@ def test_allgather_waiting_compute_helps_copy(mk):
     try:
         g, C, st = run_ag(mk, True, w, a0, ap, b, "adaptive", 1)
         check_ag(g, C, a0, ap, b)
-        ag_protocol(st, w, "adaptive", 1)
-        Ch = (w.peers + 1) * (w.M // w.tile_m)
-        helped = int((st["reduce_owner"][:Ch] >> 31).sum())
-        print(f"[gpu] ag help: {helped} of {Ch} chunks copied by waiting compute workgroups", flush=True)
+        Q = ag_protocol(st, w, "adaptive", 1)
+        helped = int((st["reduce_owner"][:Q] >> 31).sum())
+        print(f"[gpu] ag help: {helped} of {Q} copy tasks run by waiting compute workgroups", flush=True)
         assert helped > 0
         mk.set_adaptive_help(False)
         g, C, st = run_ag(mk, True, w, a0, ap, b, "adaptive", 1)
         check_ag(g, C, a0, ap, b)
-        ag_protocol(st, w, "adaptive", 1)
-        assert not np.any(st["reduce_owner"][:Ch] >> 31)
+        Q = ag_protocol(st, w, "adaptive", 1)
+        assert not np.any(st["reduce_owner"][:Q] >> 31)
     finally:
         mk.set_adaptive_help(True)
         mk.set_controller_floor(2)
@@ -220,3 +225,18 @@ def test_allgather_column_bands_change_no_result(mk, shape):
                 assert np.array_equal(g, base[0]) and np.array_equal(C, base[1])
     finally:
         mk.set_xcd_bands(0)
+
+
+def test_allgather_same_grid_different_parts(mk):
+    """Two shapes with the same tile grid and chunk count (T = 16, 4 chunks)
+    but 4 and 1 copy tasks per chunk, alternated: the per-chunk counters
+    restart with the part count, so every launch completes and matches its
+    closed form."""
+    shapes = [(2, 512, 4104, 512, 256, 128), (4, 64, 256, 256, 64, 64)]
+    for i in range(4):
+        R, Ms, K, N, tm, tn = shapes[i % 2]
+        w = wl.custom(Ms, N, K, R - 1, tm, tn, 1, wid=850 + i % 2)
+        a0, ap, b = wl.make_ag_inputs(w)
+        g, C, st = run_ag(mk, True, w, a0, ap, b, "static", 2)
+        check_ag(g, C, a0, ap, b)
+        ag_protocol(st, w, "static", 2)
