@@ -50,6 +50,15 @@ What it computes, and from which passage:
   read in the direction this kernel's data flows), which its owner word
   marks.
 
+* `ring_attention` / `ring_attention_at` and the `ra_*` protocol forms -- one
+  rank's share of Ring Attention (Ring Attention row of the MarkTechPost
+  page's five-kernel table: sequence-parallel attention, each step passes a
+  KV chunk around the ring while the local FlashAttention consumes the chunk
+  received before; compute and ring send/receive run together in one
+  persistent kernel.  "【学习】mKernel 分析" section 2.6, Table 3: 128-row KV
+  tiles).  The result is the definition of attention over every rank's keys,
+  in float64; the readings are written at that section below.
+
 Parity pins (tests/test_oracle.py) tie each function to something other than
 itself: hand-worked fixtures, closed forms (A = 0, no peers, B = I, all-ones,
 rank-1), an independent C brute force on tiny shapes, the controller's
@@ -623,6 +632,185 @@ def ag_check_state(maps: Dict[str, np.ndarray], ranks: int, chunks_per_shard: in
     if np.any(po_wg < po_ns):
         i = int(np.nonzero(po_wg < po_ns)[0][0])
         bad.append(f"tile {i} computed by workgroup {int(po_wg[i])} while the copy target was {int(po_ns[i])}")
+    if mode in ("static", "deterministic"):
+        if np.any(co_ns != n_copy) or np.any(po_ns != n_copy):
+            bad.append("static partition changed during the launch")
+    return bad
+
+
+# ---------------------------------------------------------------------------
+# Ring Attention, one rank's share
+# ---------------------------------------------------------------------------
+#
+# Ring Attention row of the MarkTechPost page's five-kernel table: attention
+# over a sequence split across ranks; at each step every rank passes the KV
+# chunk it holds to the next rank while its local FlashAttention consumes the
+# chunk it received before, both inside one persistent kernel.
+# "【学习】mKernel 分析" section 2.6, Table 3: sequence parallelism, the
+# step's compute and transfer are independent, KV moves in 128-row tiles.
+#
+# The readings used (the pages fix neither masking nor layout):
+# - R ranks hold S consecutive tokens each; this is rank 0.  Q, K and V are
+#   [S, H, D] (token, head, head dimension), bfloat16.  The ring brings the
+#   other ranks' K and V one step at a time; peers[s - 1] is the KV chunk
+#   that arrives at step s (s = 1 .. R - 1).  Step 0 uses the local K, V.
+# - Attention is not causal: every query attends to all R S keys, so the
+#   result does not depend on the ring order.  Scale 1 / sqrt(D).
+# - Outputs: O [S, H, D] and the log-sum-exp LSE [H, S] (natural log) of
+#   each query's scaled scores, the quantity a ring step passes on to merge
+#   partial results.
+# - A KV tile is 128 tokens of one step's K and V, all heads; its arrival
+#   flag gates every read of it.  A copy task moves at most 64 KiB of one
+#   tile (K and V together); the task whose count completes the tile sets
+#   its flag.  A compute task is 128 queries of one head over every key.
+
+
+def _scores_scale(D: int) -> float:
+    return 1.0 / np.sqrt(float(D))
+
+
+def ring_attention(q_bits: np.ndarray, k_local_bits: np.ndarray, v_local_bits: np.ndarray,
+                   k_peers_bits: np.ndarray, v_peers_bits: np.ndarray,
+                   row_block: int = 256) -> Tuple[np.ndarray, np.ndarray]:
+    """Rank 0's share of Ring Attention, in float64 on the exact bfloat16
+    values.  q, k_local, v_local [S, H, D]; k_peers, v_peers [R-1, S, H, D]
+    (arrival order).  Returns (O [S, H, D], LSE [H, S]):
+        s_ij = (q_i . k_j) / sqrt(D) over all R S keys j,
+        O_i = sum_j exp(s_ij) v_j / sum_j exp(s_ij),   LSE_i = log sum_j exp(s_ij)."""
+    q = np.asarray(q_bits, dtype=np.uint16)
+    kl = np.asarray(k_local_bits, dtype=np.uint16)
+    vl = np.asarray(v_local_bits, dtype=np.uint16)
+    kp = np.asarray(k_peers_bits, dtype=np.uint16)
+    vp = np.asarray(v_peers_bits, dtype=np.uint16)
+    if q.ndim != 3 or kl.shape != q.shape or vl.shape != q.shape:
+        raise ValueError("q, k_local, v_local must all be [S, H, D]")
+    if kp.ndim != 4 or kp.shape != vp.shape or kp.shape[1:] != q.shape:
+        raise ValueError("k_peers, v_peers must be [R-1, S, H, D]")
+    S, H, D = q.shape
+    K = bf16_bits_to_f64(np.concatenate([kl[None], kp], axis=0).reshape(-1, H, D))
+    V = bf16_bits_to_f64(np.concatenate([vl[None], vp], axis=0).reshape(-1, H, D))
+    Q = bf16_bits_to_f64(q)
+    O = np.zeros((S, H, D), dtype=np.float64)
+    L = np.zeros((H, S), dtype=np.float64)
+    sc = _scores_scale(D)
+    for h in range(H):
+        Kh, Vh = K[:, h, :], V[:, h, :]
+        for i0 in range(0, S, row_block):
+            s_ = (Q[i0:i0 + row_block, h, :] @ Kh.T) * sc
+            m = s_.max(axis=1, keepdims=True)
+            w = np.exp(s_ - m)
+            l = w.sum(axis=1, keepdims=True)
+            O[i0:i0 + row_block, h, :] = (w @ Vh) / l
+            L[h, i0:i0 + row_block] = (m + np.log(l))[:, 0]
+    return O, L
+
+
+def ring_attention_at(q_bits, k_local_bits, v_local_bits, k_peers_bits, v_peers_bits,
+                      rows: Sequence[int], heads: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+    """The same definition for the sampled queries (rows[n], heads[n]) only:
+    returns (O [n, D], LSE [n]).  For full-size checks."""
+    q = np.asarray(q_bits, dtype=np.uint16)
+    S, H, D = q.shape
+    kl, vl = np.asarray(k_local_bits), np.asarray(v_local_bits)
+    kp, vp = np.asarray(k_peers_bits), np.asarray(v_peers_bits)
+    rows = np.asarray(rows, dtype=np.int64)
+    heads = np.asarray(heads, dtype=np.int64)
+    O = np.zeros((rows.size, D), dtype=np.float64)
+    L = np.zeros(rows.size, dtype=np.float64)
+    sc = _scores_scale(D)
+    for h in np.unique(heads):
+        Kh = bf16_bits_to_f64(np.concatenate([kl[None, :, h, :], kp[:, :, h, :]], axis=0).reshape(-1, D))
+        Vh = bf16_bits_to_f64(np.concatenate([vl[None, :, h, :], vp[:, :, h, :]], axis=0).reshape(-1, D))
+        sel = np.nonzero(heads == h)[0]
+        s_ = (bf16_bits_to_f64(q[rows[sel], h, :]) @ Kh.T) * sc
+        m = s_.max(axis=1, keepdims=True)
+        w = np.exp(s_ - m)
+        l = w.sum(axis=1, keepdims=True)
+        O[sel] = (w @ Vh) / l
+        L[sel] = (m + np.log(l))[:, 0]
+    return O, L
+
+
+def ra_kv_tiles(S: int, kv_rows: int = 128) -> int:
+    """KV tiles of one step: ceil(S / 128) (the last one ragged)."""
+    return -(-S // kv_rows)
+
+
+def ra_parts_per_tile(H: int, D: int, kv_rows: int = 128) -> int:
+    """Copy tasks one KV tile is split into: ceil(2 (K and V) x 128 H D x 2
+    bytes / 64 KiB), at least 1 and at most 64."""
+    parts = -(-(2 * kv_rows * H * D * 2) // 65536)
+    return int(max(1, min(parts, 64)))
+
+
+def ra_expected_state(n_tiles: int, n_tasks: int, epoch: int, calls: int,
+                      parts: int = 1) -> Dict[str, np.ndarray]:
+    """Integer state after `calls` complete launches of one shape: every
+    arriving KV tile's flag holds the last epoch, each of its `parts` copy
+    tasks ran and every compute task ran exactly once per call."""
+    return {
+        "tile_flag": np.full(n_tiles, epoch, dtype=np.int64),
+        "tile_copy_cnt": np.full(n_tiles, parts * calls, dtype=np.int64),
+        "task_compute_cnt": np.full(n_tasks, calls, dtype=np.int64),
+    }
+
+
+def ra_deterministic_owners(n_tiles: int, n_tasks: int, B: int, n_copy: int,
+                            parts: int = 1) -> Tuple[np.ndarray, np.ndarray]:
+    """Owner maps of the deterministic static schedule: copy task i (tiles in
+    arrival order, step by step, the parts of each in order; index
+    tile * parts + part) goes to workgroup i mod n_copy, compute task j
+    (head-major: j = head * query blocks + block) to n_copy + j mod
+    (B - n_copy)."""
+    i = np.arange(n_tiles * parts, dtype=np.int64)
+    j = np.arange(n_tasks, dtype=np.int64)
+    return i % n_copy, n_copy + j % (B - n_copy)
+
+
+def ra_check_state(maps: Dict[str, np.ndarray], n_tiles: int, n_tasks: int, epoch: int, calls: int,
+                   B: int, mode: str, n_copy: int, parts: int = 1) -> List[str]:
+    """Compare a Ring Attention launch's protocol state with its closed form.
+    Owner words are (mark << 31) | (copy target seen << 16) | workgroup; a
+    copy task run by a workgroup at or above the copy target is legal only
+    with the mark (a compute workgroup waiting for a tile helped), only in
+    adaptive mode; a compute task never carries the mark and needs an index
+    at or above the target."""
+    bad: List[str] = []
+    for key, want in ra_expected_state(n_tiles, n_tasks, epoch, calls, parts).items():
+        got = np.asarray(maps[key], dtype=np.int64)
+        if got.shape != want.shape:
+            bad.append(f"{key}: shape {got.shape} != {want.shape}")
+            continue
+        idx = np.nonzero(got != want)[0]
+        if idx.size:
+            i = int(idx[0])
+            bad.append(f"{key}[{i}] = {int(got[i])}, expected {int(want[i])} ({idx.size} mismatches)")
+    co = np.asarray(maps["copy_owner"], dtype=np.int64)
+    po = np.asarray(maps["compute_owner"], dtype=np.int64)
+    if co.shape != (n_tiles * parts,) or po.shape != (n_tasks,):
+        return bad + [f"owner maps: shapes {co.shape}, {po.shape}"]
+    co_wg, co_ns, co_help = co & OWNER_WG_MASK, (co >> 16) & OWNER_NS_MASK, (co & OWNER_HELP) != 0
+    po_wg, po_ns, po_mark = po & OWNER_WG_MASK, (po >> 16) & OWNER_NS_MASK, (po & OWNER_HELP) != 0
+    if np.any(co_wg >= B) or np.any(po_wg >= B):
+        bad.append("owner outside [0, B)")
+    if mode == "deterministic":
+        dc, dp = ra_deterministic_owners(n_tiles, n_tasks, B, n_copy, parts)
+        if not np.array_equal(co_wg, dc):
+            i = int(np.nonzero(co_wg != dc)[0][0])
+            bad.append(f"copy_owner[{i}] = {int(co_wg[i])}, expected {int(dc[i])}")
+        if not np.array_equal(po_wg, dp):
+            i = int(np.nonzero(po_wg != dp)[0][0])
+            bad.append(f"compute_owner[{i}] = {int(po_wg[i])}, expected {int(dp[i])}")
+    if np.any(po_mark):
+        bad.append(f"task {int(np.nonzero(po_mark)[0][0])}: compute owner carries the help mark")
+    if mode != "adaptive" and np.any(co_help):
+        bad.append(f"copy task {int(np.nonzero(co_help)[0][0])}: help copy outside adaptive mode")
+    if np.any((co_wg >= co_ns) & ~co_help):
+        i = int(np.nonzero((co_wg >= co_ns) & ~co_help)[0][0])
+        bad.append(f"copy task {i} run by workgroup {int(co_wg[i])} while the copy target was {int(co_ns[i])}")
+    if np.any(po_wg < po_ns):
+        i = int(np.nonzero(po_wg < po_ns)[0][0])
+        bad.append(f"task {i} computed by workgroup {int(po_wg[i])} while the copy target was {int(po_ns[i])}")
     if mode in ("static", "deterministic"):
         if np.any(co_ns != n_copy) or np.any(po_ns != n_copy):
             bad.append("static partition changed during the launch")

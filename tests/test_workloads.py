@@ -81,3 +81,24 @@ def test_named_workloads_match_their_descriptions():
     # algorithmic bytes: A + B once, peers once, C once
     tp = W["tp_share"]
     assert tp.algorithmic_bytes == 2 * 4096 * 1792 * 2 + 4 * 7 * 4096 * 4096 + 4 * 4096 * 4096
+
+
+def test_ring_attention_inputs_are_seeded_and_shaped():
+    w = wl.ra_custom(3, 130, 2, 128, wid=201)
+    a = wl.make_ra_inputs(w)
+    b = wl.make_ra_inputs(w)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+    assert a[0].shape == (130, 2, 128) and a[3].shape == (2, 130, 2, 128)
+    assert all(x.dtype == np.uint16 for x in a)
+    # every buffer its own stream: Q, K, V and each peer's K and V differ
+    flat = [a[0], a[1], a[2], a[3][0], a[4][0], a[3][1], a[4][1]]
+    assert len({x.tobytes() for x in flat}) == len(flat)
+    c = wl.make_ra_inputs(w, seed=1)
+    assert not np.array_equal(a[0], c[0])
+
+
+def test_ring_attention_workload_sizes():
+    W = wl.RA_WORKLOADS
+    assert (W["ra_sp_share"].ranks, W["ra_sp_share"].S, W["ra_sp_share"].H, W["ra_sp_share"].D) == (8, 4096, 32, 128)
+    assert W["ra_sp_share"].tasks == 1024 and W["ra_sp_share"].kv_tiles == 7 * 32
+    assert W["ra_sp_share"].flops == 4 * 4096 * 32768 * 128 * 32

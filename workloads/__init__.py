@@ -229,3 +229,85 @@ def make_ag_inputs(w: Workload, seed: int = DEFAULT_SEED):
     for p in range(P):
         a_peers[p] = round_to_bf16_bits(_draw(_rng(seed, w.wid, 2 + p), (Ms, K), w.dist_ab))
     return a_local, a_peers, b
+
+
+# ---------------------------------------------------------------------------
+# Ring Attention, one rank's share
+# ---------------------------------------------------------------------------
+# R ranks hold S consecutive tokens each; this rank's Q, K and V [S, H, D]
+# are buffers 0, 1 and 2, the K and V that arrive at ring step s (s = 1 ..
+# R - 1) are buffers 1 + 2s and 2 + 2s.  All from `dist`, rounded to
+# bfloat16.  The pages give no shapes for this kernel; the workloads take a
+# 4096-token share of a 32-head, 128-dimension attention layer (a 32k-token
+# sequence over 8 ranks) and a long-context share (64k tokens over 4 ranks,
+# 8 heads); with N(0, 1) inputs the scaled scores are N(0, 1).
+
+
+@dataclasses.dataclass(frozen=True)
+class RaWorkload:
+    name: str
+    wid: int
+    ranks: int            # R: this rank plus the R - 1 whose KV arrives around the ring
+    S: int                # tokens per rank
+    H: int                # heads
+    D: int                # head dimension
+    dist: Tuple = ("normal", 1.0)
+    mode: str = "adaptive"
+    n_copy: int = 0
+    description: str = ""
+
+    @property
+    def flops(self) -> int:
+        """Q.K^T and P.V over every (query, key, head): 4 S (R S) D H."""
+        return 4 * self.S * self.ranks * self.S * self.D * self.H
+
+    @property
+    def tasks(self) -> int:
+        return self.H * -(-self.S // 128)
+
+    @property
+    def kv_tiles(self) -> int:
+        """KV tiles that arrive (steps 1 .. R - 1)."""
+        return (self.ranks - 1) * -(-self.S // 128)
+
+
+RA_WORKLOADS = {
+    w.name: w
+    for w in [
+        RaWorkload("ra_tiny", 20, 2, 256, 2, 128, mode="static", n_copy=2,
+                   description="2 ranks x 256 tokens, 2 heads of 128"),
+        RaWorkload("ra_sp_share", 21, 8, 4096, 32, 128,
+                   description="8 ranks x 4096 tokens (32k), 32 heads of 128"),
+        RaWorkload("ra_long", 22, 4, 16384, 8, 128,
+                   description="4 ranks x 16384 tokens (64k), 8 heads of 128"),
+    ]
+}
+
+
+def ra_workload(name: str) -> RaWorkload:
+    return RA_WORKLOADS[name]
+
+
+def ra_custom(ranks, S, H, D=128, wid=200, mode="static", n_copy=2) -> RaWorkload:
+    return RaWorkload(f"ra_custom_{ranks}x{S}x{H}x{D}", wid, ranks, S, H, D, mode=mode, n_copy=n_copy)
+
+
+def make_ra_inputs(w: RaWorkload, seed: int = DEFAULT_SEED):
+    """Draw (q, k_local, v_local [S,H,D], k_peers, v_peers [R-1,S,H,D]), all
+    uint16 bfloat16 patterns; peers in ring arrival order."""
+    shape = (w.S, w.H, w.D)
+    q = round_to_bf16_bits(_draw(_rng(seed, w.wid, 0), shape, w.dist))
+    kl = round_to_bf16_bits(_draw(_rng(seed, w.wid, 1), shape, w.dist))
+    vl = round_to_bf16_bits(_draw(_rng(seed, w.wid, 2), shape, w.dist))
+    P = w.ranks - 1
+    kp = np.empty((P,) + shape, dtype=np.uint16)
+    vp = np.empty((P,) + shape, dtype=np.uint16)
+
+    def fill(s):
+        kp[s - 1] = round_to_bf16_bits(_draw(_rng(seed, w.wid, 1 + 2 * s), shape, w.dist))
+        vp[s - 1] = round_to_bf16_bits(_draw(_rng(seed, w.wid, 2 + 2 * s), shape, w.dist))
+
+    if P:
+        with _cf.ThreadPoolExecutor(min(P, 8)) as ex:
+            list(ex.map(fill, range(1, P + 1)))
+    return q, kl, vl, kp, vp
