@@ -96,6 +96,9 @@ SIGNATURES = {
                                                _vp]),
     "mk_allgather_gemm_local": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp]),
     "mk_allgather_gemm_unfused": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp]),
+    "mk_ring_attention_local": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _vp]),
+    "mk_ring_attention_unfused": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _i32,
+                                         _vp]),
     "mk_set_partition": (_i32, [_i32, _i32]),
     "mk_set_controller_floor": (_i32, [_i32]),
     "mk_set_controller_cap": (_i32, [_i32]),
@@ -254,6 +257,44 @@ def allgather_gemm_local(A_local, A_peers, A_gathered, B, C, tile_m: int, tile_n
 def allgather_gemm_unfused(A_local, A_peers, A_gathered, B, C, tile_m: int, tile_n: int, stream=None) -> None:
     """The same from two launches: gather, then GEMM (mk_allgather_gemm_unfused)."""
     _call_ag(lib.mk_allgather_gemm_unfused, A_local, A_peers, A_gathered, B, C, tile_m, tile_n, stream)
+
+
+def _call_ring(fn, q, k_local, v_local, k_peers, v_peers, k_ring, v_ring, O, lse, stream):
+    torch = _torch()
+    for name, t, dt in (("q", q, torch.bfloat16), ("k_local", k_local, torch.bfloat16),
+                        ("v_local", v_local, torch.bfloat16), ("O", O, torch.float32)):
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous() or t.dim() != 3:
+            raise ValueError(f"{name} must be a contiguous 3-D {dt} CUDA tensor [S, H, D]")
+    S, H, D = q.shape
+    if tuple(k_local.shape) != (S, H, D) or tuple(v_local.shape) != (S, H, D) or tuple(O.shape) != (S, H, D):
+        raise ValueError("q, k_local, v_local and O must all be [S, H, D]")
+    if lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous() or tuple(lse.shape) != (H, S):
+        raise ValueError("lse must be a contiguous [H, S] float32 CUDA tensor")
+    P = 0
+    if k_peers is not None:
+        P = k_peers.shape[0]
+        for name, t in (("k_peers", k_peers), ("v_peers", v_peers), ("k_ring", k_ring), ("v_ring", v_ring)):
+            if (t is None or t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous()
+                    or tuple(t.shape) != (P, S, H, D)):
+                raise ValueError(f"{name} must be a contiguous [P, S, H, D] bfloat16 CUDA tensor")
+    ptr = lambda t: t.data_ptr() if (t is not None and P > 0) else None
+    _check(fn(q.data_ptr(), k_local.data_ptr(), v_local.data_ptr(), ptr(k_peers), ptr(v_peers), P,
+              ptr(k_ring), ptr(v_ring), O.data_ptr(), lse.data_ptr(), S, H, D, _stream_handle(stream)))
+
+
+def ring_attention_local(q, k_local, v_local, k_peers, v_peers, k_ring, v_ring, O, lse, stream=None) -> None:
+    """Rank 0's share of Ring Attention in one persistent launch
+    (mk_ring_attention_local): O [S,H,D] and lse [H,S] of attention over
+    every rank's keys (no mask, scale 1/sqrt(D)); k_ring / v_ring receive the
+    arriving K and V.  k_peers / v_peers are [P,S,H,D] in arrival order, or
+    None for one rank."""
+    _call_ring(lib.mk_ring_attention_local, q, k_local, v_local, k_peers, v_peers, k_ring, v_ring, O, lse, stream)
+
+
+def ring_attention_unfused(q, k_local, v_local, k_peers, v_peers, k_ring, v_ring, O, lse, stream=None) -> None:
+    """The same from two launches: gather, then attention (mk_ring_attention_unfused)."""
+    _call_ring(lib.mk_ring_attention_unfused, q, k_local, v_local, k_peers, v_peers, k_ring, v_ring, O, lse,
+               stream)
 
 
 def set_partition(mode, n_reduce: int = 0) -> None:

@@ -12,8 +12,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmk.so")
-SOURCES = [os.path.join(CSRC, n) for n in ("mk_kernels.hip", "mk_allgather.hip", "mk_api.hip")]
-HEADERS = [os.path.join(CSRC, n) for n in ("mk_internal.hpp", "mk_device.hpp", "mk_allgather.hpp")] + [os.path.join(ROOT, "include", "mk.h")]
+SOURCES = [os.path.join(CSRC, n) for n in ("mk_kernels.hip", "mk_allgather.hip", "mk_ring.hip", "mk_api.hip")]
+HEADERS = [os.path.join(CSRC, n) for n in ("mk_internal.hpp", "mk_device.hpp", "mk_allgather.hpp", "mk_ring.hpp")] + [os.path.join(ROOT, "include", "mk.h")]
 
 # Packed fp32 instructions are switched off for all device code.  LLVM's
 # atomic optimizer is off too: every atomic here is issued by one lane, and the

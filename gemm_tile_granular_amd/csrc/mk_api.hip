@@ -8,10 +8,12 @@
 #include <mutex>
 #include <cstring>
 #include <cstdio>
+#include <cmath>
 
 #include "mk.h"
 #include "mk_internal.hpp"
 #include "mk_allgather.hpp"
+#include "mk_ring.hpp"
 
 namespace {
 
@@ -55,7 +57,7 @@ constexpr int kMaxDevices = 64;
 
 struct Launch {
     bool valid = false;
-    uint32_t kind = 0;   // 0 GEMM+AllReduce, 1 GEMM+ReduceScatter, 2 AllGather+GEMM
+    uint32_t kind = 0;   // 0 GEMM+AllReduce, 1 GEMM+ReduceScatter, 2 AllGather+GEMM, 3 Ring Attention
     uint32_t epoch = 0, calls = 0, nwg = 0, T = 0, Ch = 0, tpc = 0, tm = 0, tn = 0;
     uint32_t mode = 0, ns_init = 0;
     uint32_t local = 0, keep = 1, cap = 0, bands = 1, help = 1;
@@ -745,6 +747,152 @@ int run_allgather(bool fused, const void *A_local, const void *A_peers, int num_
     return MK_OK;
 }
 
+
+// One rank's share of Ring Attention (see mk_ring.hip).  fused: one
+// persistent launch with copy and compute roles; otherwise a gather kernel
+// then the attention kernel.
+int run_ring(bool fused, const void *q, const void *k_local, const void *v_local, const void *k_peers,
+             const void *v_peers, int num_peers, void *k_ring, void *v_ring, float *O, float *lse, int64_t S,
+             int H, int D, void *stream) {
+    if (S < 0 || H < 1) return fail(MK_ERR_INVALID_ARG, "S must be >= 0 and H >= 1");
+    if (num_peers < 0) return fail(MK_ERR_INVALID_ARG, "num_peers < 0");
+    if (D != kRaHeadDim) return fail(MK_ERR_SHAPE, "head dimension %d not supported (128)", D);
+    if (S * (int64_t)H * D * 4 >= (int64_t)INT32_MAX)
+        return fail(MK_ERR_SHAPE, "S x H x D too large for 32-bit in-buffer offsets");
+    const int64_t R = (int64_t)num_peers + 1;
+    if (S == 0) return MK_OK;
+    if (!q || !k_local || !v_local || !O || !lse) return fail(MK_ERR_INVALID_ARG, "NULL pointer");
+    if (num_peers > 0 && (!k_peers || !v_peers || !k_ring || !v_ring))
+        return fail(MK_ERR_INVALID_ARG, "peer or ring buffers NULL with num_peers > 0");
+    const void *ptrs[] = {q, k_local, v_local, k_peers, v_peers, k_ring, v_ring, O, lse};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return fail(MK_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+    const int64_t eb = S * H * D * 2, pb = (int64_t)num_peers * eb, ob = S * H * D * 4, lb = S * H * 4;
+    const void *ins[] = {q, k_local, v_local, k_peers, v_peers};
+    const int64_t inb[] = {eb, eb, eb, pb, pb};
+    const void *outs[] = {k_ring, v_ring, O, lse};
+    const int64_t outb[] = {pb, pb, ob, lb};
+    for (int i = 0; i < 4; ++i) {
+        if (!outs[i] || outb[i] == 0) continue;
+        for (int j = 0; j < 5; ++j)
+            if (ins[j] && inb[j] && overlaps(outs[i], outb[i], ins[j], inb[j]))
+                return fail(MK_ERR_INVALID_ARG, "an output overlaps an input");
+        for (int j = i + 1; j < 4; ++j)
+            if (outs[j] && outb[j] && overlaps(outs[i], outb[i], outs[j], outb[j]))
+                return fail(MK_ERR_INVALID_ARG, "outputs overlap each other");
+    }
+    const Settings set = g_set;
+    DevState *dp = nullptr;
+    int rc = device_state(&dp);
+    if (rc) return rc;
+    DevState &dev = *dp;
+    hipStream_t s = (hipStream_t)stream;
+
+    RaArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = (const uint16_t *)q;
+    a.k_local = (const uint16_t *)k_local;
+    a.v_local = (const uint16_t *)v_local;
+    a.k_peers = (const uint16_t *)k_peers;
+    a.v_peers = (const uint16_t *)v_peers;
+    a.k_ring = (uint16_t *)k_ring;
+    a.v_ring = (uint16_t *)v_ring;
+    a.O = O;
+    a.lse = lse;
+    a.S = S;
+    a.H = H;
+    a.R = (int32_t)R;
+    a.nkv = (uint32_t)((S + kRaKvRows - 1) / kRaKvRows);
+    a.nqb = (uint32_t)((S + kRaQRows - 1) / kRaQRows);
+    a.Ch = (uint32_t)(num_peers * (int64_t)a.nkv);
+    {
+        // a copy task moves at most 64 KiB of a tile (K and V together)
+        int64_t parts = (2 * (int64_t)kRaKvRows * H * D * 2 + 65535) / 65536;
+        if (parts > 64) parts = 64;
+        if (parts < 1) parts = 1;
+        a.parts = (uint32_t)parts;
+    }
+    a.Qc = a.Ch * a.parts;
+    a.NTk = (uint32_t)H * a.nqb;
+    {
+        const int want = set.xcd_bands ? set.xcd_bands : kMaxXcd;
+        a.bands = (dev.xcd_ok && H >= want) ? (uint32_t)want : 1u;
+    }
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+    const uint64_t Tmap = a.NTk > a.Qc ? a.NTk : a.Qc;
+    if (Tmap >= (uint64_t)kMaxTiles || a.Ch >= (1u << 22))
+        return fail(MK_ERR_SHAPE, "too many tasks (%llu)", (unsigned long long)Tmap);
+
+    if (!fused) {
+        hipError_t e = launch_ring_unfused(a, dev.num_cu, dev.xcd_ok, s);
+        if (e != hipSuccess) return hip_fail(e, "Ring Attention (unfused) launch");
+        return MK_OK;
+    }
+
+    const int per_cu = ring_workgroups_per_cu();
+    if (per_cu < 1) return fail(MK_ERR_HIP, "occupancy query for the Ring Attention kernel failed");
+    const int resident = dev.num_cu * per_cu;
+    const int nwg = set.num_wg ? set.num_wg : (resident < kMaxWG ? resident : kMaxWG);
+    if (nwg < 2 || nwg > resident)
+        return fail(MK_ERR_INVALID_ARG, "workgroups %d outside [2, %d resident workgroups]", nwg, resident);
+    int ns_init = set.n_reduce;
+    if (set.mode != MK_PART_ADAPTIVE && (ns_init < 1 || ns_init > nwg - 1))
+        return fail(MK_ERR_INVALID_ARG, "static copy count %d outside [1, %d]", ns_init, nwg - 1);
+    int cap = set.cap ? set.cap : nwg - 1;
+    if (cap > nwg - 1) cap = nwg - 1;
+    if (cap < 1) cap = 1;
+    // at least one copy workgroup while copy tasks remain: compute tasks wait
+    // for arriving tiles, so the copy role never empties
+    const int floor = set.floor < 1 ? 1 : set.floor;
+    if (set.mode == MK_PART_ADAPTIVE) {
+        // default start: the cap (communication feeds compute; the data
+        // dependency sets a copy-heavy start, as for AllGather+GEMM)
+        if (ns_init == 0) ns_init = cap;
+        if (ns_init > cap) ns_init = cap;
+        if (ns_init < 1) ns_init = 1;
+    }
+    const uint32_t Ch_ws = a.Ch ? a.Ch : 1u;
+    rc = ensure_workspace(dev.heap, (uint32_t)Tmap, Ch_ws, s);
+    if (rc) return rc;
+    Workspace &d = dev.heap;
+    rc = prepare_launch(d, (uint32_t)Tmap, 0xC0000000u | ((a.parts - 1u) << 24) | a.Ch, s);
+    if (rc) return rc;
+    a.Tcap = d.Tcap;
+    a.epoch = d.epoch;
+    a.calls = d.calls;
+    a.mode = set.mode;
+    a.ns_init = ns_init;
+    a.ns_floor = floor;
+    a.ns_cap = cap;
+    a.nwg = nwg;
+    a.timeout_ticks = set.timeout_us * (dev.timer_hz / 1000000ull);
+    a.skip_publish = set.skip_publish;
+    a.ws = view_of(d);
+    hipError_t e = launch_ring_attention(a, s);
+    if (e != hipSuccess) {
+        d.dirty = true;
+        return hip_fail(e, "Ring Attention launch");
+    }
+    dev.recent = &d;
+    d.last = Launch();
+    d.last.valid = true;
+    d.last.kind = 3;
+    d.last.epoch = d.epoch;
+    d.last.calls = d.calls;
+    d.last.nwg = (uint32_t)nwg;
+    d.last.T = (uint32_t)Tmap;   // length of the per-task maps
+    d.last.Ch = a.Ch;
+    d.last.tpc = a.parts;        // reported as copy tasks per KV tile
+    d.last.tm = (uint32_t)kRaQRows;
+    d.last.tn = (uint32_t)kRaKvRows;
+    d.last.mode = (uint32_t)set.mode;
+    d.last.ns_init = (uint32_t)ns_init;
+    d.last.cap = (uint32_t)cap;
+    d.last.bands = a.bands;
+    d.last.help = 0;
+    return MK_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -763,6 +911,22 @@ int mk_allgather_gemm_unfused(const void *A_local, const void *A_peers, int num_
     return run_allgather(false, A_local, A_peers, num_peers, A_gathered, B, C, Ms, N, K, tile_m, tile_n, stream);
 }
 
+
+int mk_ring_attention_local(const void *q, const void *k_local, const void *v_local, const void *k_peers,
+                            const void *v_peers, int num_peers, void *k_ring, void *v_ring, float *O, float *lse,
+                            int64_t S, int H, int D, void *stream) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    return run_ring(true, q, k_local, v_local, k_peers, v_peers, num_peers, k_ring, v_ring, O, lse, S, H, D,
+                    stream);
+}
+
+int mk_ring_attention_unfused(const void *q, const void *k_local, const void *v_local, const void *k_peers,
+                              const void *v_peers, int num_peers, void *k_ring, void *v_ring, float *O, float *lse,
+                              int64_t S, int H, int D, void *stream) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    return run_ring(false, q, k_local, v_local, k_peers, v_peers, num_peers, k_ring, v_ring, O, lse, S, H, D,
+                    stream);
+}
 
 int mk_gemm_reduce_local(const void *A, const void *B, const float *peers, int num_peers, float *C,
                          int64_t M, int64_t N, int64_t K, int tile_m, int tile_n,

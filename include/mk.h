@@ -249,6 +249,73 @@ int mk_allgather_gemm_unfused(const void *A_local, const void *A_peers, int num_
                               int tile_n, void *stream);
 
 /*
+ * mk_ring_attention_local -- one rank's share of Ring Attention in one
+ * persistent launch (Ring Attention row of the MarkTechPost page's
+ * five-kernel table: sequence-parallel attention; each step passes a KV
+ * chunk around the ring while the local FlashAttention consumes the chunk
+ * received before, compute and transfer in one persistent kernel.
+ * "【学习】mKernel 分析" section 2.6, Table 3: KV moves in 128-row tiles).
+ * This rank is rank 0 of R = num_peers + 1; each rank holds S tokens.  After
+ * the call, with keys j running over all R*S tokens (this rank's, then each
+ * arriving step's) and scale 1/sqrt(D), no causal mask:
+ *     O[i][h][:] = sum_j softmax_j(q_i . k_j * scale) v_j
+ *     lse[h][i]  = log sum_j exp(q_i . k_j * scale)          (natural log)
+ *     k_ring[s-1], v_ring[s-1] = k_peers[s-1], v_peers[s-1]  for every step s.
+ * Workgroups take a copy role or a compute role.  A KV tile is 128 tokens of
+ * one step's K and V, every head; P_t = min(ceil(2 * 128 * H * D * 2 / 64 KiB),
+ * 64) copy tasks move a tile into the ring buffers, written through, and the
+ * task that completes the tile's count sets its arrival flag.  Copy tasks go
+ * in arrival order (step 1's tiles first).  A compute task is 128 queries of
+ * one head against every key: the local K, V at once, then each arriving
+ * tile once its flag carries the launch's epoch.
+ *
+ *   q, k_local, v_local  bfloat16 [S, H, D], row-major (device, read only).
+ *   k_peers, v_peers     bfloat16 [num_peers, S, H, D], contiguous, in ring
+ *                        arrival order: index s-1 arrives at step s (device,
+ *                        read only; stands in for the other ranks' KV); NULL
+ *                        only when num_peers == 0.
+ *   k_ring, v_ring       bfloat16 [num_peers, S, H, D] (device, written: the
+ *                        rank's receive buffers); NULL only when num_peers == 0.
+ *   O                    fp32 [S, H, D] (device, written).
+ *   lse                  fp32 [H, S] (device, written).
+ *   S                    tokens per rank (any; the last tiles are ragged).
+ *   H, D                 heads (>= 1) and head dimension (128 only).
+ * Pointers 16-byte aligned; outputs must not overlap each other or any input
+ * (MK_ERR_INVALID_ARG); S*H*D*4 must stay below 2^31 (MK_ERR_SHAPE).
+ * Partition (mk_set_partition): the count is the copy role's; adaptive starts
+ * at the cap unless set, and keeps at least one copy workgroup (the floor is
+ * at least 1) while copy tasks remain; static copiers leave once every copy
+ * task is claimed; the deterministic schedule deals copy tasks in arrival
+ * order round-robin to workgroups [0, n) and compute tasks (head-major:
+ * head * ceil(S/128) + block) to [n, B).  Compute claims go in one queue per
+ * XCD band of heads (head h in band h mod 8) when H >= 8.  mk_get_stats
+ * reports kind 3, with num_tiles = the length of the per-task maps
+ * (max(compute tasks, copy tasks)), num_chunks = (R-1) ceil(S/128) arriving
+ * tiles, tiles_per_chunk = P_t, tile_m = 128 (queries per compute task),
+ * tile_n = 128 (tokens per KV tile), compute_tasks = H ceil(S/128),
+ * reduce_tasks = copy tasks run, chunks_released = tiles arrived, and in the
+ * maps: chunk_flag = arrival flags, chunk_cnt = copy tasks per tile (P_t per
+ * call), tile_reduce_cnt[j] = runs of compute task j, compute_owner[j],
+ * reduce_owner[t*P_t + p] = the owner of tile t's copy task p,
+ * compute_start/end[j], reduce_start/end[t*P_t + p], chunk_release[t] = when
+ * tile t arrived.  Errors as for mk_gemm_reduce_local.
+ */
+int mk_ring_attention_local(const void *q, const void *k_local, const void *v_local, const void *k_peers,
+                            const void *v_peers, int num_peers, void *k_ring, void *v_ring, float *O,
+                            float *lse, int64_t S, int H, int D, void *stream);
+
+/*
+ * mk_ring_attention_unfused -- the same results from two launches: a gather
+ * kernel copies every arriving tile into the ring buffers, then the
+ * attention kernel (the same core, no flags, one workgroup per CU, tasks
+ * dealt round-robin within each head band) computes O and lse.  Arguments as
+ * above; touches no workspace state.
+ */
+int mk_ring_attention_unfused(const void *q, const void *k_local, const void *v_local, const void *k_peers,
+                              const void *v_peers, int num_peers, void *k_ring, void *v_ring, float *O,
+                              float *lse, int64_t S, int H, int D, void *stream);
+
+/*
  * mk_set_partition -- partition of the persistent workgroups into reduce and
  * compute roles for subsequent mk_gemm_reduce_local launches (process-wide).
  *   mode       mk_part_mode.
@@ -372,8 +439,10 @@ typedef struct mk_stats {
                                      every kind raised by any launch since the
                                      last mk_get_stats (see there)             */
     uint32_t kind;                /* 0 GEMM+AllReduce, 1 GEMM+ReduceScatter,
-                                     2 AllGather+GEMM (see mk_allgather_gemm_local
-                                     for how its statistics map onto these)  */
+                                     2 AllGather+GEMM, 3 Ring Attention (see
+                                     mk_allgather_gemm_local and
+                                     mk_ring_attention_local for how their
+                                     statistics map onto these)              */
 } mk_stats;
 
 /* Words per map in the optional `maps` output of mk_get_stats, in order:
