@@ -79,6 +79,11 @@ def parse(argv=None):
                          "prints its own JSON line")
     ap.add_argument("--no-allgather", action="store_true",
                     help="leave the AllGather+GEMM share out of the default line")
+    ap.add_argument("--ring", default=None, metavar="WORKLOAD",
+                    help="only one Ring Attention workload (ra_tiny, ra_sp_share, ra_long); "
+                         "prints its own JSON line")
+    ap.add_argument("--no-ring", action="store_true",
+                    help="leave the Ring Attention share out of the default line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of this size (counter calibration)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -519,6 +524,95 @@ def measure_allgather(args, w, mk, wl, np, torch, sweep=True):
     return rec
 
 
+RA_SUITE = ("ra_tiny", "ra_sp_share", "ra_long")
+
+
+def ra_algorithmic_bytes(w):
+    """One rank's share of Ring Attention: Q, K and V read once, every
+    arriving K and V read once and written once into the ring buffers, O
+    (fp32) and LSE written once."""
+    e = w.S * w.H * w.D
+    P = w.ranks - 1
+    return 2 * 3 * e + 2 * 2 * 2 * P * e + 4 * e + 4 * w.S * w.H
+
+
+def measure_ring(args, w, mk, wl, np, torch, sweep=True):
+    """One rank's share of Ring Attention: fused (adaptive), unfused (gather
+    kernel then the attention kernel), static copy partitions 2..64."""
+    q, kl, vl, kp, vp = wl.make_ra_inputs(w)
+    dev = "cuda:0"
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+    Q, KL, VL, KP, VP = t(q), t(kl), t(vl), t(kp), t(vp)
+    KR, VR = torch.empty_like(KP), torch.empty_like(VP)
+    O = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    L = torch.empty((w.H, w.S), dtype=torch.float32, device=dev)
+    del q, kl, vl, kp, vp
+    stream = torch.cuda.current_stream()
+    flush = None
+    if not args.no_flush:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+        def flush():
+            scratch.fill_(1)
+
+    def fused():
+        mk.ring_attention_local(Q, KL, VL, KP, VP, KR, VR, O, L)
+
+    def unfused():
+        mk.ring_attention_unfused(Q, KL, VL, KP, VP, KR, VR, O, L)
+
+    fixed = w.mode != "adaptive"
+    set_adaptive_defaults(mk)
+    ms_f, _ = time_leg(fused, args.steps, args.warmup, flush, stream, torch)
+    st = check_leg(mk, f"{w.name} fused", maps=True)
+    ms = statistics.fmean(ms_f)
+    flops = w.flops
+    bytes_ = ra_algorithmic_bytes(w)
+    sec = ms / 1e3
+    t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    t_hbm = bytes_ / (HBM_PEAK_GBPS * 1e9)
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": bytes_ / sec / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / sec / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    copy_us = (st["reduce_ticks_end"] - st["reduce_ticks_start"]) / st["timer_hz"] * 1e6
+    rec = {"config": {"ranks": w.ranks, "tokens_per_rank": w.S, "heads": w.H, "head_dim": w.D,
+                      "kv_tile_tokens": 128, "query_block": 128},
+           "partition": "adaptive", "fused_ms": summary(ms_f), "ms": ms, "tflops": flops / sec / 1e12,
+           "roofline": roof, "algorithmic_flops": flops, "algorithmic_bytes": bytes_,
+           "copy_window_us": copy_us,
+           "n_copy_range": [st["n_reduce_min_seen"], st["n_reduce_max_seen"]]}
+    print(f"[bench] {w.name} fused: {summary(ms_f)}", file=sys.stderr, flush=True)
+    ms_u, _ = time_leg(unfused, args.steps, args.warmup, flush, stream, torch)
+    rec["unfused_ms"] = summary(ms_u)
+    rec["fused_vs_unfused"] = statistics.fmean(ms_u) / ms
+    print(f"[bench] {w.name} unfused: {summary(ms_u)}", file=sys.stderr, flush=True)
+    if fixed:
+        mk.set_partition(w.mode, w.n_copy)
+        ms_x, _ = time_leg(fused, args.steps, args.warmup, flush, stream, torch)
+        check_leg(mk, f"{w.name} {w.mode} {w.n_copy}")
+        set_adaptive_defaults(mk)
+        rec["recipe_partition"] = {"mode": w.mode, "n_copy": w.n_copy, "fused_ms": summary(ms_x),
+                                   "fused_vs_unfused": statistics.fmean(ms_u) / statistics.fmean(ms_x)}
+    if fixed or not sweep:
+        set_adaptive_defaults(mk)
+        return rec
+    table = {}
+    for n in STATIC_SWEEP:
+        mk.set_partition("static", n)
+        ms_n, _ = time_leg(fused, max(3, args.steps // 2), 1, flush, stream, torch)
+        check_leg(mk, f"{w.name} static {n}")
+        table[n] = statistics.fmean(ms_n)
+    set_adaptive_defaults(mk)
+    best = min(table, key=table.get)
+    rec["static_sweep_ms"] = {str(k): v for k, v in table.items()}
+    rec["best_static_2_64"] = {"n_copy": best, "ms": table[best]}
+    rec["adaptive_vs_best_static_2_64"] = table[best] / ms
+    print(f"[bench] {w.name} static sweep: {table}", file=sys.stderr, flush=True)
+    return rec
+
+
 def geomean(xs):
     xs = [x for x in xs if x]
     return math.exp(sum(math.log(x) for x in xs) / len(xs)) if xs else None
@@ -604,6 +698,15 @@ def main(argv=None):
     if args.reduce_scatter:
         reduce_scatter(args, w_head, mk, wl, upload, np, torch)
         return
+    if args.ring:
+        w = wl.ra_workload(args.ring)
+        rec = measure_ring(args, w, mk, wl, np, torch, sweep=not (args.no_sweep or args.fused_only))
+        print(json.dumps({"metric": "Ring Attention TFLOP/s (one rank's share, fused adaptive)",
+                          "value": rec["tflops"], "unit": "TFLOP/s", "ms_per_step": rec["ms"],
+                          "steps": args.steps, "warmup": args.warmup, "dtype": "bf16",
+                          "data": "synthetic", "config": {"workload": args.ring, **rec["config"]},
+                          **{k: v for k, v in rec.items() if k != "config"}}), flush=True)
+        return
     if args.allgather:
         rec = measure_allgather(args, wl.ag_workload(args.allgather), mk, wl, np, torch,
                                 sweep=not (args.no_sweep or args.fused_only))
@@ -676,6 +779,13 @@ def main(argv=None):
             torch.cuda.empty_cache()
         result["allgather_gemm"] = ag
         result["allgather_min_fused_vs_unfused"] = min(r["fused_vs_unfused"] for r in ag.values())
+    if args.workload == "all" and not (args.fused_only or args.no_ring):
+        ra = {}
+        for name in RA_SUITE:
+            ra[name] = measure_ring(args, wl.ra_workload(name), mk, wl, np, torch, sweep=not args.no_sweep)
+            torch.cuda.empty_cache()
+        result["ring_attention"] = ra
+        result["ring_attention_min_fused_vs_unfused"] = min(r["fused_vs_unfused"] for r in ra.values())
     print(json.dumps(result), flush=True)
 
 

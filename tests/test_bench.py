@@ -137,3 +137,15 @@ def test_allgather_algorithmic_bytes():
     assert bench.ag_algorithmic_bytes(w) == (2 * R * w.M * w.K * 2 + 2 * w.K * w.N
                                             + 4 * R * w.M * w.N)
     assert set(bench.AG_SUITE) == set(wl.AG_WORKLOADS)
+
+
+def test_ring_attention_algorithmic_work():
+    """Ring Attention share: 4 S (R S) D H flops; Q, K, V read once, every
+    arriving K and V read once and written once, O (fp32) and LSE written."""
+    import bench
+    import workloads as wl
+    w = wl.ra_workload("ra_sp_share")
+    e = w.S * w.H * w.D
+    assert w.flops == 4 * w.S * (w.ranks * w.S) * w.D * w.H
+    assert bench.ra_algorithmic_bytes(w) == 3 * 2 * e + (w.ranks - 1) * 2 * 2 * 2 * e + 4 * e + 4 * w.S * w.H
+    assert set(bench.RA_SUITE) == set(wl.RA_WORKLOADS)
