@@ -115,11 +115,12 @@ struct Fa {
         }
     }
 
-    // One stage: scores, online softmax, P.V.  `rows` keys are valid.
-    static __device__ __forceinline__ void stage(const Lane &ln, const lchar *sl, const bf16x8 (&qf)[8],
-                                                 f32x16 (&o)[4], float &m, float &l, int rows, float c) {
-        const int hl = (threadIdx.x & 63) >> 5;
-        f32x16 s0 = {}, s1 = {};
+    // S^T of one stage: s0 keys 0..31, s1 keys 32..63 (lane (j + 32 hl),
+    // register v: key 8 (v / 4) + 4 hl + v % 4 of the block, query j)
+    static __device__ __forceinline__ void qk(const Lane &ln, const lchar *sl, const bf16x8 (&qf)[8], f32x16 &s0,
+                                              f32x16 &s1) {
+        s0 = f32x16{};
+        s1 = f32x16{};
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const bf16x8 k0 = *(const lbf16x8 *)(sl + ln.kofs[s]);
@@ -127,25 +128,42 @@ struct Fa {
             s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], s0, 0, 0, 0);
             s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], s1, 0, 0, 0);
         }
-        // lane (j + 32 hl), register v holds key 8 (v / 4) + 4 hl + v % 4 of
-        // each 32-key block, query j
-        if (__builtin_amdgcn_readfirstlane(rows) < KVB) {
+    }
+
+    // Online softmax of one stage's scores and P.V.  `rows` keys are valid.
+    // The running maximum m (log2 units) moves only when a stage's maximum
+    // exceeds it by more than kLazy: then p <= 2^kLazy, which fp32 sums and
+    // bf16 P hold without loss, and most stages skip rescaling O (the test is
+    // per query, the skip per wave).
+    static constexpr float kLazy = 8.f;
+
+    // Keys at or past `rows` get score -inf (a stage at the ragged end of a
+    // step).  Called under a uniform branch; the empty asm keeps it a branch
+    // instead of selects executed in every stage.
+    static __device__ __forceinline__ void mask(f32x16 &s0, f32x16 &s1, int rows) {
+        asm volatile("" ::: "memory");
+        const int hl = (threadIdx.x & 63) >> 5;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int key = 8 * (v >> 2) + 4 * hl + (v & 3);
-                if (key >= rows) s0[v] = -__builtin_inff();
-                if (key + 32 >= rows) s1[v] = -__builtin_inff();
-            }
+        for (int v = 0; v < 16; ++v) {
+            const int key = 8 * (v >> 2) + 4 * hl + (v & 3);
+            if (key >= rows) s0[v] = -__builtin_inff();
+            if (key + 32 >= rows) s1[v] = -__builtin_inff();
         }
+    }
+
+    // Exponentiated scores of one stage as the bf16 P^T operands; returns the
+    // new running maximum (m moves only when a stage's maximum exceeds it by
+    // more than kLazy, so p <= 2^kLazy) and adds the stage's sum to ls.  No
+    // branch inside: the caller's score MFMAs of the next stage can be
+    // interleaved with this vector work.
+    static __device__ __forceinline__ float softmax(const f32x16 &s0, const f32x16 &s1, float m, float c,
+                                                    bf16x8 (&p)[2][2], float &ls) {
         float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
         for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(s0[v], s1[v]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mn = fmaxf(m, mx * c);
-        const float alpha = __builtin_amdgcn_exp2f(m - mn);
-        m = mn;
-        float ls = 0.f;
-        bf16x8 p[2][2];
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+        const float mn = mx > m + kLazy ? mx : m;
+        float acc = 0.f;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             f32x8 a0, a1;
@@ -153,14 +171,18 @@ struct Fa {
             for (int e = 0; e < 8; ++e) {
                 a0[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[8 * t + e], c, -mn));
                 a1[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[8 * t + e], c, -mn));
-                ls += a0[e] + a1[e];
+                acc += a0[e] + a1[e];
             }
             p[0][t] = __builtin_convertvector(a0, bf16x8);
             p[1][t] = __builtin_convertvector(a1, bf16x8);
         }
-        l = l * alpha + ls;
-#pragma unroll
-        for (int fd = 0; fd < 4; ++fd) o[fd] = o[fd] * alpha;
+        ls = acc;
+        return mn;
+    }
+
+    // O^T += V^T P^T for one stage
+    static __device__ __forceinline__ void pv(const Lane &ln, const lchar *sl, const bf16x8 (&p)[2][2],
+                                              f32x16 (&o)[4]) {
         const lchar *vb = sl + KV_BYTES;
 #pragma unroll
         for (int fd = 0; fd < 4; ++fd)
@@ -205,8 +227,20 @@ __device__ __forceinline__ bool fa_task(const RaArgs &a, const Fa::Lane &ln, lch
                                         uint32_t qb) {
     constexpr int D = Fa::D;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5;
+    // every field the task needs, read once into locals: the loads of the
+    // K/V stream are inline assembly that clobbers memory, so fields read
+    // inside the loop would be reloaded at every stage
     const int64_t S = a.S;
     const int64_t HD = (int64_t)a.H * D;
+    const uint32_t nkv = a.nkv, epoch = a.epoch;
+    const uint32_t U = (uint32_t)a.R * nkv;     // KV tiles in ring order, step 0 first
+    const uint16_t *const k_loc = a.k_local + (int64_t)h * D, *const v_loc = a.v_local + (int64_t)h * D;
+    const uint16_t *const k_rng = a.k_ring + (int64_t)h * D, *const v_rng = a.v_ring + (int64_t)h * D;
+    uint32_t *const flags = a.ws.chunk_flag;
+    const uint64_t timeout_ticks = a.timeout_ticks;
+    const float c = a.scale_log2;
+    float *const Oh = a.O + (int64_t)h * D;
+    float *const lse_h = a.lse + (int64_t)h * S;
     const int64_t q0 = (int64_t)qb * kRaQRows;
     const int64_t row = q0 + 32 * wave + (lane & 31);
     const uint32_t base = (uint32_t)(uintptr_t)lds;
@@ -223,72 +257,116 @@ __device__ __forceinline__ bool fa_task(const RaArgs &a, const Fa::Lane &ln, lch
                                                    kPolicyDefault));
     }
 
-    const uint32_t U = (uint32_t)a.R * a.nkv;   // KV tiles in ring order, step 0 first
     const uint32_t nst = 2 * U;
-    bool dead = false;                          // this wave gave up on a wait
-
-    // issue stage x of the task's stage sequence into its ring slot
-    auto issue_stage = [&](uint32_t x) {
-        const uint32_t u = x >> 1, j = x & 1;
-        const uint32_t step = u / a.nkv, t = u - step * a.nkv;
+    // issue the next stage of the task's sequence (stages are issued in
+    // order: tile u = (step, t), half j) into its ring slot; the position is
+    // advanced here, without divisions
+    uint32_t ix = 0, i_step = 0, i_t = 0;
+    auto issue_stage = [&]() {
+        const uint32_t x = ix++, u = x >> 1, j = x & 1;
+        const uint32_t step = i_step, t = i_t;
+        if (j == 1 && ++i_t == nkv) {
+            i_t = 0;
+            ++i_step;
+        }
         if constexpr (GATED) {
-            if (step > 0 && j == 0 && !dead) {
-                const uint32_t c = u - a.nkv;
-                // the flag fetched two tiles ahead (a 32-bit word in LDS)
+            if (step > 0 && j == 0) {
+                // the flag fetched two tiles ahead (a 32-bit word in LDS),
+                // else a bounded wait; after a failed wait (the error is
+                // recorded) the stage is read anyway and the launch's result
+                // is reported invalid
                 bool ok = false;
                 if (u >= 2) ok = *(const volatile __attribute__((address_space(3))) uint32_t *)(
-                                     lds + Fa::FLAG_OFS + 4 * (u & 3)) == a.epoch;
-                if (!ok) ok = ra_wait_tile(a.ws.chunk_flag + c, a.epoch, a.timeout_ticks, L);
-                if (!ok) dead = true;
+                                     lds + Fa::FLAG_OFS + 4 * (u & 3)) == epoch;
+                if (!ok) ra_wait_tile(flags + (u - nkv), epoch, timeout_ticks, L);
             }
             // fetch the flag of tile u + 2 into LDS, behind this stage's loads
             // in wave 0's queue; it is read two tiles later
-            if (j == 0 && wave == 0 && u + 2 < U && u + 2 >= a.nkv) {
-                const uint32_t c2 = u + 2 - a.nkv;
+            if (j == 0 && wave == 0 && u + 2 < U && u + 2 >= nkv) {
+                const uint32_t c2 = u + 2 - nkv;
                 if (lane == 0) {
-                    const u32x4 df = make_desc(a.ws.chunk_flag);
+                    const u32x4 df = make_desc(flags);
                     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen sc1 lds"
                                  :
-                                 : "s"(base + Fa::FLAG_OFS + 4 * ((u + 2) & 3)), "v"(c2 * 4u), "s"(df)
+                                 : "s"(__builtin_amdgcn_readfirstlane(base + Fa::FLAG_OFS + 4 * ((u + 2) & 3))),
+                                   "v"(c2 * 4u), "s"(df)
                                  : "memory", "m0");
                 }
             }
-            if (dead) return;
         }
         const int64_t kv0 = (int64_t)t * kRaKvRows + (int64_t)j * Fa::KVB;
         const int rows = (int)(S - kv0 < Fa::KVB ? S - kv0 : Fa::KVB);
-        const int64_t off = (kv0 * a.H + h) * D;
-        const uint16_t *kp = step == 0 ? a.k_local + off : a.k_ring + (int64_t)(step - 1) * S * HD + off;
-        const uint16_t *vp = step == 0 ? a.v_local + off : a.v_ring + (int64_t)(step - 1) * S * HD + off;
+        const int64_t off = kv0 * HD;
+        const uint16_t *kp = step == 0 ? k_loc + off : k_rng + (int64_t)(step - 1) * S * HD + off;
+        const uint16_t *vp = step == 0 ? v_loc + off : v_rng + (int64_t)(step - 1) * S * HD + off;
         Fa::issue(ln, base + (x % Fa::NSLOT) * Fa::SLOT, kp, vp, rows);
     };
 
     const uint32_t pre = nst < (uint32_t)Fa::AHEAD ? nst : (uint32_t)Fa::AHEAD;
-    for (uint32_t x = 0; x < pre; ++x) issue_stage(x);
+    for (uint32_t x = 0; x < pre; ++x) issue_stage();
 
     f32x16 o[4] = {};
     float m = -__builtin_inff(), l = 0.f;
-    const float c = a.scale_log2;
-    for (uint32_t b = 0; b < nst; ++b) {
-        // stages issued after b: at most AHEAD - 1
-        const uint32_t later = nst - 1 - b < (uint32_t)(Fa::AHEAD - 1) ? nst - 1 - b : (uint32_t)(Fa::AHEAD - 1);
-        if (later >= 2) wait_vmcnt<2 * 2 * Fa::PIECES>();
-        else if (later == 1) wait_vmcnt<2 * Fa::PIECES>();
-        else wait_vmcnt<0>();
-        __syncthreads();   // stage b has landed for every wave; slot (b - 1) is free
-        if (b + Fa::AHEAD < nst) issue_stage(b + Fa::AHEAD);
-        const uint32_t u = b >> 1, j = b & 1;
-        const uint32_t t = u % a.nkv;
-        const int64_t kv0 = (int64_t)t * kRaKvRows + (int64_t)j * Fa::KVB;
-        const int rows = (int)(S - kv0 < Fa::KVB ? S - kv0 : Fa::KVB);
-        Fa::stage(ln, lds + (b % Fa::NSLOT) * Fa::SLOT, qf, o, m, l, rows, c);
+    // valid keys of the stages consumed in order, tracked without divisions
+    uint32_t c_t = 0, c_j = 0;
+    auto rows_next = [&]() {
+        const int64_t kv0 = (int64_t)c_t * kRaKvRows + (int64_t)c_j * Fa::KVB;
+        if (c_j == 1 && ++c_t == nkv) c_t = 0;
+        c_j ^= 1;
+        return (int)(S - kv0 < Fa::KVB ? S - kv0 : Fa::KVB);
+    };
+    // Stage b's scores are computed one step ahead: the MFMAs of S(b + 1) run
+    // while the vector units exponentiate S(b).  Two score sets alternate
+    // (the loop body covers two stages), so no registers are copied.
+    f32x16 sa0, sa1, sb0, sb1;
+    // stages issued after stage 0: pre - 1
+    if (pre >= 3) wait_vmcnt<2 * 2 * Fa::PIECES>();
+    else if (pre == 2) wait_vmcnt<2 * Fa::PIECES>();
+    else wait_vmcnt<0>();
+    __syncthreads();   // stage 0 has landed
+    Fa::qk(ln, lds, qf, sa0, sa1);
+    // one step of the pipeline: wait for stage b + 1, refill, then S(b + 1)
+    // on the matrix cores while the vector units exponentiate S(b), then
+    // P.V of stage b.  The score MFMAs run even past the last stage (on a
+    // stale slot, result unused) so that block has no branch to split it.
+    auto step = [&](uint32_t b, f32x16 &c0, f32x16 &c1, f32x16 &n0, f32x16 &n1) {
+        if (b + 1 < nst) {
+            if (b + 2 < nst) wait_vmcnt<2 * Fa::PIECES>();
+            else wait_vmcnt<0>();
+        }
+        __syncthreads();   // stage b + 1 has landed for every wave; slot (b - 1) is free
+        if (b + Fa::AHEAD < nst) issue_stage();
+        const int rows = rows_next();
+        if (__builtin_amdgcn_readfirstlane(rows) < Fa::KVB) Fa::mask(c0, c1, rows);
+        Fa::qk(ln, lds + ((b + 1) % Fa::NSLOT) * Fa::SLOT, qf, n0, n1);
+        bf16x8 p[2][2];
+        float ls;
+        const float mn = Fa::softmax(c0, c1, m, c, p, ls);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one score MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // vector work of the softmax
+        }
+        if (__ballot(mn != m)) {
+            const float alpha = __builtin_amdgcn_exp2f(m - mn);
+            l *= alpha;
+#pragma unroll
+            for (int fd = 0; fd < 4; ++fd) o[fd] = o[fd] * alpha;
+        }
+        m = mn;
+        l += ls;
+        Fa::pv(ln, lds + (b % Fa::NSLOT) * Fa::SLOT, p, o);
+    };
+    for (uint32_t b = 0; b < nst; b += 2) {
+        step(b, sa0, sa1, sb0, sb1);
+        if (b + 1 < nst) step(b + 1, sb0, sb1, sa0, sa1);
     }
     __syncthreads();   // every wave is done with the ring before the next task refills it
 
     // normalise and store: lane (j + 32 hl) holds O^T rows 32 fd + 8 g + 4 hl + 0..3
     const float lt = l + __shfl_xor(l, 32);
     const float inv = 1.f / lt;
-    const auto ro = scalar_rsrc(a.O + (int64_t)h * D);
+    const auto ro = scalar_rsrc(Oh);
     const bool ok = row < S;
 #pragma unroll
     for (int fd = 0; fd < 4; ++fd)
@@ -299,10 +377,8 @@ __device__ __forceinline__ bool fa_task(const RaArgs &a, const Fa::Lane &ln, lch
             f32x4 v{o[fd][4 * g] * inv, o[fd][4 * g + 1] * inv, o[fd][4 * g + 2] * inv, o[fd][4 * g + 3] * inv};
             __builtin_amdgcn_raw_buffer_store_b128(v, ro, off, 0, kPolicyStream);
         }
-    if (hl == 0 && ok) a.lse[(int64_t)h * S + row] = (m + __log2f(lt)) * 0.69314718055994531f;
-    bool alive = true;
-    if constexpr (GATED) alive = !__builtin_amdgcn_readfirstlane((int)dead);
-    return alive;
+    if (hl == 0 && ok) lse_h[row] = (m + __log2f(lt)) * 0.69314718055994531f;
+    return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -431,19 +507,32 @@ __device__ RaDecision ra_next(const RaArgs &a, Live *L, uint32_t wg, RaSched &s)
     return {kRaExit, 0, ns};
 }
 
-__global__ __launch_bounds__(Fa::NT, 1) void ring_attention_kernel(RaArgs a) {
+// The argument block is read through a pointer to the kernel-argument
+// segment that is laundered at the top of every task: each task reloads the
+// fields it needs (scalar loads) instead of keeping all of them in scalar
+// registers across the persistent loop, which spilled dozens of them into
+// vector lanes read back inside the attention loop.
+__device__ __forceinline__ const RaArgs *ra_args() {
+    const RaArgs *p = (const RaArgs *)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(p));
+    return p;
+}
+
+__global__ __launch_bounds__(Fa::NT, 1) void ring_attention_kernel(RaArgs a_arg) {
     __shared__ __attribute__((aligned(1024))) char lds_raw[Fa::LDS_BYTES];
     __shared__ RaDecision sh_dec;
     __shared__ RaSched sh_sched;
     __shared__ uint64_t sh_c0, sh_r0;
+    (void)a_arg;
     lchar *lds = (lchar *)lds_raw;
     const int tid = threadIdx.x;
     const uint32_t wg = blockIdx.x;
-    Live *L = a.ws.live;
     Fa::Lane ln;
-    Fa::init_lane(ln, (uint32_t)a.H * Fa::D * 2u);
+    Fa::init_lane(ln, (uint32_t)ra_args()->H * Fa::D * 2u);
     RaSched &s = sh_sched;
     if (tid == 0) {
+        const RaArgs &a = *ra_args();
+        Live *L = a.ws.live;
         s.target = (uint32_t)a.ns_init;
         s.det_i = 0;
         s.bands_done = 0;
@@ -452,6 +541,8 @@ __global__ __launch_bounds__(Fa::NT, 1) void ring_attention_kernel(RaArgs a) {
         min_relaxed(&L->t_start, ticks_now());
     }
     for (;;) {
+        const RaArgs &a = *ra_args();
+        Live *L = a.ws.live;
         if (tid == 0) {
             sh_dec = ld_relaxed(&L->error) != kErrNone ? RaDecision{kRaExit, 0, 0} : ra_next(a, L, wg, s);
             sh_c0 = cycles_now();
@@ -526,6 +617,8 @@ __global__ __launch_bounds__(Fa::NT, 1) void ring_attention_kernel(RaArgs a) {
         __syncthreads();
     }
     if (tid == 0) {
+        const RaArgs &a = *ra_args();
+        Live *L = a.ws.live;
         max_relaxed(&L->t_end, ticks_now());
         drain_vmem();
         const uint32_t old = add_relaxed(&L->exit_count, 1u);
@@ -558,17 +651,21 @@ __global__ __launch_bounds__(256) void ring_gather_kernel(RaArgs a) {
 // the same attention core over every tile, no flags; workgroup b takes the
 // tasks of band b mod bands round-robin (the fused kernel's claim order,
 // fixed)
-__global__ __launch_bounds__(Fa::NT, 1) void ring_fa_kernel(RaArgs a) {
+__global__ __launch_bounds__(Fa::NT, 1) void ring_fa_kernel(RaArgs a_arg) {
     __shared__ __attribute__((aligned(1024))) char lds_raw[Fa::LDS_BYTES];
+    (void)a_arg;
     lchar *lds = (lchar *)lds_raw;
     Fa::Lane ln;
-    Fa::init_lane(ln, (uint32_t)a.H * Fa::D * 2u);
-    const uint32_t nb = a.bands, b = blockIdx.x, x = b % nb;
-    const uint32_t per = (gridDim.x - x + nb - 1) / nb;   // workgroups of band x
-    const uint32_t heads = ((uint32_t)a.H - x + nb - 1) / nb;
-    for (uint32_t i = b / nb; i < heads * a.nqb; i += per) {
-        const uint32_t h = x + nb * (i / a.nqb), qb = i % a.nqb;
-        fa_task<false>(a, ln, lds, nullptr, h, qb);
+    Fa::init_lane(ln, (uint32_t)ra_args()->H * Fa::D * 2u);
+    const uint32_t b = blockIdx.x;
+    for (uint32_t i = 0;; ++i) {
+        const RaArgs &a = *ra_args();
+        const uint32_t nb = a.bands, x = b % nb;
+        const uint32_t per = (gridDim.x - x + nb - 1) / nb;   // workgroups of band x
+        const uint32_t heads = ((uint32_t)a.H - x + nb - 1) / nb;
+        const uint32_t k = b / nb + i * per;                  // this workgroup's i-th task of the band
+        if (k >= heads * a.nqb) break;
+        fa_task<false>(a, ln, lds, nullptr, x + nb * (k / a.nqb), k % a.nqb);
     }
 }
 
