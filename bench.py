@@ -87,11 +87,35 @@ def parse(argv=None):
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of this size (counter calibration)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_S * 1e3,
+                    help="untimed run of each leg before its warm-up steps, so that it is timed "
+                         "at the GPU's settled clock (0: none)")
     return ap.parse_args(argv)
 
 
-def time_leg(fn, steps, warmup, flush, stream, torch):
-    """Per-launch durations (ms) from HIP events recorded on the launch stream."""
+SETTLE_S = 0.2
+
+
+def time_leg(fn, steps, warmup, flush, stream, torch, settle_s=None):
+    """Per-launch durations (ms) from HIP events recorded on the launch stream.
+
+    Before its warm-up steps a leg runs untimed for settle_s seconds of wall
+    time.  After an idle spell (input generation, a host-side check) the
+    GPU's power management answers a heavy launch by cutting the shader clock
+    and restores it over about ten launches: GRBM_GUI_ACTIVE per dispatch on
+    the 16384x8192x8192 GEMM+AllReduce reads 1.65 GHz on the first launch,
+    1.13 on the second and 1.48 on the sixth.  A leg timed in that transient
+    is slower for the clock alone, so every leg is timed at its settled clock.
+    """
+    if settle_s is None:
+        settle_s = SETTLE_S
+    t_end = time.perf_counter() + settle_s
+    while time.perf_counter() < t_end:
+        for _ in range(4):
+            if flush is not None:
+                flush()
+            fn()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         if flush is not None:
             flush()
@@ -634,7 +658,7 @@ def gemm_only(args, w, mk, wl, upload, np, torch):
     mean = statistics.fmean(ms)
     print(json.dumps({"metric": "GEMM TFLOP/s (unfused baseline's GEMM kernel, no peers)",
                       "value": w.flops / (mean * 1e-3) / 1e12, "unit": "TFLOP/s",
-                      "ms_per_step": mean, "steps": args.steps, "warmup": args.warmup,
+                      "ms_per_step": mean, "steps": args.steps, "warmup": args.warmup, "settle_ms": args.settle_ms,
                       "dtype": "bf16", "data": "synthetic",
                       "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
                                  "tile": [w.tile_m, w.tile_n]}}), flush=True)
@@ -669,7 +693,7 @@ def reduce_scatter(args, w, mk, wl, upload, np, torch):
     print(json.dumps({"metric": "GEMM+ReduceScatter TFLOP/s (one rank's share, fused adaptive)",
                       "value": w.flops / (mf * 1e-3) / 1e12, "unit": "TFLOP/s",
                       "ms_per_step": mf, "unfused_ms_per_step": mu, "fused_over_unfused": mu / mf,
-                      "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic",
+                      "steps": args.steps, "warmup": args.warmup, "settle_ms": args.settle_ms, "dtype": "bf16", "data": "synthetic",
                       "fused_ms": summary(ms_f), "unfused_ms": summary(ms_u),
                       "status": st["status_name"],
                       "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "ranks": w.peers + 1,
@@ -677,7 +701,9 @@ def reduce_scatter(args, w, mk, wl, upload, np, torch):
 
 
 def main(argv=None):
+    global SETTLE_S
     args = parse(argv)
+    SETTLE_S = max(0.0, args.settle_ms) / 1e3
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
               "multi-GPU GEMM+AllReduce is not part of it.", file=sys.stderr)
@@ -703,7 +729,7 @@ def main(argv=None):
         rec = measure_ring(args, w, mk, wl, np, torch, sweep=not (args.no_sweep or args.fused_only))
         print(json.dumps({"metric": "Ring Attention TFLOP/s (one rank's share, fused adaptive)",
                           "value": rec["tflops"], "unit": "TFLOP/s", "ms_per_step": rec["ms"],
-                          "steps": args.steps, "warmup": args.warmup, "dtype": "bf16",
+                          "steps": args.steps, "warmup": args.warmup, "settle_ms": args.settle_ms, "dtype": "bf16",
                           "data": "synthetic", "config": {"workload": args.ring, **rec["config"]},
                           **{k: v for k, v in rec.items() if k != "config"}}), flush=True)
         return
@@ -712,7 +738,7 @@ def main(argv=None):
                                 sweep=not (args.no_sweep or args.fused_only))
         print(json.dumps({"metric": "AllGather+GEMM TFLOP/s (one rank's share, fused adaptive)",
                           "value": rec["tflops"], "unit": "TFLOP/s", "ms_per_step": rec["ms"],
-                          "steps": args.steps, "warmup": args.warmup, "dtype": "bf16",
+                          "steps": args.steps, "warmup": args.warmup, "settle_ms": args.settle_ms, "dtype": "bf16",
                           "data": "synthetic", "config": {"workload": args.allgather, **rec["config"]},
                           **{k: v for k, v in rec.items() if k != "config"}}), flush=True)
         return
@@ -740,6 +766,7 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": head["ms"],
         "higher_is_better": True,
         "scaling": "weak",

@@ -78,36 +78,55 @@ class _FakeLib:
                 "sticky_errors": bits}
 
 
+class _Ev:
+    def __init__(self, enable_timing=True):
+        pass
+
+    def record(self, stream):
+        pass
+
+    def elapsed_time(self, other):
+        return 1.0
+
+
+class _Torch:
+    class cuda:
+        Event = _Ev
+
+        @staticmethod
+        def synchronize():
+            pass
+
+
 @pytest.mark.parametrize("faulty", [0, 7, 19])
 def test_a_failed_launch_anywhere_in_a_leg_fails_the_bench(faulty):
     """A timeout in any launch of a timed leg (first, middle, last) makes the
     leg's status check end the bench with a non-zero exit and no line."""
     import bench
     fake = _FakeLib(faulty)
-
-    class _Ev:
-        def __init__(self, enable_timing=True):
-            pass
-
-        def record(self, stream):
-            pass
-
-        def elapsed_time(self, other):
-            return 1.0
-
-    class _Torch:
-        class cuda:
-            Event = _Ev
-
-            @staticmethod
-            def synchronize():
-                pass
-
-    bench.time_leg(lambda: fake.gemm_reduce_local(), 20, 0, None, None, _Torch)
+    bench.time_leg(lambda: fake.gemm_reduce_local(), 20, 0, None, None, _Torch, settle_s=0)
     assert fake.launches == 20
     with pytest.raises(SystemExit) as e:
         bench.check_leg(fake, "fused")
     assert e.value.code == 3
+
+
+def test_a_failed_launch_while_settling_fails_the_bench():
+    """The untimed settling launches count too: the leg's status check covers
+    every launch since the previous check."""
+    import bench
+    fake = _FakeLib(faulty=2)
+    ms, _ = bench.time_leg(lambda: fake.gemm_reduce_local(), 5, 1, None, None, _Torch, settle_s=0.01)
+    assert len(ms) == 5 and fake.launches >= 4 + 1 + 5
+    with pytest.raises(SystemExit) as e:
+        bench.check_leg(fake, "fused")
+    assert e.value.code == 3
+
+
+def test_settle_defaults_and_flag():
+    import bench
+    assert bench.parse([]).settle_ms == pytest.approx(bench.SETTLE_S * 1e3)
+    assert bench.parse(["--settle-ms", "0"]).settle_ms == 0
 
 
 def test_a_clean_leg_passes_the_status_check():
