@@ -201,22 +201,23 @@ __device__ __forceinline__ void ag_copy(const AgArgs &a, uint32_t u) {
     const uint32_t n16 = (uint32_t)(n16c * (part + 1) / a.parts) - i0;
     const auto rs = scalar_rsrc(src + (int64_t)i0 * 8);
     const auto rd = scalar_rsrc(dst + (int64_t)i0 * 8);
-    constexpr int U = NT >= 512 ? 8 : 16;   // 64 KiB in flight per workgroup
-    uint32_t i = threadIdx.x;
-    for (; i + (U - 1) * NT < n16; i += U * NT) {
-        u32x4 v[U];
+    // Every load of a pass is issued before its first store, and a pass
+    // covers up to 80 KiB: a part of up to that size (64 KiB, or a little
+    // more where the part count is capped) is one load round trip and one
+    // store drain.  Pieces past the part read zero and drop their stores.
+    constexpr int U = NT >= 512 ? 10 : 20;
+    for (uint32_t b = 0; b < n16; b += U * NT) {
+        uint32_t off[U];
+        f32x4 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (i + u * NT) * 16u, 0,
-                                                                                   kPolicyStream));
+        for (int k = 0; k < U; ++k) {
+            const uint32_t i = b + k * NT + threadIdx.x;
+            off[k] = i < n16 ? i * 16u : kOOB;
+            v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[k], 0, kPolicyStream);
+        }
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(f32x4, v[u]), rd, (i + u * NT) * 16u, 0,
-                                                   kPolicyCoherentStream);
-    }
-    for (; i < n16; i += NT) {
-        const f32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, i * 16u, 0, kPolicyStream);
-        __builtin_amdgcn_raw_buffer_store_b128(v, rd, i * 16u, 0, kPolicyCoherentStream);
+        for (int k = 0; k < U; ++k)
+            __builtin_amdgcn_raw_buffer_store_b128(v[k], rd, off[k], 0, kPolicyCoherentStream);
     }
 }
 

@@ -400,25 +400,31 @@ __device__ __forceinline__ void ra_copy(const RaArgs &a, uint32_t u) {
     const uint32_t i0 = (uint32_t)(n16t * part / a.parts);
     const uint32_t n16 = (uint32_t)(n16t * (part + 1) / a.parts) - i0;
     const int64_t eoff = ((int64_t)s1 * a.S + t0) * HD + (int64_t)i0 * 8;
+    const auto rsk = scalar_rsrc(a.k_peers + eoff), rsv = scalar_rsrc(a.v_peers + eoff);
+    const auto rdk = scalar_rsrc(a.k_ring + eoff), rdv = scalar_rsrc(a.v_ring + eoff);
+    // The part's K and V loads of a pass are all issued before its first
+    // store (up to 2 x 32 KiB per pass): a 64 KiB part is one load round trip
+    // and one store drain.  Pieces past the part read zero and drop their
+    // stores.
     constexpr int U = 8;
+    for (uint32_t b = 0; b < n16; b += U * NT) {
+        uint32_t off[U];
+        f32x4 vk[U], vv[U];
 #pragma unroll
-    for (int kv = 0; kv < 2; ++kv) {
-        const auto rs = scalar_rsrc((kv ? a.v_peers : a.k_peers) + eoff);
-        const auto rd = scalar_rsrc((kv ? a.v_ring : a.k_ring) + eoff);
-        uint32_t i = threadIdx.x;
-        for (; i + (U - 1) * NT < n16; i += U * NT) {
-            f32x4 v[U];
-#pragma unroll
-            for (int k = 0; k < U; ++k)
-                v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (i + k * NT) * 16u, 0, kPolicyStream);
-#pragma unroll
-            for (int k = 0; k < U; ++k)
-                __builtin_amdgcn_raw_buffer_store_b128(v[k], rd, (i + k * NT) * 16u, 0, kPolicyCoherentStream);
+        for (int k = 0; k < U; ++k) {
+            const uint32_t i = b + k * NT + threadIdx.x;
+            off[k] = i < n16 ? i * 16u : kOOB;
+            vk[k] = __builtin_amdgcn_raw_buffer_load_b128(rsk, off[k], 0, kPolicyStream);
         }
-        for (; i < n16; i += NT) {
-            const f32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, i * 16u, 0, kPolicyStream);
-            __builtin_amdgcn_raw_buffer_store_b128(v, rd, i * 16u, 0, kPolicyCoherentStream);
-        }
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+            vv[k] = __builtin_amdgcn_raw_buffer_load_b128(rsv, off[k], 0, kPolicyStream);
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+            __builtin_amdgcn_raw_buffer_store_b128(vk[k], rdk, off[k], 0, kPolicyCoherentStream);
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+            __builtin_amdgcn_raw_buffer_store_b128(vv[k], rdv, off[k], 0, kPolicyCoherentStream);
     }
 }
 
