@@ -504,16 +504,6 @@ def check_state(maps: Dict[str, np.ndarray], T: int, tiles_per_chunk: int, epoch
 #   are computed from the local shard directly).  Compute order: local tile
 #   rows first, then the other ranks' rows in the order they are copied,
 #   which is plain row order; blocks left to right inside a tile row.
-# - A chunk is moved as `parts` K-slices: slice p is the columns
-#   [b_p, b_(p+1)) of all the chunk's rows, cut at multiples of 64 columns
-#   (128 bytes, one cache line of a row), the last ending at K.  Every slice
-#   carries its own arrival flag, and the chunk's flag follows once all its
-#   slices have landed (the pages' rule that an arrival flag names a
-#   completed payload, applied to each slice a mover carries).  A GEMM block
-#   consumes A in K order, so where K is a multiple of 64 the copy claims go
-#   slice by slice (slice 0 of every chunk in chunk order, then slice 1, ...)
-#   and a block may begin once its chunk's first slice is in; otherwise they
-#   go chunk by chunk, the slices of a chunk one after another.
 
 
 def allgather_gemm(a_local_bits: np.ndarray, a_peers_bits: np.ndarray,
@@ -551,62 +541,17 @@ def ag_parts_per_chunk(tile_m: int, K: int, tiles_n: int) -> int:
     """Copy tasks one chunk is split into.  The pages fix the chunk (the
     arrival unit, one tile row of A) but not how many movers share it; here
     one copy task moves at most 64 KiB of the chunk's tile_m x K bf16 bytes:
-    ceil(2 tile_m K / 65536) parts, at least 1 and at most min(tiles_n, 64).
-    (For tile_m <= 512 that is at most ceil(K / 64), one 64-column unit per
-    K-slice.)"""
+    ceil(2 tile_m K / 65536) parts, at least 1 and at most min(tiles_n, 64)."""
     parts = -(-(2 * tile_m * K) // 65536)
     return int(max(1, min(parts, tiles_n, 64)))
-
-
-AG_SLICE_COLS = 64   # slice bounds are multiples of 64 columns (128 bytes of bf16)
-
-
-def ag_part_bounds(K: int, parts: int) -> np.ndarray:
-    """Column bounds b_0 = 0 < b_1 < ... < b_parts = K of a chunk's K-slices:
-    the U = ceil(K / 64) 64-column units are dealt as evenly as floor division
-    allows, b_p = 64 floor(p U / parts) for p < parts, and the last slice ends
-    at K.  Needs 1 <= parts <= U (every slice at least one unit)."""
-    U = -(-K // AG_SLICE_COLS)
-    if K < 1 or parts < 1 or parts > U:
-        raise ValueError("need K >= 1 and 1 <= parts <= ceil(K / 64)")
-    p = np.arange(parts + 1, dtype=np.int64)
-    b = AG_SLICE_COLS * ((p * U) // parts)
-    b[parts] = K
-    return b
-
-
-def ag_part_of_column(col: int, K: int, parts: int) -> int:
-    """The K-slice holding column `col` of a chunk (0 <= col < K)."""
-    b = ag_part_bounds(K, parts)
-    if not 0 <= col < K:
-        raise ValueError("column outside [0, K)")
-    return int(np.searchsorted(b, col, side="right") - 1)
-
-
-def ag_sliced_order(K: int) -> bool:
-    """Copy claims go slice by slice when K is a whole number of 64-column
-    units (each slice's rows start and end on cache-line bounds)."""
-    return K % AG_SLICE_COLS == 0
-
-
-def ag_copy_tasks(ranks: int, chunks_per_shard: int, parts: int, sliced: bool) -> np.ndarray:
-    """Copy task ids (chunk id * parts + slice) in claim order: slice by
-    slice over the chunks in copy order when `sliced`, else chunk by chunk
-    with each chunk's slices in order."""
-    order = ag_copy_order(ranks, chunks_per_shard)
-    if sliced:
-        return (order[None, :] * parts + np.arange(parts, dtype=np.int64)[:, None]).reshape(-1)
-    return (order[:, None] * parts + np.arange(parts, dtype=np.int64)[None, :]).reshape(-1)
 
 
 def ag_expected_state(n_chunks: int, n_tiles: int, epoch: int, calls: int,
                       parts: int = 1) -> Dict[str, np.ndarray]:
     """Integer state after `calls` complete launches of one shape: every
-    slice's and every chunk's arrival flag holds the last epoch, each of a
-    chunk's `parts` copy tasks ran and every tile was computed exactly once
-    per call."""
+    chunk's arrival flag holds the last epoch, each of a chunk's `parts`
+    copy tasks ran and every tile was computed exactly once per call."""
     return {
-        "part_flag": np.full(n_chunks * parts, epoch, dtype=np.int64),
         "chunk_flag": np.full(n_chunks, epoch, dtype=np.int64),
         "chunk_copy_cnt": np.full(n_chunks, parts * calls, dtype=np.int64),
         "tile_compute_cnt": np.full(n_tiles, calls, dtype=np.int64),
@@ -614,17 +559,19 @@ def ag_expected_state(n_chunks: int, n_tiles: int, epoch: int, calls: int,
 
 
 def ag_deterministic_owners(ranks: int, chunks_per_shard: int, tiles_n: int, B: int, n_copy: int,
-                            tiles_per_task: int = 1, parts: int = 1,
-                            sliced: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+                            tiles_per_task: int = 1, parts: int = 1) -> Tuple[np.ndarray, np.ndarray]:
     """Owner maps of the deterministic static schedule: workgroups
-    [0, n_copy) copy, the others compute.  Copy task i in claim order
-    (ag_copy_tasks) goes to workgroup i mod n_copy.  Compute task j (blocks
-    of `tiles_per_task` adjacent tiles, row by row) goes to
-    n_copy + j mod (B - n_copy).  Returns (copy owner per copy task, indexed
-    chunk id * parts + slice; compute owner per tile)."""
-    tasks = ag_copy_tasks(ranks, chunks_per_shard, parts, sliced)
-    copy_owner = np.zeros(tasks.shape[0], dtype=np.int64)
-    copy_owner[tasks] = np.arange(tasks.shape[0], dtype=np.int64) % n_copy
+    [0, n_copy) copy, the others compute.  Copy tasks are the chunks in copy
+    order, each split into `parts` consecutive tasks; copy task i goes to
+    workgroup i mod n_copy.  Compute task j (blocks of `tiles_per_task`
+    adjacent tiles, row by row) goes to n_copy + j mod (B - n_copy).
+    Returns (copy owner per copy task, indexed chunk id * parts + part;
+    compute owner per tile)."""
+    order = ag_copy_order(ranks, chunks_per_shard)
+    n_tasks = order.shape[0] * parts
+    i = np.arange(n_tasks, dtype=np.int64)
+    copy_owner = np.zeros(n_tasks, dtype=np.int64)
+    copy_owner[order[i // parts] * parts + i % parts] = i % n_copy
     T = ranks * chunks_per_shard * tiles_n
     task = compute_task_of_tile(T, tiles_n, tiles_per_task)
     return copy_owner, n_copy + task % (B - n_copy)
@@ -632,7 +579,7 @@ def ag_deterministic_owners(ranks: int, chunks_per_shard: int, tiles_n: int, B: 
 
 def ag_check_state(maps: Dict[str, np.ndarray], ranks: int, chunks_per_shard: int, tiles_n: int,
                    epoch: int, calls: int, B: int, mode: str, n_copy: int,
-                   tiles_per_task: int = 1, parts: int = 1, sliced: bool = False) -> List[str]:
+                   tiles_per_task: int = 1, parts: int = 1) -> List[str]:
     """Compare an AllGather+GEMM launch's protocol state with its closed form.
 
     Owner words are (mark << 31) | (copy target seen << 16) | workgroup.  A
@@ -661,8 +608,7 @@ def ag_check_state(maps: Dict[str, np.ndarray], ranks: int, chunks_per_shard: in
     if np.any(co_wg >= B) or np.any(po_wg >= B):
         bad.append("owner outside [0, B)")
     if mode == "deterministic":
-        dc, dp = ag_deterministic_owners(ranks, chunks_per_shard, tiles_n, B, n_copy, tiles_per_task, parts,
-                                         sliced)
+        dc, dp = ag_deterministic_owners(ranks, chunks_per_shard, tiles_n, B, n_copy, tiles_per_task, parts)
         if not np.array_equal(co_wg, dc):
             i = int(np.nonzero(co_wg != dc)[0][0])
             bad.append(f"copy_owner[{i}] = {int(co_wg[i])}, expected {int(dc[i])}")

@@ -225,69 +225,3 @@ def test_ag_check_state_with_parts():
     bad = {k: v.copy() for k, v in maps.items()}
     bad["copy_owner"][[0, 1]] = bad["copy_owner"][[1, 0]]
     assert oracle.ag_check_state(bad, 2, 2, 3, 3, 2, 5, "deterministic", 2, 2, parts=3)
-
-
-# ---------------------------------------------------------------------------
-# K-slices of a chunk
-# ---------------------------------------------------------------------------
-
-def test_part_bounds_hand_values():
-    # 4096 columns = 64 units over 14 slices: 64 floor(p 64 / 14)
-    np.testing.assert_array_equal(
-        oracle.ag_part_bounds(4096, 14),
-        [0, 256, 576, 832, 1152, 1408, 1728, 2048, 2304, 2624, 2880, 3200, 3456, 3776, 4096])
-    # 1784 columns = 28 units (the last one 56 columns wide) over 7 slices
-    np.testing.assert_array_equal(oracle.ag_part_bounds(1784, 7), [0, 256, 512, 768, 1024, 1280, 1536, 1784])
-    np.testing.assert_array_equal(oracle.ag_part_bounds(200, 1), [0, 200])
-    np.testing.assert_array_equal(oracle.ag_part_bounds(8192, 64), np.arange(65) * 128)
-    with pytest.raises(ValueError):
-        oracle.ag_part_bounds(100, 3)      # 2 units cannot make 3 slices
-
-
-@pytest.mark.parametrize("K,parts", [(64, 1), (4104, 4), (1784, 7), (4096, 14), (8192, 64), (520, 2), (130, 3)])
-def test_part_bounds_properties(K, parts):
-    b = oracle.ag_part_bounds(K, parts)
-    assert b[0] == 0 and b[-1] == K and np.all(np.diff(b) > 0)
-    assert np.all(b[1:-1] % 64 == 0)                       # interior cuts on cache-line columns
-    w = np.diff(b[:-1]) if parts > 1 else np.array([], dtype=np.int64)
-    if w.size:
-        assert w.max() - w.min() <= 64                     # full slices differ by at most one unit
-    # every column lies in exactly the slice the lookup names
-    for col in range(0, K, max(1, K // 97)):
-        p = oracle.ag_part_of_column(col, K, parts)
-        assert b[p] <= col < b[p + 1]
-
-
-def test_copy_tasks_hand_example():
-    # 2 ranks x 1 chunk, 2 slices; chunk order [1, 0]
-    np.testing.assert_array_equal(oracle.ag_copy_tasks(2, 1, 2, True), [2, 0, 3, 1])
-    np.testing.assert_array_equal(oracle.ag_copy_tasks(2, 1, 2, False), [2, 3, 0, 1])
-    # 3 ranks x 2 chunks, 3 slices, slice by slice: the other ranks' chunks
-    # 2..5 then ours 0, 1, for each slice in turn
-    t = oracle.ag_copy_tasks(3, 2, 3, True)
-    np.testing.assert_array_equal(t[:6], [6, 9, 12, 15, 0, 3])
-    np.testing.assert_array_equal(np.sort(t), np.arange(18))
-    assert oracle.ag_sliced_order(4096) and oracle.ag_sliced_order(64)
-    assert not oracle.ag_sliced_order(1784) and not oracle.ag_sliced_order(200)
-
-
-def test_deterministic_owners_sliced_hand_example():
-    # tasks [2, 0, 3, 1] dealt to workgroups 0, 1, 2, 0; indexed chunk*2 + slice
-    co, _ = oracle.ag_deterministic_owners(2, 1, 1, 5, 3, 1, parts=2, sliced=True)
-    np.testing.assert_array_equal(co, [1, 0, 0, 2])
-
-
-def test_ag_check_state_part_flags_and_order():
-    exp = oracle.ag_expected_state(4, 12, 3, 2, parts=3)
-    assert exp["part_flag"].shape == (12,) and np.all(exp["part_flag"] == 3)
-    co, po = oracle.ag_deterministic_owners(2, 2, 3, 5, 2, 2, parts=3, sliced=True)
-    maps = {k: v.copy() for k, v in exp.items()}
-    maps["copy_owner"] = co | (2 << 16)
-    maps["compute_owner"] = po | (2 << 16)
-    assert oracle.ag_check_state(maps, 2, 2, 3, 3, 2, 5, "deterministic", 2, 2, parts=3, sliced=True) == []
-    # the chunk-by-chunk deal is a different schedule
-    assert oracle.ag_check_state(maps, 2, 2, 3, 3, 2, 5, "deterministic", 2, 2, parts=3, sliced=False)
-    # a slice whose flag was never set is caught even when its chunk's is
-    bad = {k: v.copy() for k, v in maps.items()}
-    bad["part_flag"][7] = 2
-    assert oracle.ag_check_state(bad, 2, 2, 3, 3, 2, 5, "deterministic", 2, 2, parts=3, sliced=True)
