@@ -694,12 +694,13 @@ int run_allgather(bool fused, const void *A_local, const void *A_peers, int num_
     if (cap > nwg - 1) cap = nwg - 1;
     if (cap < 1) cap = 1;
     if (set.mode == MK_PART_ADAPTIVE) {
-        // default start: the cap.  Communication feeds compute here, and the
-        // analysis page's section 2.4 lets the data dependency decide the
-        // initial split: rows must arrive before they are computed, so the
-        // copy role starts at its largest and the controller shrinks it once
-        // both roles have measured costs
-        if (ns_init == 0) ns_init = cap;
+        // default start: three quarters of the workgroups.  Communication
+        // feeds compute here, and the analysis page's section 2.4 lets the
+        // data dependency decide the initial split: rows must arrive before
+        // they are computed, so the copy role starts large and the controller
+        // shrinks it once both roles have measured costs.  A quarter computes
+        // from the start: this rank's own rows need no copy.
+        if (ns_init == 0) ns_init = (3 * nwg) / 4;
         if (ns_init > cap) ns_init = cap;
         if (ns_init < 1) ns_init = 1;
     }

@@ -217,9 +217,10 @@ int mk_gemm_reduce_scatter_unfused(const void *A, const void *B, const float *pe
  *   tile_m, tile_n   64x64, 128x128 or 256x128.
  * Pointers 16-byte aligned; A_gathered and C must not overlap each other or
  * any input (MK_ERR_INVALID_ARG).  Partition (mk_set_partition): the count is
- * the copy role's; adaptive starts at the cap unless set (0: communication
- * feeds compute, so the data dependency sets a copy-heavy start), and the
- * cap is B - 1 unless mk_set_controller_cap sets one; static copiers
+ * the copy role's; adaptive starts at 3B/4 (capped) unless set (0:
+ * communication feeds compute, so the data dependency sets a copy-heavy
+ * start, and this rank's own rows keep the rest busy), and the cap is B - 1
+ * unless mk_set_controller_cap sets one; static copiers
  * leave once every chunk is claimed; the deterministic schedule deals copy
  * tasks (in copy order) round-robin to workgroups [0, n) and compute blocks
  * (row-major) to [n, B).  mk_set_adaptive_help(0) makes a waiting compute
