@@ -13,10 +13,14 @@ legs, plus geometric means over the four full-size workloads.
 Legs per workload (all on the same seeded inputs, same stream):
   fused (adaptive partition)          -> ms, TFLOP/s, roofline fraction
   unfused: GEMM kernel then reduce kernel -> fused_vs_unfused
+  headline only: the GEMM kernel alone, no peers (the bound a fused launch
+    cannot beat) -> fused_over_gemm_alone
   the pages' plain controller rule (start 2, no cap, no help)
   static partitions 2..64 reduce workgroups (and 96..224 beyond the pages'
     range) -> adaptive_vs_best_static_2_64, adaptive_vs_best_static_any
   chunk release lag of the last fused launch (per-chunk stamps)
+Each leg runs untimed for --settle-ms first (the GPU's clock settles after
+an idle spell), then its warm-up launches, then the timed ones.
 Every leg ends with mk_get_stats, whose status is sticky over all the leg's
 launches: a timeout or protocol violation in any launch fails the bench.
 Before each timed launch a 512 MiB scratch buffer is rewritten (outside the
@@ -322,7 +326,7 @@ def set_adaptive_defaults(mk):
     mk.set_controller_cap(0)
 
 
-def measure(args, w, mk, wl, upload, np, torch, keep_host=False):
+def measure(args, w, mk, wl, upload, np, torch, keep_host=False, headline=False):
     """Every leg of one workload.  Returns (record, host inputs or None)."""
     t_gen = time.perf_counter()
     a, b, p = wl.make_inputs(w)
@@ -401,6 +405,17 @@ def measure(args, w, mk, wl, upload, np, torch, keep_host=False):
     rec["unfused_ms"] = summary(ms_unf)
     rec["fused_vs_unfused"] = statistics.fmean(ms_unf) / ms
     print(f"[bench] {w.name} unfused: {summary(ms_unf)}", file=sys.stderr, flush=True)
+
+    if headline:
+        # the bound a fused launch cannot beat: the same GEMM kernel with no
+        # peers to reduce (the unfused baseline's first kernel alone)
+        def gemm_alone():
+            mk.gemm_reduce_unfused(A, B, None, C, w.tile_m, w.tile_n, w.tiles_per_chunk)
+
+        ms_g, _ = time_leg(gemm_alone, args.steps, args.warmup, flush, stream, torch)
+        rec["gemm_alone_ms"] = summary(ms_g)
+        rec["fused_over_gemm_alone"] = statistics.fmean(ms_g) / ms
+        print(f"[bench] {w.name} GEMM alone: {summary(ms_g)}", file=sys.stderr, flush=True)
 
     if fixed:
         mk.set_partition(w.mode, w.n_reduce)
@@ -750,7 +765,7 @@ def main(argv=None):
     for name in names:
         w = wl.workload(name)
         want_cpu = name == head_name and not args.no_cpu and not args.fused_only
-        rec, host = measure(args, w, mk, wl, upload, np, torch, keep_host=want_cpu)
+        rec, host = measure(args, w, mk, wl, upload, np, torch, keep_host=want_cpu, headline=name == head_name)
         per[name] = rec
         if want_cpu:
             cpu = cpu_baseline(w, *host, args.cpu_seconds)
@@ -779,9 +794,9 @@ def main(argv=None):
                    "cache_flush_between_steps": not args.no_flush},
         "roofline": head["roofline"],
     }
-    for key in ("fused_vs_unfused", "adaptive_vs_best_static_2_64", "adaptive_vs_best_static_any",
-                "labelled_variants_gain", "chunk_release_lag", "phases", "counters", "fused_ms",
-                "unfused_ms"):
+    for key in ("fused_vs_unfused", "fused_over_gemm_alone", "adaptive_vs_best_static_2_64",
+                "adaptive_vs_best_static_any", "labelled_variants_gain", "chunk_release_lag", "phases",
+                "counters", "fused_ms", "unfused_ms", "gemm_alone_ms"):
         if key in head:
             result[key] = head[key]
     if cpu is not None:
