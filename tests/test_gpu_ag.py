@@ -240,3 +240,20 @@ def test_allgather_same_grid_different_parts(mk):
         g, C, st = run_ag(mk, True, w, a0, ap, b, "static", 2)
         check_ag(g, C, a0, ap, b)
         ag_protocol(st, w, "static", 2)
+
+
+@pytest.mark.parametrize("nwg,mode,n", [(2, "adaptive", 0), (2, "static", 1), (3, "deterministic", 1),
+                                        (5, "adaptive", 0), (5, "static", 2)])
+def test_allgather_few_workgroups(mk, nwg, mode, n):
+    """Grids of 2-5 workgroups: every chunk still arrives (a copy workgroup
+    never computes while copies remain) and every block is computed once."""
+    mk.set_num_workgroups(nwg)
+    try:
+        w = wl.custom(128, 136, 128, 2, 64, 64, 1, wid=870 + nwg)
+        a0, ap, b = wl.make_ag_inputs(w)
+        g, C, st = run_ag(mk, True, w, a0, ap, b, mode, n)
+        assert st["num_wg"] == nwg
+        check_ag(g, C, a0, ap, b)
+        ag_protocol(st, w, mode, n)
+    finally:
+        mk.set_num_workgroups(0)

@@ -220,3 +220,20 @@ def test_ring_full_size_sampled(mk, name):
     assert float(np.max(np.abs(L[heads, rows] - Lref))) <= LSE_TOL
     Ou, Lu, _, _, _ = run_ring(mk, False, w, inp)
     assert np.array_equal(O, Ou) and np.array_equal(L, Lu)
+
+
+@pytest.mark.parametrize("nwg,mode,n", [(2, "adaptive", 0), (2, "static", 1), (3, "deterministic", 1),
+                                        (5, "adaptive", 0), (5, "static", 2)])
+def test_ring_few_workgroups(mk, nwg, mode, n):
+    """Grids of 2-5 workgroups: the copy role keeps at least one workgroup
+    while tiles remain to copy, so every compute task completes."""
+    mk.set_num_workgroups(nwg)
+    try:
+        w = wl.ra_custom(3, 200, 2, 128, wid=340 + nwg)
+        inp = wl.make_ra_inputs(w)
+        O, L, kr, vr, st = run_ring(mk, True, w, inp, mode, n)
+        assert st["num_wg"] == nwg
+        check_ring(O, L, kr, vr, inp)
+        ring_protocol(st, w, mode, n)
+    finally:
+        mk.set_num_workgroups(0)
