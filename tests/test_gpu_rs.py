@@ -189,3 +189,21 @@ def test_reduce_scatter_full_size_sampled(mk, name, mode, n):
     Cu, Ru, _ = run_rs(mk, False, w, a, b, p, r0)
     assert np.array_equal(C, Cu)
     assert np.array_equal(R, Ru)
+
+
+@pytest.mark.parametrize("nwg,mode,n", [(2, "deterministic", 1), (2, "static", 1), (3, "static", 2),
+                                        (5, "adaptive", 3)])
+def test_reduce_scatter_few_workgroups(mk, nwg, mode, n):
+    """Grids of 2-5 workgroups: the shard's tiles are computed and reduced
+    once each and every outside row still reaches its inbox."""
+    mk.set_num_workgroups(nwg)
+    try:
+        w = wl.custom(1100, 264, 200, 1, 128, 128, 4, wid=760 + nwg)
+        a, b, p = wl.make_inputs(w)
+        r0 = wl.make_remote(w)
+        C, R, st = run_rs(mk, True, w, a, b, p, r0, mode=mode, n_reduce=n)
+        assert st["num_wg"] == nwg
+        check_rs_full(C, R, a, b, p, r0, w)
+        check_rs_protocol(st, w, mode, n)
+    finally:
+        mk.set_num_workgroups(0)
